@@ -1,0 +1,160 @@
+"""Python binding of the gfx950 scaled-FP8 Linear-layer GEMM library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libte_fp8.so`` behind the C ABI declared in ``include/te_fp8.h``.
+PyTorch supplies device memory and the current stream.  There is no fallback:
+if the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libte_fp8.so")
+
+# te_status_t
+TE_OK = 0
+# te_dtype_t
+TE_DTYPE_E4M3 = 1
+TE_DTYPE_E5M2 = 2
+TE_DTYPE_BF16 = 3
+TE_DTYPE_F32 = 4
+# te_accum_t
+TE_ACCUM_FULL_FP32 = 1
+TE_ACCUM_FAST = 2
+# epilogue flags
+TE_EPI_NONE = 0
+TE_EPI_BIAS = 1
+TE_EPI_GELU = 2
+TE_EPI_AUX_PREACT = 4
+TE_EPI_DGELU = 8
+TE_EPI_BGRAD = 16
+# cast flags
+TE_CAST_POW2_SCALE = 1
+
+EXPORTED = ("te_cast_fp8_per_token", "te_fp8_gemm_fwd", "te_fp8_gemm_dgrad", "te_fp8_wgrad_accum",
+            "te_fp8_kgrouped_wgrad", "te_status_string", "te_last_error_message")
+
+
+class TeFp8Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+
+def load_library():
+    """Load libte_fp8.so (built in-tree by ``fp8_linear_layer_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m fp8_linear_layer_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, U32, I32, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_int32, ctypes.c_int
+    lib.te_status_string.restype = ctypes.c_char_p
+    lib.te_status_string.argtypes = [I]
+    lib.te_last_error_message.restype = ctypes.c_char_p
+    lib.te_last_error_message.argtypes = []
+    lib.te_cast_fp8_per_token.restype = I
+    lib.te_cast_fp8_per_token.argtypes = [P, I64, I64, I64, I, U32, P, I64, P, P]
+    lib.te_fp8_gemm_fwd.restype = I
+    lib.te_fp8_gemm_fwd.argtypes = [P, P, I, P, P, I, I64, I64, I64, P, U32, P, I, I64, P, I64, I, P]
+    lib.te_fp8_gemm_dgrad.restype = I
+    lib.te_fp8_gemm_dgrad.argtypes = [P, P, I, P, P, I, I64, I64, I64, U32, P, I64, P, P, I, I64, I, P]
+    lib.te_fp8_wgrad_accum.restype = I
+    lib.te_fp8_wgrad_accum.argtypes = [P, P, I, P, P, I, I64, I64, I64, P, I64, I, P]
+    lib.te_fp8_kgrouped_wgrad.restype = I
+    lib.te_fp8_kgrouped_wgrad.argtypes = [P, P, I, P, P, I, I64, I64, P, I32, P, I, P]
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != TE_OK:
+        lib = load_library()
+        msg = lib.te_last_error_message().decode()
+        raise TeFp8Error(status, f"{lib.te_status_string(status).decode()}: {msg}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _cols(t):
+    return t.shape[-1]
+
+
+# --------------------------------------------------------------- entry points
+def te_cast_fp8_per_token(x, out_dtype=TE_DTYPE_E4M3, flags=0, q=None, scales=None, stream=None):
+    """bf16 x [rows, cols] -> (q uint8 [rows, cols], scales fp32 [rows, cols/128])."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device)
+    _check(load_library().te_cast_fp8_per_token(_ptr(x), rows, cols, x.stride(0), out_dtype, flags,
+                                                _ptr(q), q.stride(0), _ptr(scales), _stream(stream)))
+    return q, scales
+
+
+def te_fp8_gemm_fwd(x, x_scales, x_dtype, w, w_scales, w_dtype, bias=None, epilogue=TE_EPI_NONE,
+                    y=None, y_dtype=TE_DTYPE_BF16, preact=None, accum=TE_ACCUM_FAST, stream=None):
+    """Y[M,N] = epi(X[M,K] W[N,K]^T (+ b)); returns y (and fills preact if given)."""
+    M, K = x.shape
+    N = w.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16 if y_dtype == TE_DTYPE_BF16 else torch.float32, device=x.device)
+    _check(load_library().te_fp8_gemm_fwd(
+        _ptr(x), _ptr(x_scales), x_dtype, _ptr(w), _ptr(w_scales), w_dtype, M, N, K,
+        _ptr(bias), epilogue, _ptr(y), y_dtype, y.stride(0),
+        _ptr(preact), preact.stride(0) if preact is not None else 0, accum, _stream(stream)))
+    return y
+
+
+def te_fp8_gemm_dgrad(dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, epilogue=TE_EPI_NONE, preact=None,
+                      bias_grad=None, dx=None, dx_dtype=TE_DTYPE_BF16, accum=TE_ACCUM_FULL_FP32, stream=None):
+    """D[M,N] = dY[M,K] Wt[N,K]^T, then dGELU / bias-grad; returns dx."""
+    M, K = dy.shape
+    N = wt.shape[0]
+    if dx is None:
+        dx = torch.empty((M, N), dtype=torch.bfloat16 if dx_dtype == TE_DTYPE_BF16 else torch.float32, device=dy.device)
+    _check(load_library().te_fp8_gemm_dgrad(
+        _ptr(dy), _ptr(dy_scales), dy_dtype, _ptr(wt), _ptr(wt_scales), wt_dtype, M, N, K, epilogue,
+        _ptr(preact), preact.stride(0) if preact is not None else 0, _ptr(bias_grad),
+        _ptr(dx), dx_dtype, dx.stride(0), accum, _stream(stream)))
+    return dx
+
+
+def te_fp8_wgrad_accum(a, a_scales, a_dtype, b, b_scales, b_dtype, out, accum=TE_ACCUM_FULL_FP32, stream=None):
+    """out[M,N] += A[M,K] B[N,K]^T in fp32; returns out."""
+    M, K = a.shape
+    N = b.shape[0]
+    _check(load_library().te_fp8_wgrad_accum(
+        _ptr(a), _ptr(a_scales), a_dtype, _ptr(b), _ptr(b_scales), b_dtype, M, N, K,
+        _ptr(out), out.stride(0), accum, _stream(stream)))
+    return out
+
+
+def te_fp8_kgrouped_wgrad(a, a_scales, a_dtype, b, b_scales, b_dtype, group_k, out,
+                          accum=TE_ACCUM_FULL_FP32, stream=None):
+    """out[g] += A[:, group g] B[:, group g]^T; group_k is a host sequence of ints."""
+    M = a.shape[0]
+    N = b.shape[0]
+    gk = (ctypes.c_int64 * len(group_k))(*[int(k) for k in group_k])
+    _check(load_library().te_fp8_kgrouped_wgrad(
+        _ptr(a), _ptr(a_scales), a_dtype, _ptr(b), _ptr(b_scales), b_dtype, M, N,
+        ctypes.cast(gk, ctypes.c_void_p), len(group_k), _ptr(out), accum, _stream(stream)))
+    return out

@@ -1,0 +1,346 @@
+// C-ABI front end: argument validation, dispatch, per-call logging.
+//
+// Every check runs on the host before anything is enqueued, so a rejected call
+// launches nothing and touches no output.  The library allocates no memory and
+// never synchronises; all work goes onto the caller's stream.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+#include "te_fp8.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+te_status_t fail(te_status_t st, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+te_status_t ok()
+{
+    g_last_error.clear();
+    return TE_OK;
+}
+
+bool log_enabled()
+{
+    static const bool on = [] {
+        const char* v = std::getenv("TE_FP8_LOG");
+        return v && v[0] && std::strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+const char* dtype_name(te_dtype_t d)
+{
+    switch (d) {
+    case TE_DTYPE_E4M3: return "e4m3";
+    case TE_DTYPE_E5M2: return "e5m2";
+    case TE_DTYPE_BF16: return "bf16";
+    case TE_DTYPE_F32: return "f32";
+    }
+    return "?";
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool is_fp8(te_dtype_t d) { return d == TE_DTYPE_E4M3 || d == TE_DTYPE_E5M2; }
+
+int to_fmt(te_dtype_t d) { return d == TE_DTYPE_E4M3 ? tefp8::FMT_E4M3 : tefp8::FMT_E5M2; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+// Checks shared by every GEMM entry point.
+te_status_t check_operands(const char* fn, const void* a, const float* sa, te_dtype_t da, const void* b,
+                           const float* sb, te_dtype_t db, int64_t M, int64_t N, int64_t K, te_accum_t accum)
+{
+    if (!a || !sa || !b || !sb) return fail(TE_ERR_INVALID_ARGUMENT, "%s: operand or scale pointer is null", fn);
+    if (!is_fp8(da) || !is_fp8(db))
+        return fail(TE_ERR_INVALID_ARGUMENT, "%s: operand dtypes must be TE_DTYPE_E4M3 or TE_DTYPE_E5M2 (got %d, %d)", fn, (int)da, (int)db);
+    if (M < 1 || N < 1 || M >= kMaxDim || N >= kMaxDim)
+        return fail(TE_ERR_INVALID_ARGUMENT, "%s: M and N must be in [1, 2^31) (got M=%lld N=%lld)", fn, (long long)M, (long long)N);
+    if (K < 128 || K % 128 != 0 || K >= kMaxDim)
+        return fail(TE_ERR_INVALID_ARGUMENT, "%s: K must be a positive multiple of 128 below 2^31 (got %lld)", fn, (long long)K);
+    if (accum != TE_ACCUM_FULL_FP32 && accum != TE_ACCUM_FAST)
+        return fail(TE_ERR_INVALID_ARGUMENT, "%s: accum must be TE_ACCUM_FULL_FP32 or TE_ACCUM_FAST (got %d)", fn, (int)accum);
+    if (!aligned(a, 16) || !aligned(b, 16)) return fail(TE_ERR_MISALIGNED, "%s: fp8 operands must be 16-byte aligned", fn);
+    if (!aligned(sa, 4) || !aligned(sb, 4)) return fail(TE_ERR_MISALIGNED, "%s: scales must be 4-byte aligned", fn);
+    return TE_OK;
+}
+
+// Output matrix [M][ld] of dtype d (bf16 or fp32), base 16-byte aligned, rows 16-byte multiples.
+te_status_t check_output(const char* fn, const char* what, const void* p, te_dtype_t d, int64_t ld, int64_t N)
+{
+    if (!p) return fail(TE_ERR_INVALID_ARGUMENT, "%s: %s pointer is null", fn, what);
+    if (d != TE_DTYPE_BF16 && d != TE_DTYPE_F32)
+        return fail(TE_ERR_INVALID_ARGUMENT, "%s: %s dtype must be TE_DTYPE_BF16 or TE_DTYPE_F32 (got %d)", fn, what, (int)d);
+    if (ld < N) return fail(TE_ERR_INVALID_ARGUMENT, "%s: leading dimension of %s (%lld) is below N (%lld)", fn, what, (long long)ld, (long long)N);
+    const int64_t per16 = d == TE_DTYPE_BF16 ? 8 : 4;
+    if (!aligned(p, 16) || ld % per16 != 0)
+        return fail(TE_ERR_MISALIGNED, "%s: %s must be 16-byte aligned with a row stride that is a multiple of 16 bytes", fn, what);
+    return TE_OK;
+}
+
+tefp8::GemmArgs base_args(const void* a, const float* sa, te_dtype_t da, const void* b, const float* sb,
+                          te_dtype_t db, int64_t M, int64_t N, int64_t K, te_accum_t accum)
+{
+    tefp8::GemmArgs g;
+    std::memset(&g, 0, sizeof g);
+    g.a = static_cast<const uint8_t*>(a);
+    g.sa = sa;
+    g.b = static_cast<const uint8_t*>(b);
+    g.sb = sb;
+    g.M = M;
+    g.N = N;
+    g.lda = K;
+    g.ldb = K;
+    g.lsa = K / 128;
+    g.lsb = K / 128;
+    g.fmt_a = to_fmt(da);
+    g.fmt_b = to_fmt(db);
+    g.fast = accum == TE_ACCUM_FAST;
+    g.num_groups = 1;
+    g.groups[0] = tefp8::Group{0, (int32_t)(K / 128), 0, 0};
+    return g;
+}
+
+te_status_t launch(const char* fn, const tefp8::GemmArgs& g, hipStream_t stream, int64_t K, te_dtype_t da,
+                   te_dtype_t db, te_accum_t accum, uint32_t epi)
+{
+    tefp8::LaunchInfo info{};
+    hipError_t e = tefp8::launch_gemm(g, stream, &info);
+    if (log_enabled())
+        std::fprintf(stderr, "[te_fp8] %s M=%lld N=%lld K=%lld a=%s b=%s accum=%s epi=0x%x tile=%dx%d threads=%d grid=%lld groups=%d\n",
+                     fn, (long long)g.M, (long long)g.N, (long long)K, dtype_name(da), dtype_name(db),
+                     accum == TE_ACCUM_FAST ? "fast" : "full", epi, info.tile_m, info.tile_n, info.threads,
+                     (long long)info.grid, g.num_groups);
+    if (e != hipSuccess) return fail(TE_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* te_status_string(te_status_t s)
+{
+    switch (s) {
+    case TE_OK: return "TE_OK";
+    case TE_ERR_INVALID_ARGUMENT: return "TE_ERR_INVALID_ARGUMENT";
+    case TE_ERR_MISALIGNED: return "TE_ERR_MISALIGNED";
+    case TE_ERR_UNSUPPORTED: return "TE_ERR_UNSUPPORTED";
+    case TE_ERR_HIP: return "TE_ERR_HIP";
+    case TE_ERR_INTERNAL: return "TE_ERR_INTERNAL";
+    }
+    return "TE_ERR_UNKNOWN";
+}
+
+const char* te_last_error_message(void) { return g_last_error.c_str(); }
+
+te_status_t te_cast_fp8_per_token(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                  te_dtype_t out_dtype, uint32_t flags, void* q, int64_t ld_q,
+                                  float* scales, hipStream_t stream)
+{
+    try {
+        const char* fn = "te_cast_fp8_per_token";
+        if (!x_bf16 || !q || !scales) return fail(TE_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
+        if (rows < 1 || rows >= kMaxDim) return fail(TE_ERR_INVALID_ARGUMENT, "%s: rows must be in [1, 2^31) (got %lld)", fn, (long long)rows);
+        if (cols < 128 || cols % 128 != 0 || cols >= kMaxDim)
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: cols must be a positive multiple of 128 (got %lld)", fn, (long long)cols);
+        if (ld_x < cols || ld_q < cols) return fail(TE_ERR_INVALID_ARGUMENT, "%s: ld_x and ld_q must be >= cols", fn);
+        if (!is_fp8(out_dtype)) return fail(TE_ERR_INVALID_ARGUMENT, "%s: out_dtype must be TE_DTYPE_E4M3 or TE_DTYPE_E5M2 (got %d)", fn, (int)out_dtype);
+        if (flags & ~(uint32_t)TE_CAST_POW2_SCALE) return fail(TE_ERR_INVALID_ARGUMENT, "%s: unknown flag bits 0x%x", fn, flags);
+        if (!aligned(x_bf16, 16) || ld_x % 8 != 0) return fail(TE_ERR_MISALIGNED, "%s: x must be 16-byte aligned with ld_x a multiple of 8", fn);
+        if (!aligned(q, 16) || ld_q % 16 != 0) return fail(TE_ERR_MISALIGNED, "%s: q must be 16-byte aligned with ld_q a multiple of 16", fn);
+        if (!aligned(scales, 4)) return fail(TE_ERR_MISALIGNED, "%s: scales must be 4-byte aligned", fn);
+        tefp8::LaunchInfo info{};
+        hipError_t e = tefp8::launch_cast(static_cast<const uint16_t*>(x_bf16), rows, cols, ld_x, to_fmt(out_dtype),
+                                          (flags & TE_CAST_POW2_SCALE) != 0, static_cast<uint8_t*>(q), ld_q, scales,
+                                          stream, &info);
+        if (log_enabled())
+            std::fprintf(stderr, "[te_fp8] %s rows=%lld cols=%lld out=%s pow2=%d threads=%d grid=%lld\n", fn,
+                         (long long)rows, (long long)cols, dtype_name(out_dtype), (flags & TE_CAST_POW2_SCALE) ? 1 : 0,
+                         info.threads, (long long)info.grid);
+        if (e != hipSuccess) return fail(TE_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+        return ok();
+    } catch (...) {
+        return fail(TE_ERR_INTERNAL, "te_cast_fp8_per_token: internal error");
+    }
+}
+
+te_status_t te_fp8_gemm_fwd(const void* x, const float* x_scales, te_dtype_t x_dtype,
+                            const void* w, const float* w_scales, te_dtype_t w_dtype,
+                            int64_t M, int64_t N, int64_t K,
+                            const void* bias_bf16, uint32_t epilogue,
+                            void* y, te_dtype_t y_dtype, int64_t ld_y,
+                            void* preact_bf16, int64_t ld_preact,
+                            te_accum_t accum, hipStream_t stream)
+{
+    try {
+        const char* fn = "te_fp8_gemm_fwd";
+        te_status_t st = check_operands(fn, x, x_scales, x_dtype, w, w_scales, w_dtype, M, N, K, accum);
+        if (st != TE_OK) return st;
+        const uint32_t allowed = TE_EPI_BIAS | TE_EPI_GELU | TE_EPI_AUX_PREACT;
+        if (epilogue & ~allowed) return fail(TE_ERR_INVALID_ARGUMENT, "%s: epilogue flags 0x%x are not forward flags", fn, epilogue);
+        if ((epilogue & TE_EPI_AUX_PREACT) && !(epilogue & TE_EPI_GELU))
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: TE_EPI_AUX_PREACT requires TE_EPI_GELU", fn);
+        if ((epilogue & TE_EPI_BIAS) && !bias_bf16) return fail(TE_ERR_INVALID_ARGUMENT, "%s: TE_EPI_BIAS needs bias_bf16", fn);
+        if (bias_bf16 && !(epilogue & TE_EPI_BIAS)) return fail(TE_ERR_INVALID_ARGUMENT, "%s: bias_bf16 given without TE_EPI_BIAS", fn);
+        if (bias_bf16 && !aligned(bias_bf16, 16)) return fail(TE_ERR_MISALIGNED, "%s: bias must be 16-byte aligned", fn);
+        st = check_output(fn, "y", y, y_dtype, ld_y, N);
+        if (st != TE_OK) return st;
+        if (epilogue & TE_EPI_AUX_PREACT) {
+            st = check_output(fn, "preact", preact_bf16, TE_DTYPE_BF16, ld_preact, N);
+            if (st != TE_OK) return st;
+        } else if (preact_bf16) {
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: preact given without TE_EPI_AUX_PREACT", fn);
+        }
+        tefp8::GemmArgs g = base_args(x, x_scales, x_dtype, w, w_scales, w_dtype, M, N, K, accum);
+        g.epi = tefp8::Epi::Fwd;
+        g.flags = epilogue;
+        g.out = y;
+        g.out_bf16 = y_dtype == TE_DTYPE_BF16;
+        g.ld_out = ld_y;
+        g.bias = static_cast<const uint16_t*>(bias_bf16);
+        g.aux = static_cast<uint16_t*>(preact_bf16);
+        g.ld_aux = ld_preact;
+        return launch(fn, g, stream, K, x_dtype, w_dtype, accum, epilogue);
+    } catch (...) {
+        return fail(TE_ERR_INTERNAL, "te_fp8_gemm_fwd: internal error");
+    }
+}
+
+te_status_t te_fp8_gemm_dgrad(const void* dy, const float* dy_scales, te_dtype_t dy_dtype,
+                              const void* wt, const float* wt_scales, te_dtype_t wt_dtype,
+                              int64_t M, int64_t N, int64_t K, uint32_t epilogue,
+                              const void* preact_bf16, int64_t ld_preact,
+                              float* bias_grad,
+                              void* dx, te_dtype_t dx_dtype, int64_t ld_dx,
+                              te_accum_t accum, hipStream_t stream)
+{
+    try {
+        const char* fn = "te_fp8_gemm_dgrad";
+        te_status_t st = check_operands(fn, dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, M, N, K, accum);
+        if (st != TE_OK) return st;
+        const uint32_t allowed = TE_EPI_DGELU | TE_EPI_BGRAD;
+        if (epilogue & ~allowed) return fail(TE_ERR_INVALID_ARGUMENT, "%s: epilogue flags 0x%x are not dgrad flags", fn, epilogue);
+        if (epilogue & TE_EPI_DGELU) {
+            if (!preact_bf16) return fail(TE_ERR_INVALID_ARGUMENT, "%s: TE_EPI_DGELU needs preact_bf16", fn);
+            if (ld_preact < N) return fail(TE_ERR_INVALID_ARGUMENT, "%s: ld_preact (%lld) is below N", fn, (long long)ld_preact);
+            if (!aligned(preact_bf16, 16) || ld_preact % 8 != 0)
+                return fail(TE_ERR_MISALIGNED, "%s: preact must be 16-byte aligned with ld_preact a multiple of 8", fn);
+        } else if (preact_bf16) {
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: preact given without TE_EPI_DGELU", fn);
+        }
+        if (epilogue & TE_EPI_BGRAD) {
+            if (!bias_grad) return fail(TE_ERR_INVALID_ARGUMENT, "%s: TE_EPI_BGRAD needs bias_grad", fn);
+            if (!aligned(bias_grad, 4)) return fail(TE_ERR_MISALIGNED, "%s: bias_grad must be 4-byte aligned", fn);
+        } else if (bias_grad) {
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: bias_grad given without TE_EPI_BGRAD", fn);
+        }
+        st = check_output(fn, "dx", dx, dx_dtype, ld_dx, N);
+        if (st != TE_OK) return st;
+        tefp8::GemmArgs g = base_args(dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, M, N, K, accum);
+        g.epi = tefp8::Epi::Dgrad;
+        g.flags = epilogue;
+        g.out = dx;
+        g.out_bf16 = dx_dtype == TE_DTYPE_BF16;
+        g.ld_out = ld_dx;
+        g.preact = static_cast<const uint16_t*>(preact_bf16);
+        g.ld_aux = ld_preact;
+        g.bias_grad = bias_grad;
+        if (epilogue & TE_EPI_BGRAD) {
+            hipError_t e = tefp8::launch_zero_f32(bias_grad, N, stream);
+            if (e != hipSuccess) return fail(TE_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+        }
+        return launch(fn, g, stream, K, dy_dtype, wt_dtype, accum, epilogue);
+    } catch (...) {
+        return fail(TE_ERR_INTERNAL, "te_fp8_gemm_dgrad: internal error");
+    }
+}
+
+te_status_t te_fp8_wgrad_accum(const void* a, const float* a_scales, te_dtype_t a_dtype,
+                               const void* b, const float* b_scales, te_dtype_t b_dtype,
+                               int64_t M, int64_t N, int64_t K,
+                               float* out, int64_t ld_out,
+                               te_accum_t accum, hipStream_t stream)
+{
+    try {
+        const char* fn = "te_fp8_wgrad_accum";
+        te_status_t st = check_operands(fn, a, a_scales, a_dtype, b, b_scales, b_dtype, M, N, K, accum);
+        if (st != TE_OK) return st;
+        st = check_output(fn, "out", out, TE_DTYPE_F32, ld_out, N);
+        if (st != TE_OK) return st;
+        tefp8::GemmArgs g = base_args(a, a_scales, a_dtype, b, b_scales, b_dtype, M, N, K, accum);
+        g.epi = tefp8::Epi::Wgrad;
+        g.out = out;
+        g.ld_out = ld_out;
+        return launch(fn, g, stream, K, a_dtype, b_dtype, accum, 0);
+    } catch (...) {
+        return fail(TE_ERR_INTERNAL, "te_fp8_wgrad_accum: internal error");
+    }
+}
+
+te_status_t te_fp8_kgrouped_wgrad(const void* a, const float* a_scales, te_dtype_t a_dtype,
+                                  const void* b, const float* b_scales, te_dtype_t b_dtype,
+                                  int64_t M, int64_t N, const int64_t* group_k, int32_t G,
+                                  float* out, te_accum_t accum, hipStream_t stream)
+{
+    try {
+        const char* fn = "te_fp8_kgrouped_wgrad";
+        if (!group_k) return fail(TE_ERR_INVALID_ARGUMENT, "%s: group_k is null", fn);
+        if (G < 1 || G > 1024) return fail(TE_ERR_INVALID_ARGUMENT, "%s: G must be in [1, 1024] (got %d)", fn, (int)G);
+        int64_t sumk = 0;
+        for (int32_t g = 0; g < G; ++g) {
+            if (group_k[g] < 0 || group_k[g] % 128 != 0 || group_k[g] >= kMaxDim)
+                return fail(TE_ERR_INVALID_ARGUMENT, "%s: group_k[%d] = %lld is not a non-negative multiple of 128", fn, (int)g,
+                            (long long)group_k[g]);
+            sumk += group_k[g];
+        }
+        te_status_t st = check_operands(fn, a, a_scales, a_dtype, b, b_scales, b_dtype, M, N, sumk, accum);
+        if (st != TE_OK) return st;
+        st = check_output(fn, "out", out, TE_DTYPE_F32, N, N);
+        if (st != TE_OK) return st;
+
+        // longest group first; empty groups get no work
+        std::vector<tefp8::Group> work;
+        int64_t off = 0;
+        for (int32_t g = 0; g < G; ++g) {
+            if (group_k[g] > 0) work.push_back(tefp8::Group{(int32_t)(off / 128), (int32_t)(group_k[g] / 128), g, 0});
+            off += group_k[g];
+        }
+        std::stable_sort(work.begin(), work.end(),
+                         [](const tefp8::Group& x, const tefp8::Group& y) { return x.kb_len > y.kb_len; });
+
+        tefp8::GemmArgs g = base_args(a, a_scales, a_dtype, b, b_scales, b_dtype, M, N, sumk, accum);
+        g.epi = tefp8::Epi::Wgrad;
+        g.out = out;
+        g.ld_out = N;
+        g.out_group_stride = M * N;
+        for (size_t start = 0; start < work.size(); start += tefp8::kMaxGroupsPerLaunch) {
+            const size_t cnt = std::min(work.size() - start, (size_t)tefp8::kMaxGroupsPerLaunch);
+            g.num_groups = (int)cnt;
+            for (size_t i = 0; i < cnt; ++i) g.groups[i] = work[start + i];
+            st = launch(fn, g, stream, sumk, a_dtype, b_dtype, accum, 0);
+            if (st != TE_OK) return st;
+        }
+        return ok();
+    } catch (...) {
+        return fail(TE_ERR_INTERNAL, "te_fp8_kgrouped_wgrad: internal error");
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Internal interface between the C-ABI front end (api.cpp) and the gfx950
+// kernels (cast.hip, gemm.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace tefp8 {
+
+// fp8 operand format as the matrix-core instruction encodes it (cbsz/blgp).
+enum Fmt : int { FMT_E4M3 = 0, FMT_E5M2 = 1 };
+
+enum class Epi : int {
+    Wgrad = 0,  // out[m][n] += acc (fp32 read-modify-write)
+    Fwd = 1,    // bias / GELU / aux pre-activation, bf16 or fp32 store
+    Dgrad = 2   // dGELU / bias-gradient, bf16 or fp32 store
+};
+
+// One contraction group (dense GEMMs have exactly one).
+struct Group {
+    int32_t kb_off;   // first 128-column block of the group
+    int32_t kb_len;   // number of 128-column blocks (>= 1)
+    int32_t out_idx;  // which output matrix (out + out_idx * out_group_stride)
+    int32_t pad;
+};
+
+constexpr int kMaxGroupsPerLaunch = 128;
+
+struct GemmArgs {
+    const uint8_t* a;      // [M][lda] fp8
+    const float* sa;       // [M][lsa]
+    const uint8_t* b;      // [N][ldb] fp8
+    const float* sb;       // [N][lsb]
+    int64_t M, N;
+    int64_t lda, ldb;      // bytes
+    int64_t lsa, lsb;      // floats
+    int fmt_a, fmt_b;      // Fmt
+    bool fast;             // accumulation policy
+    Epi epi;
+    uint32_t flags;        // TE_EPI_* bits
+    // outputs
+    void* out;             // fp32 (wgrad / f32 store) or bf16
+    bool out_bf16;
+    int64_t ld_out;        // elements
+    int64_t out_group_stride;  // elements between consecutive out matrices (grouped)
+    const uint16_t* bias;  // [N] bf16 (Fwd)
+    uint16_t* aux;         // [M][ld_aux] bf16 pre-activation store (Fwd)
+    const uint16_t* preact;  // [M][ld_aux] bf16 (Dgrad)
+    int64_t ld_aux;
+    float* bias_grad;      // [N] (Dgrad)
+    // groups
+    int num_groups;
+    Group groups[kMaxGroupsPerLaunch];
+};
+
+struct LaunchInfo {
+    int tile_m, tile_n, threads;
+    int64_t grid;
+};
+
+hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream, LaunchInfo* info);
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
+hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
+                       bool pow2, uint8_t* q, int64_t ld_q, float* scales, hipStream_t stream,
+                       LaunchInfo* info);
+
+}  // namespace tefp8

@@ -1,0 +1,234 @@
+/*
+ * te_fp8.h - C ABI of the MI355X (gfx950) scaled-FP8 Linear-layer GEMM library.
+ *
+ * Five operations make up the FP8 hot path of a transformer Linear layer in
+ * training: the per-token fp8 cast that produces the operands, the forward
+ * GEMM with its bias/GELU epilogue, the data-gradient GEMM with its dGELU and
+ * bias-gradient epilogue, the weight-gradient GEMM that accumulates into an
+ * fp32 buffer, and its K-grouped (mixture-of-experts) variant.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Layout.   Every matrix is row-major.  Every GEMM is "NT": both operands are
+ *            stored contraction-contiguous, A as [M][K] and B as [N][K] with
+ *            row stride exactly K bytes, and the result is D[M][N] = A * B^T.
+ *            The Linear layer's three products map onto this form as
+ *              forward:  A = X   [tokens][in],   B = W   [out][in]
+ *              dgrad:    A = dY  [tokens][out],  B = W^T [in][out]
+ *              wgrad:    A = dY^T[out][tokens],  B = X^T [in][tokens]
+ *            so no GEMM_m/GEMM_n swap between BLAS orders ever arises and the
+ *            bias vector always has length N, the output-feature count.
+ *  Scales.   Operands are fp8 with one fp32 dequantisation scale per row and
+ *            per 128 consecutive contraction elements ("1x128" groups): the
+ *            value of element (r, k) is dec(q[r][k]) * s[r][k/128].  Scales
+ *            are row-major [rows][K/128], contiguous.  K must be a multiple of
+ *            128.
+ *  Formats.  TE_DTYPE_E4M3 is OCP E4M3FN (max 448), TE_DTYPE_E5M2 is OCP
+ *            E5M2 (max 57344).  Any pairing of the two is accepted.
+ *  Accumulation policy.  Every GEMM takes an explicit te_accum_t; it is
+ *            never inferred from the operand formats.  Both policies compute
+ *            the same mathematical result in fp32:
+ *              TE_ACCUM_FULL_FP32: each 128-deep block is reduced by the
+ *                matrix cores from zero and promoted into the fp32
+ *                accumulator with its scale product in vector fp32 FMA.
+ *              TE_ACCUM_FAST: blocks whose two scales are powers of two
+ *                (the TE_CAST_POW2_SCALE cast produces only such scales)
+ *                are scaled inside the matrix-core instruction and accumulate
+ *                in one chain with no vector work; any other block falls back
+ *                to the FULL update, so the result is correct for any input.
+ *  Ownership. Every pointer is device memory owned by the caller, except
+ *            group_k, which is host memory read during the call.  The
+ *            library allocates nothing, never synchronises, and enqueues its
+ *            kernels on `stream` (NULL = the default stream); results are
+ *            ready when that stream reaches them.  Outputs must not alias
+ *            inputs.
+ *  Errors.   Arguments are validated on the host before anything is
+ *            enqueued; on any error nothing is launched, no output is
+ *            touched, and the call returns a status other than TE_OK.
+ *            te_last_error_message() then describes the failure (thread-
+ *            local).  A failed launch returns TE_ERR_HIP.  Device faults
+ *            surface at the caller's next synchronisation.  No C++ exception
+ *            crosses this interface.  Calls are thread-safe; calls that
+ *            overlap on one stream are ordered by it.
+ *  Alignment. fp8 and bf16 base pointers must be 16-byte aligned, fp32
+ *            scale and output pointers 4-byte aligned.
+ *  Logging.  With the environment variable TE_FP8_LOG=1 every call prints one
+ *            line to stderr (operation, sizes, formats, policy, epilogue,
+ *            tile, grid).  Logging never changes results.
+ *
+ * Sources: the Linear layer's forward and backward equations and the bias
+ * length are those of the maintainer's explanation on "Replaced cublasLt calls
+ * with rocblas gemm + 6 manually crafted epilogues" (ROCm/TransformerEngine
+ * pull request 3); the accumulate-into-out weight gradient and its K-grouped
+ * form are those of "Weight gradient kernels for dense and MoE models"
+ * (DeepGEMM pull request 95); the explicit per-op accumulation precision is
+ * that agreed on "FP8 GEMM for the fprop should use fast accumulation"
+ * (openxla/xla issue 6168).
+ */
+#ifndef TE_FP8_H
+#define TE_FP8_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TE_OK = 0,
+    TE_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, bad enum or flag */
+    TE_ERR_MISALIGNED = 2,       /* pointer or stride alignment violated */
+    TE_ERR_UNSUPPORTED = 3,      /* a combination this library does not implement */
+    TE_ERR_HIP = 4,              /* the HIP runtime reported an error at launch */
+    TE_ERR_INTERNAL = 5          /* anything else; a bug */
+} te_status_t;
+
+typedef enum {
+    TE_DTYPE_E4M3 = 1, /* OCP E4M3FN */
+    TE_DTYPE_E5M2 = 2, /* OCP E5M2 */
+    TE_DTYPE_BF16 = 3,
+    TE_DTYPE_F32 = 4
+} te_dtype_t;
+
+/* 0 is deliberately not a policy: a zero-initialised argument is rejected. */
+typedef enum {
+    TE_ACCUM_FULL_FP32 = 1,
+    TE_ACCUM_FAST = 2
+} te_accum_t;
+
+/* Epilogue flags.  Forward: BIAS, GELU, AUX_PREACT.  Dgrad: DGELU, BGRAD. */
+enum {
+    TE_EPI_NONE = 0,
+    TE_EPI_BIAS = 1,       /* z = acc + bias[n] (bias bf16, length N) */
+    TE_EPI_GELU = 2,       /* y = GELU(z), tanh form */
+    TE_EPI_AUX_PREACT = 4, /* also store bf16(z) to preact (needs GELU) */
+    TE_EPI_DGELU = 8,      /* D = acc * GELU'(preact[m][n]) */
+    TE_EPI_BGRAD = 16      /* bias_grad[n] = sum over m of D (after DGELU) */
+};
+
+/* Cast flags. */
+enum {
+    TE_CAST_POW2_SCALE = 1 /* round every scale up to a power of two */
+};
+
+/*
+ * Per-token 1x128 cast of a bf16 matrix to fp8 with fp32 scales.
+ *
+ * The pages name this step (the wgrad example casts both operands with a
+ * per-token cast before the GEMM) but do not define it; this is the reading:
+ * for every row r and every group g of 128 consecutive columns,
+ *     amax   = max |x[r][128g .. 128g+127]|,   amax_c = max(amax, 2^-100)
+ *     s      = fl32(amax_c / FP8_MAX)                      (dequant scale)
+ *     q[r][k]= enc(fl32(x[r][k] * fl32(FP8_MAX / amax_c)))
+ * with fp32 IEEE division and product, and enc() rounding to nearest even and
+ * saturating to +-FP8_MAX (sign kept on zero).  With TE_CAST_POW2_SCALE,
+ * s = 2^j for the smallest integer j with FP8_MAX * 2^j >= amax_c, and
+ * q = enc(x * 2^-j).  Inputs must be finite (otherwise the output is
+ * unspecified).
+ *
+ *  x_bf16   [rows][ld_x] bf16, the first `cols` columns are cast
+ *  rows     >= 1;  cols >= 128 and a multiple of 128;  ld_x >= cols, ld_x % 8 == 0
+ *  out_dtype TE_DTYPE_E4M3 or TE_DTYPE_E5M2
+ *  flags    0 or TE_CAST_POW2_SCALE
+ *  q        [rows][ld_q] bytes, ld_q >= cols, ld_q % 16 == 0
+ *  scales   [rows][cols/128] fp32, contiguous
+ */
+te_status_t te_cast_fp8_per_token(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                  te_dtype_t out_dtype, uint32_t flags, void* q, int64_t ld_q,
+                                  float* scales, hipStream_t stream);
+
+/*
+ * Forward GEMM of a Linear layer, Y = X * W^T + b, with fused epilogues.
+ *   acc[m][n] = sum_k x[m][k] w[n][k]      (dequantised, fp32 accumulation)
+ *   z = acc + bias[n]          if TE_EPI_BIAS, else acc
+ *   y = GELU(z)                if TE_EPI_GELU, else z
+ *   preact[m][n] = bf16(z)     if TE_EPI_AUX_PREACT (requires TE_EPI_GELU)
+ *
+ *  x, x_scales   [M][K] fp8, [M][K/128] fp32
+ *  w, w_scales   [N][K] fp8, [N][K/128] fp32
+ *  bias_bf16     [N] bf16, required iff TE_EPI_BIAS
+ *  y             [M][ld_y], y_dtype TE_DTYPE_BF16 or TE_DTYPE_F32, ld_y >= N
+ *                (ld_y % 8 == 0 for bf16, % 4 == 0 for fp32)
+ *  preact_bf16   [M][ld_preact] bf16, required iff TE_EPI_AUX_PREACT
+ *  M, N >= 1; K >= 128, K % 128 == 0
+ */
+te_status_t te_fp8_gemm_fwd(const void* x, const float* x_scales, te_dtype_t x_dtype,
+                            const void* w, const float* w_scales, te_dtype_t w_dtype,
+                            int64_t M, int64_t N, int64_t K,
+                            const void* bias_bf16, uint32_t epilogue,
+                            void* y, te_dtype_t y_dtype, int64_t ld_y,
+                            void* preact_bf16, int64_t ld_preact,
+                            te_accum_t accum, hipStream_t stream);
+
+/*
+ * Data-gradient GEMM of a Linear layer with its backward epilogues
+ * (dX = dY * W, and for the layer before a GELU, the gradient through it):
+ *   acc[m][n] = sum_k dy[m][k] wt[n][k]
+ *   D = acc * GELU'(preact[m][n])   if TE_EPI_DGELU, else acc
+ *   bias_grad[n] = sum_m D[m][n]    if TE_EPI_BGRAD (fp32, before dx rounding;
+ *                                   overwritten, not accumulated)
+ *   dx[m][n] = D
+ * dGELU is applied before the bias gradient.  The bias-gradient sum is formed
+ * with atomic fp32 additions, so its last bits may vary from run to run.
+ *
+ *  dy, dy_scales [M][K] fp8 (typically E5M2), [M][K/128]
+ *  wt, wt_scales [N][K] fp8 (W^T re-cast along the out dimension), [N][K/128]
+ *  preact_bf16   [M][ld_preact] bf16, required iff TE_EPI_DGELU
+ *  bias_grad     [N] fp32, required iff TE_EPI_BGRAD
+ *  dx            [M][ld_dx], dx_dtype TE_DTYPE_BF16 or TE_DTYPE_F32
+ */
+te_status_t te_fp8_gemm_dgrad(const void* dy, const float* dy_scales, te_dtype_t dy_dtype,
+                              const void* wt, const float* wt_scales, te_dtype_t wt_dtype,
+                              int64_t M, int64_t N, int64_t K, uint32_t epilogue,
+                              const void* preact_bf16, int64_t ld_preact,
+                              float* bias_grad,
+                              void* dx, te_dtype_t dx_dtype, int64_t ld_dx,
+                              te_accum_t accum, hipStream_t stream);
+
+/*
+ * Weight-gradient GEMM that accumulates: out[m][n] += sum_k a[m][k] b[n][k].
+ * The product is formed in fp32 from zero and added to out once (one fp32
+ * rounding of the sum), as the gradient of a weight accumulates over
+ * micro-batches.  A second identical call adds the product again.
+ *
+ *  a, a_scales   [M][K] fp8 (dY^T, cast along tokens), [M][K/128]
+ *  b, b_scales   [N][K] fp8 (X^T, cast along tokens), [N][K/128]
+ *  out           [M][ld_out] fp32, ld_out >= N, read and written
+ */
+te_status_t te_fp8_wgrad_accum(const void* a, const float* a_scales, te_dtype_t a_dtype,
+                               const void* b, const float* b_scales, te_dtype_t b_dtype,
+                               int64_t M, int64_t N, int64_t K,
+                               float* out, int64_t ld_out,
+                               te_accum_t accum, hipStream_t stream);
+
+/*
+ * K-grouped weight gradient for mixture-of-experts layers: expert g owns the
+ * contraction columns [off_g, off_g + K_g) of both operands, off_g being the
+ * sum of the earlier K's, and
+ *   out[g][m][n] += sum_{k in group g} a[m][k] b[n][k].
+ * A group with K_g = 0 leaves out[g] untouched.
+ *
+ *  a, a_scales   [M][sumK] fp8, [M][sumK/128]
+ *  b, b_scales   [N][sumK] fp8, [N][sumK/128]
+ *  group_k       HOST array of G int64, each >= 0 and a multiple of 128,
+ *                sumK = their sum >= 128
+ *  G             1 .. 1024
+ *  out           [G][M][N] fp32, contiguous
+ */
+te_status_t te_fp8_kgrouped_wgrad(const void* a, const float* a_scales, te_dtype_t a_dtype,
+                                  const void* b, const float* b_scales, te_dtype_t b_dtype,
+                                  int64_t M, int64_t N, const int64_t* group_k, int32_t G,
+                                  float* out, te_accum_t accum, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* te_status_string(te_status_t status);
+
+/* Detail of the calling thread's most recent failure ("" if none). */
+const char* te_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TE_FP8_H */

@@ -1,0 +1,100 @@
+"""GPU parity of te_cast_fp8_per_token: fp8 codes and fp32 scales bit-identical to the oracle."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import bf16_dev, host
+
+te = pytest.importorskip("fp8_linear_layer_amd")
+pytestmark = pytest.mark.gpu
+
+FMT = {te.TE_DTYPE_E4M3: oracle.E4M3, te.TE_DTYPE_E5M2: oracle.E5M2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    te.load_library()
+
+
+def gpu_cast(bits, dt, pow2, ld_x=None, ld_q=None):
+    rows, cols = bits.shape
+    ld_x = ld_x or cols
+    ld_q = ld_q or cols
+    xb = np.zeros((rows, ld_x), np.uint16)
+    xb[:, :cols] = bits
+    x = bf16_dev(xb)[:, :cols]
+    qfull = torch.full((rows, ld_q), 0xA5, dtype=torch.uint8, device="cuda")
+    s = torch.full((rows, cols // 128), -7.0, dtype=torch.float32, device="cuda")
+    te.te_cast_fp8_per_token(x, dt, te.TE_CAST_POW2_SCALE if pow2 else 0, q=qfull[:, :cols], scales=s)
+    torch.cuda.synchronize()
+    qh = host(qfull).numpy()
+    assert (qh[:, cols:] == 0xA5).all(), "cast wrote past cols"
+    return qh[:, :cols], host(s).numpy()
+
+
+def assert_same(bits, dt, pow2, **kw):
+    q, s = gpu_cast(bits, dt, pow2, **kw)
+    qo, so = oracle.cast_per_token(bits, FMT[dt], pow2)
+    bad = np.argwhere(q != qo)
+    assert bad.size == 0, f"{len(bad)} code mismatches, first {bad[0]}: gpu {q[tuple(bad[0])]:#x} oracle {qo[tuple(bad[0])]:#x}"
+    assert np.array_equal(s.view(np.uint32), so.view(np.uint32)), "scale mismatch"
+
+
+def special_rows(dt):
+    """Rows of edge-case groups: zeros, subnormals, tiny amax, huge values, midpoints, signed zeros."""
+    fmax = oracle.fp8_max(FMT[dt])
+    rows = []
+    rows.append(np.zeros(128, np.float32))
+    r = np.zeros(128, np.float32); r[5] = -0.0; r[6] = 1e-40; r[7] = -3e-39; rows.append(r)      # subnormal bf16
+    rows.append(np.float32(2.0 ** -110) * np.arange(-64, 64, dtype=np.float32))                   # amax below the floor
+    rows.append(np.float32(1e-36) * np.linspace(-1, 1, 128, dtype=np.float32))
+    rows.append(np.float32(3e38) * np.linspace(-1, 1, 128, dtype=np.float32))                      # near fp32 max
+    r = np.full(128, 1.0625, np.float32); r[0] = fmax; rows.append(r)                               # ties at scale 1
+    r = np.linspace(-fmax, fmax, 128, dtype=np.float32); rows.append(r)
+    r = np.full(128, -0.0, np.float32); r[3] = 2.0 ** -133; rows.append(r)                        # smallest bf16 subnormal
+    rng = np.random.default_rng(3)
+    r = (rng.standard_normal(128) * 10.0 ** rng.uniform(-30, 30, 128)).astype(np.float32); rows.append(r)
+    return W.f32_to_bf16_bits(np.stack(rows))
+
+
+@pytest.mark.parametrize("dt", [te.TE_DTYPE_E4M3, te.TE_DTYPE_E5M2])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_cast_edge_groups(dt, pow2):
+    bits = special_rows(dt)
+    # pad to 256 columns with a normal group so rows also span two groups
+    extra = W.normal_bf16(np.random.SeedSequence(1), (bits.shape[0], 128))
+    assert_same(np.concatenate([bits, extra], axis=1), dt, pow2)
+
+
+@pytest.mark.parametrize("dt", [te.TE_DTYPE_E4M3, te.TE_DTYPE_E5M2])
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("rows,cols,ldx,ldq", [(1, 128, None, None), (5, 384, 392, 400), (37, 1024, 1152, 1040),
+                                               (1000, 640, None, None)])
+def test_cast_shapes_and_strides(dt, pow2, rows, cols, ldx, ldq):
+    bits = W.normal_bf16(np.random.SeedSequence(rows * 7 + cols), (rows, cols), 0.3)
+    assert_same(bits, dt, pow2, ld_x=ldx, ld_q=ldq)
+
+
+@pytest.mark.parametrize("name,shape,std,dt", [
+    ("dense-wgrad A", (7168, 4096), 1.0, te.TE_DTYPE_E4M3),
+    ("dense-wgrad B", (2112, 4096), 1.0, te.TE_DTYPE_E4M3),
+    ("fprop W", (14336, 4096), 0.02, te.TE_DTYPE_E4M3),
+    ("dgrad dZ", (8192, 14336), 1e-3, te.TE_DTYPE_E5M2),
+])
+def test_cast_workload_sizes(name, shape, std, dt):
+    bits = W.normal_bf16(np.random.SeedSequence(zlib.crc32(name.encode())), shape, std)
+    assert_same(bits, dt, False)
+    assert_same(bits[:512], dt, True)
+
+
+def test_cast_is_deterministic():
+    bits = W.normal_bf16(np.random.SeedSequence(9), (256, 1024))
+    a = gpu_cast(bits, te.TE_DTYPE_E4M3, False)
+    b = gpu_cast(bits, te.TE_DTYPE_E4M3, False)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

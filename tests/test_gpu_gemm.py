@@ -1,0 +1,321 @@
+"""GPU parity of the four GEMM entry points against the fp64 oracle.
+
+The oracle casts the seeded bf16 inputs on the host; those fp8 bytes and
+scales are uploaded and consumed by the HIP kernels, so both sides see the
+same operands (the cast kernel has its own bit-exact test).  Small cases span
+several 256 x 256 tiles with ragged edges and are compared element by element;
+the workload sizes are compared on a sampled grid of rows x columns that
+includes the first and last rows/columns and tile boundaries.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import GELU_LIP, bf16_dev, bf16_host_f64, check_bf16, check_f32, dev, host
+
+te = pytest.importorskip("fp8_linear_layer_amd")
+pytestmark = pytest.mark.gpu
+
+E4, E5 = te.TE_DTYPE_E4M3, te.TE_DTYPE_E5M2
+OF = {E4: oracle.E4M3, E5: oracle.E5M2}
+FULL, FAST = te.TE_ACCUM_FULL_FP32, te.TE_ACCUM_FAST
+POLICIES = [(FULL, False), (FAST, False), (FAST, True)]  # (accum, pow2-scaled inputs)
+PID = ["full", "fast", "fast-pow2"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    te.load_library()
+
+
+def operand(seed, rows, K, dt, std=1.0, pow2=False):
+    bits = W.normal_bf16(np.random.SeedSequence(seed), (rows, K), std)
+    q, s = oracle.cast_per_token(bits, OF[dt], pow2)
+    return q, s
+
+
+def sample_idx(n, k, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, n - 1, n - 2] + [b + d for b in (255, 256, 511, 512, n // 2) for d in (0, 1)]
+    idx = np.concatenate([np.array([i for i in fixed if 0 <= i < n]), rng.integers(0, n, k)])
+    return np.unique(idx)
+
+
+def grid_entries(qa, sa, fa, qb, sb, fb, rows, cols, k0=0, K=None):
+    mi = np.repeat(rows, len(cols)).astype(np.int64)
+    ni = np.tile(cols, len(rows)).astype(np.int64)
+    o, d = oracle.gemm_nt_entries(qa, sa, fa, qb, sb, fb, mi, ni, k0, K)
+    return o.reshape(len(rows), len(cols)), d.reshape(len(rows), len(cols))
+
+
+# ------------------------------------------------------------------ wgrad
+@pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
+@pytest.mark.parametrize("da,db", [(E4, E4), (E5, E4), (E4, E5), (E5, E5)])
+@pytest.mark.parametrize("M,N,K", [(300, 520, 384), (1, 1, 128), (256, 256, 512), (513, 200, 256)])
+def test_wgrad_small(accum, pow2, da, db, M, N, K):
+    qa, sa = operand(M * 3 + K, M, K, da, pow2=pow2)
+    qb, sb = operand(N * 5 + K + 1, N, K, db, pow2=pow2)
+    out0 = W.normal_f32(np.random.SeedSequence(M + N), (M, N))
+    o, d = oracle.gemm_nt(qa, sa, OF[da], qb, sb, OF[db])
+    want, mag = oracle.wgrad(o, d, out0)
+    ld = N + 12 - (N + 12) % 4
+    buf = torch.full((M + 1, ld), 1234.5, dtype=torch.float32, device="cuda")
+    buf[:M, :N] = dev(out0)
+    out = buf[:M, :N]
+    te.te_fp8_wgrad_accum(dev(qa), dev(sa), da, dev(qb), dev(sb), db, out, accum)
+    torch.cuda.synchronize()
+    b = host(buf).numpy()
+    assert (b[:M, N:] == 1234.5).all() and (b[M:] == 1234.5).all(), "wrote outside out"
+    check_f32(b[:M, :N], want, mag, "wgrad")
+
+
+def test_wgrad_pages_ones_example():
+    """out1 = ref.clone(); out1 += x y^T makes out1/ref ~ 2; zero-initialised out gives ~ref."""
+    m, n, k = 512, 1024, 4096
+    x = W.f32_to_bf16_bits(np.ones((m, k), np.float32))
+    y = W.uniform_bf16(np.random.SeedSequence(95), (n, k))
+    qx, sx = oracle.cast_per_token(x, oracle.E4M3)
+    qy, sy = oracle.cast_per_token(y, oracle.E4M3)
+    ref = (W.bf16_bits_to_f32(x) @ W.bf16_bits_to_f32(y).T).astype(np.float32)
+    out1 = dev(ref)
+    te.te_fp8_wgrad_accum(dev(qx), dev(sx), E4, dev(qy), dev(sy), E4, out1, FULL)
+    r = host(out1).numpy() / ref
+    assert np.all(np.abs(r - 2.0) < 2e-3), (r.min(), r.max())
+    out0 = torch.zeros((m, n), dtype=torch.float32, device="cuda")
+    te.te_fp8_wgrad_accum(dev(qx), dev(sx), E4, dev(qy), dev(sy), E4, out0, FULL)
+    r0 = host(out0).numpy() / ref
+    assert np.all(np.abs(r0 - 1.0) < 2e-3)
+    # a second call doubles
+    te.te_fp8_wgrad_accum(dev(qx), dev(sx), E4, dev(qy), dev(sy), E4, out0, FULL)
+    assert np.allclose(host(out0).numpy() / ref, 2 * r0, rtol=1e-6)
+
+
+@pytest.mark.parametrize("accum", [FULL, FAST])
+def test_wgrad_deterministic(accum):
+    qa, sa = operand(1, 384, 1024, E4)
+    qb, sb = operand(2, 640, 1024, E4)
+    outs = []
+    for _ in range(2):
+        out = torch.zeros((384, 640), dtype=torch.float32, device="cuda")
+        te.te_fp8_wgrad_accum(dev(qa), dev(sa), E4, dev(qb), dev(sb), E4, out, accum)
+        outs.append(host(out).numpy())
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+@pytest.mark.parametrize("accum,pow2", [(FULL, False), (FAST, True)], ids=["full", "fast-pow2"])
+def test_wgrad_dense_workload(accum, pow2):
+    sh = W.DENSE_WGRAD.shapes
+    inp = W.dense_wgrad_inputs()
+    qa, sa = oracle.cast_per_token(inp["a"], oracle.E4M3, pow2)
+    qb, sb = oracle.cast_per_token(inp["b"], oracle.E4M3, pow2)
+    out = dev(inp["out0"])
+    te.te_fp8_wgrad_accum(dev(qa), dev(sa), E4, dev(qb), dev(sb), E4, out, accum)
+    got = host(out).numpy()
+    rows, cols = sample_idx(sh["M"], 40, 1), sample_idx(sh["N"], 40, 2)
+    o, d = grid_entries(qa, sa, oracle.E4M3, qb, sb, oracle.E4M3, rows, cols)
+    init = inp["out0"][np.ix_(rows, cols)]
+    check_f32(got[np.ix_(rows, cols)], init.astype(np.float64) + o, np.abs(init) + d, "dense wgrad")
+
+
+# ------------------------------------------------------------------ fprop
+FWD_EPIS = [te.TE_EPI_NONE, te.TE_EPI_BIAS, te.TE_EPI_BIAS | te.TE_EPI_GELU,
+            te.TE_EPI_BIAS | te.TE_EPI_GELU | te.TE_EPI_AUX_PREACT, te.TE_EPI_GELU]
+
+
+def fwd_case(M, N, K, epi, ydt, accum, pow2, xs=1.0, ws=1.0, seed=0):
+    qx, sx = operand(seed + 11, M, K, E4, xs, pow2)
+    qw, sw = operand(seed + 12, N, K, E4, ws, pow2)
+    b = W.normal_bf16(np.random.SeedSequence(seed + 13), (N,), 0.1)
+    o, d = oracle.gemm_nt(qx, sx, oracle.E4M3, qw, sw, oracle.E4M3)
+    has_b = bool(epi & te.TE_EPI_BIAS)
+    y, z, zmag = oracle.fwd_epilogue(o, d, b if has_b else None, bool(epi & te.TE_EPI_GELU))
+    return qx, sx, qw, sw, b, y, z, zmag
+
+
+@pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
+@pytest.mark.parametrize("epi", FWD_EPIS)
+@pytest.mark.parametrize("ydt", [te.TE_DTYPE_F32, te.TE_DTYPE_BF16])
+@pytest.mark.parametrize("M,N,K", [(300, 264, 512), (17, 36, 128)])
+def test_fwd_small(accum, pow2, epi, ydt, M, N, K):
+    qx, sx, qw, sw, b, y, z, zmag = fwd_case(M, N, K, epi, ydt, accum, pow2, seed=M)
+    ymag = zmag * (GELU_LIP if epi & te.TE_EPI_GELU else 1.0)
+    tdt = torch.float32 if ydt == te.TE_DTYPE_F32 else torch.bfloat16
+    ld = (N + 8) // 8 * 8
+    ybuf = torch.full((M + 1, ld), 77.0, dtype=tdt, device="cuda")
+    yv = ybuf[:M, :N]
+    pre = None
+    if epi & te.TE_EPI_AUX_PREACT:
+        prebuf = torch.full((M, ld), 55.0, dtype=torch.bfloat16, device="cuda")
+        pre = prebuf[:, :N]
+    te.te_fp8_gemm_fwd(dev(qx), dev(sx), E4, dev(qw), dev(sw), E4,
+                       bias=bf16_dev(b) if epi & te.TE_EPI_BIAS else None, epilogue=epi,
+                       y=yv, y_dtype=ydt, preact=pre, accum=accum)
+    torch.cuda.synchronize()
+    yb = host(ybuf)
+    assert torch.all(yb[:M, N:] == 77.0) and torch.all(yb[M:] == 77.0), "wrote outside y"
+    if ydt == te.TE_DTYPE_F32:
+        check_f32(yb[:M, :N].numpy(), y, ymag, "fwd y")
+    else:
+        check_bf16(bf16_host_f64(yb[:M, :N]), y, ymag, "fwd y")
+    if pre is not None:
+        pb = host(prebuf)
+        assert torch.all(pb[:, N:] == 55.0)
+        check_bf16(bf16_host_f64(pb[:, :N]), z, zmag, "fwd preact")
+
+
+def test_fwd_tiny_workload():
+    """256x256x512, bias + GELU, fp32 out (and the wgrad out+= call on the same operands)."""
+    inp = W.tiny_fprop_inputs()
+    qx, sx = oracle.cast_per_token(inp["x"], oracle.E4M3)
+    qw, sw = oracle.cast_per_token(inp["w"], oracle.E4M3)
+    o, d = oracle.gemm_nt(qx, sx, oracle.E4M3, qw, sw, oracle.E4M3)
+    y, z, zmag = oracle.fwd_epilogue(o, d, inp["b"], True)
+    for accum in (FULL, FAST):
+        yg = te.te_fp8_gemm_fwd(dev(qx), dev(sx), E4, dev(qw), dev(sw), E4, bias=bf16_dev(inp["b"]),
+                                epilogue=te.TE_EPI_BIAS | te.TE_EPI_GELU, y_dtype=te.TE_DTYPE_F32, accum=accum)
+        check_f32(host(yg).numpy(), y, zmag * GELU_LIP, "tiny fwd")
+    want, mag = oracle.wgrad(o, d, inp["out0"])
+    out = dev(inp["out0"])
+    te.te_fp8_wgrad_accum(dev(qx), dev(sx), E4, dev(qw), dev(sw), E4, out, FULL)
+    check_f32(host(out).numpy(), want, mag, "tiny wgrad")
+
+
+@pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
+def test_fwd_workload(accum, pow2):
+    sh = W.FPROP.shapes
+    inp = W.fprop_inputs()
+    qx, sx = oracle.cast_per_token(inp["x"], oracle.E4M3, pow2)
+    qw, sw = oracle.cast_per_token(inp["w"], oracle.E4M3, pow2)
+    epi = te.TE_EPI_BIAS | te.TE_EPI_GELU | te.TE_EPI_AUX_PREACT
+    pre = torch.empty((sh["M"], sh["N"]), dtype=torch.bfloat16, device="cuda")
+    yg = te.te_fp8_gemm_fwd(dev(qx), dev(sx), E4, dev(qw), dev(sw), E4, bias=bf16_dev(inp["b"]), epilogue=epi,
+                            y_dtype=te.TE_DTYPE_BF16, preact=pre, accum=accum)
+    rows, cols = sample_idx(sh["M"], 24, 3), sample_idx(sh["N"], 40, 4)
+    o, d = grid_entries(qx, sx, oracle.E4M3, qw, sw, oracle.E4M3, rows, cols)
+    y, z, zmag = oracle.fwd_epilogue(o, d, inp["b"][cols], True)
+    check_bf16(bf16_host_f64(yg)[np.ix_(rows, cols)], y, zmag * GELU_LIP, "fprop y")
+    check_bf16(bf16_host_f64(pre)[np.ix_(rows, cols)], z, zmag, "fprop preact")
+
+
+# ------------------------------------------------------------------ dgrad
+DG_EPIS = [te.TE_EPI_NONE, te.TE_EPI_DGELU, te.TE_EPI_BGRAD, te.TE_EPI_DGELU | te.TE_EPI_BGRAD]
+
+
+@pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
+@pytest.mark.parametrize("epi", DG_EPIS)
+@pytest.mark.parametrize("dxdt", [te.TE_DTYPE_F32, te.TE_DTYPE_BF16])
+@pytest.mark.parametrize("M,N,K", [(260, 300, 640), (3, 20, 128)])
+def test_dgrad_small(accum, pow2, epi, dxdt, M, N, K):
+    qa, sa = operand(M + 21, M, K, E5, 1e-3, pow2)
+    qb, sb = operand(N + 22, N, K, E4, 0.02, pow2)
+    zb = W.normal_bf16(np.random.SeedSequence(M + 23), (M, N), 1.28)
+    o, d = oracle.gemm_nt(qa, sa, oracle.E5M2, qb, sb, oracle.E4M3)
+    D, Dm, db, dbm = oracle.dgrad_epilogue(o, d, zb if epi & te.TE_EPI_DGELU else None, bool(epi & te.TE_EPI_BGRAD))
+    tdt = torch.float32 if dxdt == te.TE_DTYPE_F32 else torch.bfloat16
+    ld = N + 8 - (N + 8) % 8
+    dxbuf = torch.full((M, ld), 9.0, dtype=tdt, device="cuda")
+    bg = torch.full((N + 4,), 3.0, dtype=torch.float32, device="cuda") if epi & te.TE_EPI_BGRAD else None
+    te.te_fp8_gemm_dgrad(dev(qa), dev(sa), E5, dev(qb), dev(sb), E4, epilogue=epi,
+                         preact=bf16_dev(zb) if epi & te.TE_EPI_DGELU else None,
+                         bias_grad=bg[:N] if bg is not None else None, dx=dxbuf[:, :N], dx_dtype=dxdt, accum=accum)
+    torch.cuda.synchronize()
+    xb = host(dxbuf)
+    assert torch.all(xb[:, N:] == 9.0), "wrote outside dx"
+    if dxdt == te.TE_DTYPE_F32:
+        check_f32(xb[:, :N].numpy(), D, Dm, "dgrad dx")
+    else:
+        check_bf16(bf16_host_f64(xb[:, :N]), D, Dm, "dgrad dx")
+    if bg is not None:
+        g = host(bg).numpy()
+        assert np.all(g[N:] == 3.0)
+        check_f32(g[:N], db, dbm, "bias grad")
+
+
+@pytest.mark.parametrize("accum", [FULL, FAST])
+def test_dgrad_workload_dx(accum):
+    """dX[8192x4096] = dY[8192x14336] (e5m2) W^T (e4m3), bf16 out."""
+    sh = W.DGRAD.shapes
+    inp = W.dgrad_inputs()
+    qa, sa = oracle.cast_per_token(inp["dy"], oracle.E5M2)
+    qb, sb = oracle.cast_per_token(inp["wt"], oracle.E4M3)
+    dx = te.te_fp8_gemm_dgrad(dev(qa), dev(sa), E5, dev(qb), dev(sb), E4, accum=accum)
+    rows, cols = sample_idx(sh["M"], 24, 5), sample_idx(sh["N"], 40, 6)
+    o, d = grid_entries(qa, sa, oracle.E5M2, qb, sb, oracle.E4M3, rows, cols)
+    check_bf16(bf16_host_f64(dx)[np.ix_(rows, cols)], o, d, "dgrad dX")
+
+
+def test_dgrad_workload_dgelu_bgrad():
+    """dZ[8192x14336] = dO (e5m2) W2^T (e4m3) through GELU'(Z), bias grad = its column sums."""
+    sh = W.DGRAD.shapes
+    M, N, K = sh["M"], sh["K"], sh["N"]  # the pre-activation GEMM: out features 14336, contraction 4096
+    inp = W.dgrad_inputs()
+    qa, sa = oracle.cast_per_token(inp["do"], oracle.E5M2)
+    qb, sb = oracle.cast_per_token(inp["w2t"], oracle.E4M3)
+    z = inp["z"]
+    bg = torch.empty((N,), dtype=torch.float32, device="cuda")
+    dz = te.te_fp8_gemm_dgrad(dev(qa), dev(sa), E5, dev(qb), dev(sb), E4,
+                              epilogue=te.TE_EPI_DGELU | te.TE_EPI_BGRAD, preact=bf16_dev(z), bias_grad=bg,
+                              accum=FULL)
+    rows, cols = sample_idx(M, 16, 7), sample_idx(N, 24, 8)
+    o, d = grid_entries(qa, sa, oracle.E5M2, qb, sb, oracle.E4M3, rows, cols)
+    D, Dm, _, _ = oracle.dgrad_epilogue(o, d, z[np.ix_(rows, cols)])
+    check_bf16(bf16_host_f64(dz)[np.ix_(rows, cols)], D, Dm, "dZ")
+    bcols = cols[:8]
+    o, d = grid_entries(qa, sa, oracle.E5M2, qb, sb, oracle.E4M3, np.arange(M), bcols)
+    _, _, db, dbm = oracle.dgrad_epilogue(o, d, z[:, bcols], bgrad=True)
+    check_f32(host(bg).numpy()[bcols], db, dbm, "bias grad")
+
+
+# ------------------------------------------------------------------ K-grouped
+@pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
+def test_kgrouped_small(accum, pow2):
+    gk = np.array([256, 0, 128, 384, 0, 128], np.int64)
+    M, N, S = 200, 300, int(gk.sum())
+    qa, sa = operand(31, M, S, E4, pow2=pow2)
+    qb, sb = operand(32, N, S, E4, pow2=pow2)
+    init = W.normal_f32(np.random.SeedSequence(33), (len(gk), M, N))
+    want, mag = oracle.kgrouped_wgrad(qa, sa, oracle.E4M3, qb, sb, oracle.E4M3, gk, init)
+    out = dev(init)
+    te.te_fp8_kgrouped_wgrad(dev(qa), dev(sa), E4, dev(qb), dev(sb), E4, gk.tolist(), out, accum)
+    got = host(out).numpy()
+    for g in range(len(gk)):
+        if gk[g] == 0:
+            assert np.array_equal(got[g].view(np.uint32), init[g].view(np.uint32)), f"empty group {g} touched"
+        else:
+            check_f32(got[g], want[g], mag[g], f"group {g}")
+
+
+def test_kgrouped_many_groups():
+    """More groups than one launch carries: 300 groups of 128 or 0 columns."""
+    rng = np.random.default_rng(4)
+    gk = (rng.integers(0, 2, 300) * 128).astype(np.int64)
+    gk[0] = 128
+    M, N, S = 16, 24, int(gk.sum())
+    qa, sa = operand(41, M, S, E4)
+    qb, sb = operand(42, N, S, E4)
+    init = W.normal_f32(np.random.SeedSequence(43), (len(gk), M, N))
+    want, mag = oracle.kgrouped_wgrad(qa, sa, oracle.E4M3, qb, sb, oracle.E4M3, gk, init)
+    out = dev(init)
+    te.te_fp8_kgrouped_wgrad(dev(qa), dev(sa), E4, dev(qb), dev(sb), E4, gk.tolist(), out, FULL)
+    check_f32(host(out).numpy(), want, mag, "300 groups")
+
+
+def test_kgrouped_workload():
+    sh = W.KGROUPED.shapes
+    inp = W.kgrouped_inputs()
+    gk = inp["group_k"]
+    qa, sa = oracle.cast_per_token(inp["a"], oracle.E4M3)
+    qb, sb = oracle.cast_per_token(inp["b"], oracle.E4M3)
+    out = dev(inp["out0"])
+    te.te_fp8_kgrouped_wgrad(dev(qa), dev(sa), E4, dev(qb), dev(sb), E4, gk.tolist(), out, FULL)
+    got = host(out).numpy()
+    offs = np.concatenate([[0], np.cumsum(gk)])
+    for g in range(sh["G"]):
+        rows, cols = sample_idx(sh["M"], 8, 10 + g), sample_idx(sh["N"], 12, 20 + g)
+        o, d = grid_entries(qa, sa, oracle.E4M3, qb, sb, oracle.E4M3, rows, cols, int(offs[g]), int(gk[g]))
+        init = inp["out0"][g][np.ix_(rows, cols)]
+        check_f32(got[g][np.ix_(rows, cols)], init.astype(np.float64) + o, np.abs(init) + d, f"expert {g}")
