@@ -1,0 +1,276 @@
+"""Benchmark of the scaled-FP8 Linear-layer hot path on one MI355X.
+
+One step = the dense weight-gradient path at 7168 x 2112 x 4096: per-token
+1x128 e4m3 cast of both bf16 operands (dY^T [7168, 4096] and X^T [2112, 4096])
+followed by the block-scaled FP8 GEMM that accumulates out[7168, 2112] += A B^T
+in fp32 with full-precision promotion.  Inputs are seeded synthetic bf16
+N(0, 1) already resident in HBM; the fp32 accumulator is pre-filled N(0, 1).
+
+Printed: one JSON line with the whole-step throughput (2 M N K flop per step),
+the GEMM kernel's roofline fraction against the FP8 dense matrix-core peak
+(kernel time from HIP events on the launch stream), the oracle's CPU
+throughput on a bounded sample, and per-kernel timings of the other
+workloads (fprop with bias+GELU at 8192 x 14336 x 4096 in both accumulation
+policies, dgrad at 8192 x 4096 x 14336 and its dGELU+bias-grad form, the
+e5m2 cast of the gradient, and the 8-expert K-grouped wgrad).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 matrix-core peak
+HBM_PEAK_GBS = 8000.0
+PAGES_TFLOPS_SAME_SHAPE = 920.0  # dense wgrad 7168x2112x4096 as published (hardware not named)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of the oracle's CPU sample")
+    ap.add_argument("--ref-copy", action="store_true",
+                    help="first run three plain 1 GiB device copies (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "cast.hip"):
+        with open(os.path.join(ROOT, "fp8_linear_layer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_key: str):
+    """HBM bytes per launch of the GEMM kernel from the committed PMC summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_hash():
+        return None
+    entry = rec.get("kernels", {}).get(kernel_key)
+    return None if entry is None else entry.get("hbm_bytes_per_launch")
+
+
+def timed(fn, reps, warm=3):
+    import torch
+    for _ in range(warm):
+        fn()
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(reps):
+        st.record()
+        fn()
+        en.record()
+        en.synchronize()
+        times.append(st.elapsed_time(en))
+    return float(np.median(times)), float(np.min(times))
+
+
+def breakdown(te, torch):
+    """Kernel times of the other workloads (inputs generated on the GPU, seeded)."""
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    out = {}
+
+    def randn(shape, std, seed):
+        g.manual_seed(seed)
+        return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
+
+    E4, E5 = te.TE_DTYPE_E4M3, te.TE_DTYPE_E5M2
+    # fprop 8192 x 14336 x 4096, bias + GELU (+ saved pre-activation), bf16 out
+    M, N, K = 8192, 14336, 4096
+    x, w, b = randn((M, K), 1.0, 1), randn((N, K), 0.02, 2), randn((N,), 0.1, 3)
+    qx, sx = te.te_cast_fp8_per_token(x, E4)
+    qw, sw = te.te_cast_fp8_per_token(w, E4)
+    px, psx = te.te_cast_fp8_per_token(x, E4, te.TE_CAST_POW2_SCALE)
+    pw, psw = te.te_cast_fp8_per_token(w, E4, te.TE_CAST_POW2_SCALE)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    z = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    flop = 2.0 * M * N * K
+    cases = {
+        "fprop_none_full": (qx, sx, qw, sw, te.TE_EPI_NONE, te.TE_ACCUM_FULL_FP32),
+        "fprop_bias_gelu_full": (qx, sx, qw, sw, te.TE_EPI_BIAS | te.TE_EPI_GELU, te.TE_ACCUM_FULL_FP32),
+        "fprop_none_fast": (qx, sx, qw, sw, te.TE_EPI_NONE, te.TE_ACCUM_FAST),
+        "fprop_none_fast_pow2": (px, psx, pw, psw, te.TE_EPI_NONE, te.TE_ACCUM_FAST),
+        "fprop_bias_gelu_fast_pow2": (px, psx, pw, psw, te.TE_EPI_BIAS | te.TE_EPI_GELU, te.TE_ACCUM_FAST),
+        "fprop_bias_gelu_aux_fast_pow2": (px, psx, pw, psw, te.TE_EPI_BIAS | te.TE_EPI_GELU | te.TE_EPI_AUX_PREACT,
+                                          te.TE_ACCUM_FAST),
+    }
+    for name, (a, sa, bb, sb, epi, acc) in cases.items():
+        fn = lambda: te.te_fp8_gemm_fwd(a, sa, E4, bb, sb, E4, bias=b if epi & te.TE_EPI_BIAS else None,
+                                        epilogue=epi, y=y, preact=z if epi & te.TE_EPI_AUX_PREACT else None,
+                                        accum=acc)
+        med, mn = timed(fn, 10)
+        out[name] = {"shape": [M, N, K], "ms": round(med, 4), "tflops": round(flop / med / 1e9, 1)}
+    cast_bytes = M * K * 2 + M * K + M * (K // 128) * 4
+    med, _ = timed(lambda: te.te_cast_fp8_per_token(x, E4, q=qx, scales=sx), 10)
+    out["cast_e4m3_8192x4096"] = {"ms": round(med, 4), "gbs": round(cast_bytes / med / 1e6, 1)}
+    del x, w, qw, sw, px, psx, pw, psw, y
+
+    # dgrad: dX [8192 x 4096] = dY [8192 x 14336] (e5m2) W^T (e4m3)
+    M, N, K = 8192, 4096, 14336
+    dy, wt = randn((M, K), 1e-3, 4), randn((N, K), 0.02, 5)
+    qd, sd = te.te_cast_fp8_per_token(dy, E5)
+    qt, st = te.te_cast_fp8_per_token(wt, E4)
+    dx = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    med, _ = timed(lambda: te.te_fp8_gemm_dgrad(qd, sd, E5, qt, st, E4, dx=dx, accum=te.TE_ACCUM_FULL_FP32), 10)
+    out["dgrad_dx_full"] = {"shape": [M, N, K], "ms": round(med, 4), "tflops": round(2.0 * M * N * K / med / 1e9, 1)}
+    cast_bytes = M * K * 2 + M * K + M * (K // 128) * 4
+    med, _ = timed(lambda: te.te_cast_fp8_per_token(dy, E5, q=qd, scales=sd), 10)
+    out["cast_e5m2_8192x14336"] = {"ms": round(med, 4), "gbs": round(cast_bytes / med / 1e6, 1),
+                                   "frac_hbm": round(cast_bytes / med / 1e6 / HBM_PEAK_GBS, 3)}
+    del dy, wt, qd, sd, qt, st, dx
+    # dgrad with dGELU + bias-grad at the pre-activation shape [8192 x 14336], contraction 4096
+    M, N, K = 8192, 14336, 4096
+    do, w2t, zz = randn((M, K), 1e-3, 6), randn((N, K), 0.02, 7), randn((M, N), 1.28, 8)
+    qo, so = te.te_cast_fp8_per_token(do, E5)
+    q2, s2 = te.te_cast_fp8_per_token(w2t, E4)
+    dz = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    bg = torch.empty((N,), dtype=torch.float32, device=dev)
+    med0, _ = timed(lambda: te.te_fp8_gemm_dgrad(qo, so, E5, q2, s2, E4, dx=dz, accum=te.TE_ACCUM_FULL_FP32), 10)
+    med1, _ = timed(lambda: te.te_fp8_gemm_dgrad(qo, so, E5, q2, s2, E4, epilogue=te.TE_EPI_DGELU | te.TE_EPI_BGRAD,
+                                                 preact=zz, bias_grad=bg, dx=dz, accum=te.TE_ACCUM_FULL_FP32), 10)
+    f = 2.0 * M * N * K
+    out["dgrad_dz_none_full"] = {"shape": [M, N, K], "ms": round(med0, 4), "tflops": round(f / med0 / 1e9, 1)}
+    out["dgrad_dz_dgelu_bgrad_full"] = {"shape": [M, N, K], "ms": round(med1, 4), "tflops": round(f / med1 / 1e9, 1),
+                                        "epilogue_overhead": round(med1 / med0 - 1.0, 3)}
+    del do, w2t, zz, qo, so, q2, s2, dz, bg
+
+    # K-grouped wgrad: 8 experts, 2048 x 7168, per-expert K multinomial in blocks of 128 summing to 32768
+    import workloads as W
+    G, M, N, S = 8, 2048, 7168, 32768
+    gk = W.moe_group_k(np.random.SeedSequence(5).spawn(4)[2], G, S).tolist()
+    a, bm = randn((M, S), 1.0, 9), randn((N, S), 1.0, 10)
+    qa, sa = te.te_cast_fp8_per_token(a, E4)
+    qb, sb = te.te_cast_fp8_per_token(bm, E4)
+    o = torch.zeros((G, M, N), dtype=torch.float32, device=dev)
+    med, _ = timed(lambda: te.te_fp8_kgrouped_wgrad(qa, sa, E4, qb, sb, E4, gk, o, te.TE_ACCUM_FULL_FP32), 10)
+    f = 2.0 * M * N * S
+    out["kgrouped_wgrad_full"] = {"group_k": gk, "ms": round(med, 4), "tflops": round(f / med / 1e9, 1)}
+    return out
+
+
+def cpu_baseline(rows: int):
+    """The oracle (as it stands) on a bounded sample of the same step: cast `rows` rows of
+    A and all of B, then `rows` x N outputs of the wgrad product; scaled to TFLOP/s."""
+    import oracle
+    import workloads as W
+    M, N, K = 7168, 2112, 4096
+    s = np.random.SeedSequence(2).spawn(3)
+    a = W.normal_bf16(s[0], (M, K))[:rows]
+    b = W.normal_bf16(s[1], (N, K))
+    out0 = W.normal_f32(s[2], (M, N))[:rows]
+    t0 = time.perf_counter()
+    qa, sa = oracle.cast_per_token(a, oracle.E4M3)
+    qb, sb = oracle.cast_per_token(b, oracle.E4M3)
+    o, d = oracle.gemm_nt(qa, sa, oracle.E4M3, qb, sb, oracle.E4M3)
+    oracle.wgrad(o, d, out0)
+    dt = time.perf_counter() - t0
+    flop = 2.0 * rows * N * K
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{rows} of 7168 output rows (all 2112 columns, K=4096) incl. the cast of those rows and of B; "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    import fp8_linear_layer_amd as te
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    te.load_library()
+    torch.cuda.set_device(0)
+    M, N, K = 7168, 2112, 4096
+    inp = W.dense_wgrad_inputs()
+    a = torch.from_numpy(inp["a"]).cuda().view(torch.bfloat16)
+    b = torch.from_numpy(inp["b"]).cuda().view(torch.bfloat16)
+    out = torch.from_numpy(inp["out0"]).cuda()
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+    qb = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((N, K // 128), dtype=torch.float32, device="cuda")
+    E4 = te.TE_DTYPE_E4M3
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def step(i=None):
+        te.te_cast_fp8_per_token(a, E4, q=qa, scales=sa)
+        te.te_cast_fp8_per_token(b, E4, q=qb, scales=sb)
+        if i is not None:
+            ev[i][0].record(stream)
+        te.te_fp8_wgrad_accum(qa, sa, E4, qb, sb, E4, out, te.TE_ACCUM_FULL_FP32)
+        if i is not None:
+            ev[i][1].record(stream)
+
+    if args.ref_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    ms_step = total * 1e3 / args.steps
+    gemm_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    flop = 2.0 * M * N * K
+    value = flop / (ms_step * 1e-3) / 1e12
+    achieved = flop / (gemm_ms * 1e-3) / 1e12
+    traffic = traffic_from_profile("wgrad_full_7168x2112x4096")
+    rec = {
+        "metric": "FP8 GEMM TFLOPS (fprop/dgrad/wgrad) and % of MI355X FP8 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / PAGES_TFLOPS_SAME_SHAPE, 4),
+        "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {"workload": "dense-wgrad-7168x2112x4096", "M": M, "N": N, "K": K,
+                   "step": "cast A + cast B (bf16 -> e4m3, 1x128 fp32 scales) + out += A B^T (fp32)",
+                   "accum": "full_fp32", "frac_of_fp8_peak": round(value / MFMA_FP8_PEAK_TFLOPS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "gemm_nt_kernel (wgrad, full)", "kernel_ms": round(gemm_ms, 5)},
+    }
+    if not args.no_breakdown:
+        rec["breakdown"] = breakdown(te, torch)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

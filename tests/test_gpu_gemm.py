@@ -219,8 +219,10 @@ def test_dgrad_small(accum, pow2, epi, dxdt, M, N, K):
     ld = N + 8 - (N + 8) % 8
     dxbuf = torch.full((M, ld), 9.0, dtype=tdt, device="cuda")
     bg = torch.full((N + 4,), 3.0, dtype=torch.float32, device="cuda") if epi & te.TE_EPI_BGRAD else None
+    zpad = np.zeros((M, ld), np.uint16)
+    zpad[:, :N] = zb
     te.te_fp8_gemm_dgrad(dev(qa), dev(sa), E5, dev(qb), dev(sb), E4, epilogue=epi,
-                         preact=bf16_dev(zb) if epi & te.TE_EPI_DGELU else None,
+                         preact=bf16_dev(zpad)[:, :N] if epi & te.TE_EPI_DGELU else None,
                          bias_grad=bg[:N] if bg is not None else None, dx=dxbuf[:, :N], dx_dtype=dxdt, accum=accum)
     torch.cuda.synchronize()
     xb = host(dxbuf)
