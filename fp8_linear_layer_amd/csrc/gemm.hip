@@ -248,8 +248,9 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p)
         const int tid = threadIdx.x;
         const float* srow = tid < kBM ? p.sa + min(m0 + tid, p.M - 1) * p.lsa
                                       : p.sb + min(n0 + (tid - kBM), p.N - 1) * p.lsb;
+        // independent loads (no short-circuit), so they are all in flight at once
         bool ok = true;
-        for (int kb = kb0; kb < kb0 + nkb; ++kb) ok = ok && is_pow2_scale(srow[kb]);
+        for (int kb = kb0; kb < kb0 + nkb; ++kb) ok &= is_pow2_scale(srow[kb]);
         if (__syncthreads_and(ok)) {
             main_loop<kFmtA, kFmtB, true>(p, smem, acc, m0, n0, kb0, nkb, wave, lane);
         } else {
