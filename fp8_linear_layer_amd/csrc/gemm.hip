@@ -27,7 +27,9 @@
 //    16-byte (fp32) / 8-byte (bf16) vectors along the output row.
 //  * Operands stream global -> LDS with global_load_lds_dwordx4 (no register
 //    staging), double-buffered: while the matrix cores consume stage s, the
-//    loads for stage s+1 are in flight.  Each 128-byte LDS row stores its
+//    loads for stage s+1 are in flight (restrict-qualified stage pointers keep
+//    the compiler from making this stage's reads wait for them, and the
+//    barrier carries no fence that would drain them).  Each 128-byte LDS row stores its
 //    16-byte chunk c at slot c ^ ((row >> 1) & 7), so the 16 rows read by one
 //    16-lane group of a ds_read_b128 fall in 16 distinct 16-byte bank groups.
 //    The two scale vectors of the block ride along in the same stage.
@@ -145,64 +147,85 @@ __device__ __forceinline__ float dgelu(float z)
     return fmaf(2.0f * kGeluC * z * s * one_minus_s, fmaf(3.0f * kGeluA, z2, 1.0f), s);
 }
 
-// The K loop.  Stage 0 has been issued by the caller.  kChain: every scale is a
-// power of two and the block scales ride in the matrix-core instruction;
-// otherwise each block's product starts from zero and is promoted in fp32.
+// Workgroup barrier without a memory fence: callers wait for their own
+// global->LDS copies explicitly; this waits for the wave's own LDS reads and
+// syncs.  (A fenced __syncthreads() would also drain the next stage's copies.)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// One contraction block, held in `stage`; the copies of the next block go to
+// `other`.  The two stages are restrict-qualified so the compiler knows the
+// copies into `other` do not feed the reads of `stage` and does not make
+// those reads wait for them: the next block's copies overlap this block's
+// matrix-core work.  kChain: every scale is a power of two and the block
+// scales ride in the matrix-core instruction; otherwise each block's product
+// starts from zero and is promoted in fp32.
 template <int kFmtA, int kFmtB, bool kChain>
-__device__ __forceinline__ void main_loop(const GemmArgs& p, uint8_t* smem, v4f (&acc)[kTM][kTN],
-                                          int64_t m0, int64_t n0, int kb0, int nkb, int wave, int lane)
+__device__ __forceinline__ void block_step(const GemmArgs& p, uint8_t* __restrict__ stage,
+                                           uint8_t* __restrict__ other, v4f (&acc)[kTM][kTN], int64_t m0,
+                                           int64_t n0, int kb0, int it, int nkb, int wave, int lane)
 {
     const int wm = wave / kWavesN, wn = wave % kWavesN;
     const int r16 = lane & 15, q4 = lane >> 4;
-    for (int it = 0; it < nkb; ++it) {
-        uint8_t* stage = smem + (it & 1) * kStageBytes;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (it + 1 < nkb) load_stage(p, smem + ((it + 1) & 1) * kStageBytes, m0, n0, kb0 + it + 1, wave, lane);
+    // this block's copies (the only ones in flight) have landed everywhere, and
+    // every wave is done reading `other` (the previous block)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    if (it + 1 < nkb) load_stage(p, other, m0, n0, kb0 + it + 1, wave, lane);
 
-        const uint8_t* As = stage;
-        const uint8_t* Bs = stage + kTileA;
-        const float* sAs = reinterpret_cast<const float*>(stage + kTileA + kTileB);
-        const float* sBs = sAs + kBM;
+    const uint8_t* As = stage;
+    const uint8_t* Bs = stage + kTileA;
+    const float* sAs = reinterpret_cast<const float*>(stage + kTileA + kTileB);
+    const float* sBs = sAs + kBM;
 
-        v8i bf[kTN];
+    v8i bf[kTN];
 #pragma unroll
-        for (int j = 0; j < kTN; ++j) bf[j] = read_frag(Bs, wn * kWN + j * 16 + r16, q4);
+    for (int j = 0; j < kTN; ++j) bf[j] = read_frag(Bs, wn * kWN + j * 16 + r16, q4);
 
-        if (kChain) {
-            // E8M0 exponent of a positive normal power of two = its fp32 exponent field
-            int eb[kTN];
+    if (kChain) {
+        // E8M0 exponent of a positive normal power of two = its fp32 exponent field
+        int eb[kTN];
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) eb[j] = (int)(__builtin_bit_cast(uint32_t, sBs[wn * kWN + j * 16 + r16]) >> 23);
+#pragma unroll
+        for (int i = 0; i < kTM; ++i) {
+            const int ea = (int)(__builtin_bit_cast(uint32_t, sAs[wm * kWM + i * 16 + r16]) >> 23);
+            const v8i af = read_frag(As, wm * kWM + i * 16 + r16, q4);
 #pragma unroll
             for (int j = 0; j < kTN; ++j)
-                eb[j] = (int)(__builtin_bit_cast(uint32_t, sBs[wn * kWN + j * 16 + r16]) >> 23);
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], kFmtB, kFmtA, 0,
+                                                                             eb[j], 0, ea);
+        }
+    } else {
+        float4 sb[kTN];
 #pragma unroll
-            for (int i = 0; i < kTM; ++i) {
-                const int ea = (int)(__builtin_bit_cast(uint32_t, sAs[wm * kWM + i * 16 + r16]) >> 23);
-                const v8i af = read_frag(As, wm * kWM + i * 16 + r16, q4);
+        for (int j = 0; j < kTN; ++j) sb[j] = *reinterpret_cast<const float4*>(sBs + wn * kWN + j * 16 + q4 * 4);
 #pragma unroll
-                for (int j = 0; j < kTN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        bf[j], af, acc[i][j], kFmtB, kFmtA, 0, eb[j], 0, ea);
-            }
-        } else {
-            float4 sb[kTN];
+        for (int i = 0; i < kTM; ++i) {
+            const float sa = sAs[wm * kWM + i * 16 + r16];
+            const v8i af = read_frag(As, wm * kWM + i * 16 + r16, q4);
 #pragma unroll
-            for (int j = 0; j < kTN; ++j) sb[j] = *reinterpret_cast<const float4*>(sBs + wn * kWN + j * 16 + q4 * 4);
-#pragma unroll
-            for (int i = 0; i < kTM; ++i) {
-                const float sa = sAs[wm * kWM + i * 16 + r16];
-                const v8i af = read_frag(As, wm * kWM + i * 16 + r16, q4);
-#pragma unroll
-                for (int j = 0; j < kTN; ++j) {
-                    const v4f P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        bf[j], af, v4f{0.f, 0.f, 0.f, 0.f}, kFmtB, kFmtA, 0, 0, 0, 0);
-                    acc[i][j][0] = fmaf(P[0], sa * sb[j].x, acc[i][j][0]);
-                    acc[i][j][1] = fmaf(P[1], sa * sb[j].y, acc[i][j][1]);
-                    acc[i][j][2] = fmaf(P[2], sa * sb[j].z, acc[i][j][2]);
-                    acc[i][j][3] = fmaf(P[3], sa * sb[j].w, acc[i][j][3]);
-                }
+            for (int j = 0; j < kTN; ++j) {
+                const v4f P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, v4f{0.f, 0.f, 0.f, 0.f},
+                                                                               kFmtB, kFmtA, 0, 0, 0, 0);
+                acc[i][j][0] = fmaf(P[0], sa * sb[j].x, acc[i][j][0]);
+                acc[i][j][1] = fmaf(P[1], sa * sb[j].y, acc[i][j][1]);
+                acc[i][j][2] = fmaf(P[2], sa * sb[j].z, acc[i][j][2]);
+                acc[i][j][3] = fmaf(P[3], sa * sb[j].w, acc[i][j][3]);
             }
         }
+    }
+}
+
+// The contraction loop over a double-buffered pair of stages; stage 0 has
+// been issued by the caller.
+template <int kFmtA, int kFmtB, bool kChain>
+__device__ __forceinline__ void main_loop(const GemmArgs& p, uint8_t* smem, v4f (&acc)[kTM][kTN], int64_t m0,
+                                          int64_t n0, int kb0, int nkb, int wave, int lane)
+{
+    for (int it = 0; it < nkb; ++it) {
+        uint8_t* cur = smem + (it & 1) * kStageBytes;
+        uint8_t* oth = smem + ((it + 1) & 1) * kStageBytes;
+        block_step<kFmtA, kFmtB, kChain>(p, cur, oth, acc, m0, n0, kb0, it, nkb, wave, lane);
     }
 }
 
