@@ -62,6 +62,8 @@ bool is_fp8(te_dtype_t d) { return d == TE_DTYPE_E4M3 || d == TE_DTYPE_E5M2; }
 int to_fmt(te_dtype_t d) { return d == TE_DTYPE_E4M3 ? tefp8::FMT_E4M3 : tefp8::FMT_E5M2; }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
+// A 256-row operand tile is addressed through one buffer resource (< 2 GiB range).
+constexpr int64_t kMaxK = (int64_t)1 << 22;
 
 // Checks shared by every GEMM entry point.
 te_status_t check_operands(const char* fn, const void* a, const float* sa, te_dtype_t da, const void* b,
@@ -72,8 +74,8 @@ te_status_t check_operands(const char* fn, const void* a, const float* sa, te_dt
         return fail(TE_ERR_INVALID_ARGUMENT, "%s: operand dtypes must be TE_DTYPE_E4M3 or TE_DTYPE_E5M2 (got %d, %d)", fn, (int)da, (int)db);
     if (M < 1 || N < 1 || M >= kMaxDim || N >= kMaxDim)
         return fail(TE_ERR_INVALID_ARGUMENT, "%s: M and N must be in [1, 2^31) (got M=%lld N=%lld)", fn, (long long)M, (long long)N);
-    if (K < 128 || K % 128 != 0 || K >= kMaxDim)
-        return fail(TE_ERR_INVALID_ARGUMENT, "%s: K must be a positive multiple of 128 below 2^31 (got %lld)", fn, (long long)K);
+    if (K < 128 || K % 128 != 0 || K > kMaxK)
+        return fail(TE_ERR_INVALID_ARGUMENT, "%s: K must be a positive multiple of 128 up to 2^22 (got %lld)", fn, (long long)K);
     if (accum != TE_ACCUM_FULL_FP32 && accum != TE_ACCUM_FAST)
         return fail(TE_ERR_INVALID_ARGUMENT, "%s: accum must be TE_ACCUM_FULL_FP32 or TE_ACCUM_FAST (got %d)", fn, (int)accum);
     if (!aligned(a, 16) || !aligned(b, 16)) return fail(TE_ERR_MISALIGNED, "%s: fp8 operands must be 16-byte aligned", fn);
@@ -305,7 +307,7 @@ te_status_t te_fp8_kgrouped_wgrad(const void* a, const float* a_scales, te_dtype
         if (G < 1 || G > 1024) return fail(TE_ERR_INVALID_ARGUMENT, "%s: G must be in [1, 1024] (got %d)", fn, (int)G);
         int64_t sumk = 0;
         for (int32_t g = 0; g < G; ++g) {
-            if (group_k[g] < 0 || group_k[g] % 128 != 0 || group_k[g] >= kMaxDim)
+            if (group_k[g] < 0 || group_k[g] % 128 != 0 || group_k[g] > kMaxK)
                 return fail(TE_ERR_INVALID_ARGUMENT, "%s: group_k[%d] = %lld is not a non-negative multiple of 128", fn, (int)g,
                             (long long)group_k[g]);
             sumk += group_k[g];

@@ -69,29 +69,49 @@ static_assert(kBM + kBN == kThreads, "one scale per thread per stage");
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
-// Issue the global -> LDS copies of one 128-deep stage (A tile, B tile, scales).
-__device__ __forceinline__ void load_stage(const GemmArgs& p, uint8_t* stage, int64_t m0, int64_t n0,
-                                           int kb, int wave, int lane)
+// Per-tile buffer resources: bases at the tile's first row, ranges cut at the
+// last valid row (rows past it read as zero: no clamping, no faults).
+struct TileSrc {
+    __amdgpu_buffer_rsrc_t a, b, sa, sb;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes)
 {
-    const int64_t kcol = (int64_t)kb * kBK;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)min(bytes, (int64_t)0x7FFFFFFF),
+                                             0x00020000);
+}
+
+__device__ __forceinline__ TileSrc tile_src(const GemmArgs& p, int64_t m0, int64_t n0)
+{
+    TileSrc s;
+    s.a = make_rsrc(p.a + m0 * p.lda, min((int64_t)kBM, p.M - m0) * p.lda);
+    s.b = make_rsrc(p.b + n0 * p.ldb, min((int64_t)kBN, p.N - n0) * p.ldb);
+    s.sa = make_rsrc(p.sa + m0 * p.lsa, min((int64_t)kBM, p.M - m0) * p.lsa * 4);
+    s.sb = make_rsrc(p.sb + n0 * p.lsb, min((int64_t)kBN, p.N - n0) * p.lsb * 4);
+    return s;
+}
+
+// Issue the global -> LDS copies of one 128-deep stage (A tile, B tile, scales).
+__device__ __forceinline__ void load_stage(const GemmArgs& p, const TileSrc& src, uint8_t* stage, int kb, int wave,
+                                           int lane)
+{
+    const int kcol = kb * kBK;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int blk = wave * 4 + t;                 // 1 KiB block = 8 rows of 128 bytes
         const int ci = blk * 64 + lane;               // 16-byte chunk index within the tile
         const int row = ci >> 3;
         const int chunk = (ci & 7) ^ ((row >> 1) & 7);
-        const int64_t ga = min(m0 + row, p.M - 1);
-        const int64_t gb = min(n0 + row, p.N - 1);
-        __builtin_amdgcn_global_load_lds(p.a + ga * p.lda + kcol + chunk * 16,
-                                         (lds_ptr_t)(stage + blk * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(p.b + gb * p.ldb + kcol + chunk * 16,
-                                         (lds_ptr_t)(stage + kTileA + blk * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.a, (lds_ptr_t)(stage + blk * 1024), 16,
+                                                 (uint32_t)(row * p.lda + chunk * 16), kcol, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.b, (lds_ptr_t)(stage + kTileA + blk * 1024), 16,
+                                                 (uint32_t)(row * p.ldb + chunk * 16), kcol, 0, 0);
     }
     // scales: waves 0-3 fetch sA for the 256 tile rows, waves 4-7 sB for the 256 tile columns
-    const float* src;
-    if (wave < 4) src = p.sa + min(m0 + wave * 64 + lane, p.M - 1) * p.lsa + kb;
-    else src = p.sb + min(n0 + (wave - 4) * 64 + lane, p.N - 1) * p.lsb + kb;
-    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(stage + kTileA + kTileB + wave * 256), 4, 0, 0);
+    const bool is_a = wave < 4;
+    const int r = (is_a ? wave : wave - 4) * 64 + lane;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? src.sa : src.sb, (lds_ptr_t)(stage + kTileA + kTileB + wave * 256),
+                                             4, (uint32_t)(r * (is_a ? p.lsa : p.lsb) * 4), kb * 4, 0, 0);
 }
 
 __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int q4)
@@ -161,8 +181,8 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // starts from zero and is promoted in fp32.
 template <int kFmtA, int kFmtB, bool kChain>
 __device__ __forceinline__ void block_step(const GemmArgs& p, uint8_t* __restrict__ stage,
-                                           uint8_t* __restrict__ other, v4f (&acc)[kTM][kTN], int64_t m0,
-                                           int64_t n0, int kb0, int it, int nkb, int wave, int lane)
+                                           uint8_t* __restrict__ other, v4f (&acc)[kTM][kTN], const TileSrc& src,
+                                           int kb0, int it, int nkb, int wave, int lane)
 {
     const int wm = wave / kWavesN, wn = wave % kWavesN;
     const int r16 = lane & 15, q4 = lane >> 4;
@@ -170,7 +190,7 @@ __device__ __forceinline__ void block_step(const GemmArgs& p, uint8_t* __restric
     // every wave is done reading `other` (the previous block)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
-    if (it + 1 < nkb) load_stage(p, other, m0, n0, kb0 + it + 1, wave, lane);
+    if (it + 1 < nkb) load_stage(p, src, other, kb0 + it + 1, wave, lane);
 
     const uint8_t* As = stage;
     const uint8_t* Bs = stage + kTileA;
@@ -186,10 +206,21 @@ __device__ __forceinline__ void block_step(const GemmArgs& p, uint8_t* __restric
         int eb[kTN];
 #pragma unroll
         for (int j = 0; j < kTN; ++j) eb[j] = (int)(__builtin_bit_cast(uint32_t, sBs[wn * kWN + j * 16 + r16]) >> 23);
+        v8i afq[3];
+        int eaq[3];
+#pragma unroll
+        for (int d = 0; d < 3 - 1; ++d) {
+            afq[d] = read_frag(As, wm * kWM + d * 16 + r16, q4);
+            eaq[d] = (int)(__builtin_bit_cast(uint32_t, sAs[wm * kWM + d * 16 + r16]) >> 23);
+        }
 #pragma unroll
         for (int i = 0; i < kTM; ++i) {
-            const int ea = (int)(__builtin_bit_cast(uint32_t, sAs[wm * kWM + i * 16 + r16]) >> 23);
-            const v8i af = read_frag(As, wm * kWM + i * 16 + r16, q4);
+            if (i + 3 - 1 < kTM) {
+                afq[(i + 3 - 1) % 3] = read_frag(As, wm * kWM + (i + 3 - 1) * 16 + r16, q4);
+                eaq[(i + 3 - 1) % 3] = (int)(__builtin_bit_cast(uint32_t, sAs[wm * kWM + (i + 3 - 1) * 16 + r16]) >> 23);
+            }
+            const v8i af = afq[i % 3];
+            const int ea = eaq[i % 3];
 #pragma unroll
             for (int j = 0; j < kTN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], kFmtB, kFmtA, 0,
@@ -199,10 +230,21 @@ __device__ __forceinline__ void block_step(const GemmArgs& p, uint8_t* __restric
         float4 sb[kTN];
 #pragma unroll
         for (int j = 0; j < kTN; ++j) sb[j] = *reinterpret_cast<const float4*>(sBs + wn * kWN + j * 16 + q4 * 4);
+        v8i afq[3];
+        float saq[3];
+#pragma unroll
+        for (int d = 0; d < 3 - 1; ++d) {
+            afq[d] = read_frag(As, wm * kWM + d * 16 + r16, q4);
+            saq[d] = sAs[wm * kWM + d * 16 + r16];
+        }
 #pragma unroll
         for (int i = 0; i < kTM; ++i) {
-            const float sa = sAs[wm * kWM + i * 16 + r16];
-            const v8i af = read_frag(As, wm * kWM + i * 16 + r16, q4);
+            if (i + 3 - 1 < kTM) {
+                afq[(i + 3 - 1) % 3] = read_frag(As, wm * kWM + (i + 3 - 1) * 16 + r16, q4);
+                saq[(i + 3 - 1) % 3] = sAs[wm * kWM + (i + 3 - 1) * 16 + r16];
+            }
+            const v8i af = afq[i % 3];
+            const float sa = saq[i % 3];
 #pragma unroll
             for (int j = 0; j < kTN; ++j) {
                 const v4f P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, v4f{0.f, 0.f, 0.f, 0.f},
@@ -219,13 +261,13 @@ __device__ __forceinline__ void block_step(const GemmArgs& p, uint8_t* __restric
 // The contraction loop over a double-buffered pair of stages; stage 0 has
 // been issued by the caller.
 template <int kFmtA, int kFmtB, bool kChain>
-__device__ __forceinline__ void main_loop(const GemmArgs& p, uint8_t* smem, v4f (&acc)[kTM][kTN], int64_t m0,
-                                          int64_t n0, int kb0, int nkb, int wave, int lane)
+__device__ __forceinline__ void main_loop(const GemmArgs& p, uint8_t* smem, v4f (&acc)[kTM][kTN],
+                                          const TileSrc& src, int kb0, int nkb, int wave, int lane)
 {
     for (int it = 0; it < nkb; ++it) {
         uint8_t* cur = smem + (it & 1) * kStageBytes;
         uint8_t* oth = smem + ((it + 1) & 1) * kStageBytes;
-        block_step<kFmtA, kFmtB, kChain>(p, cur, oth, acc, m0, n0, kb0, it, nkb, wave, lane);
+        block_step<kFmtA, kFmtB, kChain>(p, cur, oth, acc, src, kb0, it, nkb, wave, lane);
     }
 }
 
@@ -262,7 +304,8 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p)
 #pragma unroll
         for (int j = 0; j < kTN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    load_stage(p, smem, m0, n0, kb0, wave, lane);
+    const TileSrc src = tile_src(p, m0, n0);
+    load_stage(p, src, smem, kb0, wave, lane);
 
     if (kFast) {
         // The scaled matrix-core chain is exact only for power-of-two scales:
@@ -275,12 +318,12 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p)
         bool ok = true;
         for (int kb = kb0; kb < kb0 + nkb; ++kb) ok &= is_pow2_scale(srow[kb]);
         if (__syncthreads_and(ok)) {
-            main_loop<kFmtA, kFmtB, true>(p, smem, acc, m0, n0, kb0, nkb, wave, lane);
+            main_loop<kFmtA, kFmtB, true>(p, smem, acc, src, kb0, nkb, wave, lane);
         } else {
-            main_loop<kFmtA, kFmtB, false>(p, smem, acc, m0, n0, kb0, nkb, wave, lane);
+            main_loop<kFmtA, kFmtB, false>(p, smem, acc, src, kb0, nkb, wave, lane);
         }
     } else {
-        main_loop<kFmtA, kFmtB, false>(p, smem, acc, m0, n0, kb0, nkb, wave, lane);
+        main_loop<kFmtA, kFmtB, false>(p, smem, acc, src, kb0, nkb, wave, lane);
     }
 
     // ---- epilogue: lane holds D[m][n..n+3] for every (i, j)

@@ -22,7 +22,8 @@
  *            per 128 consecutive contraction elements ("1x128" groups): the
  *            value of element (r, k) is dec(q[r][k]) * s[r][k/128].  Scales
  *            are row-major [rows][K/128], contiguous.  K must be a multiple of
- *            128.
+ *            128 and at most 2^22 (for the K-grouped call: the sum of the
+ *            groups' K).
  *  Formats.  TE_DTYPE_E4M3 is OCP E4M3FN (max 448), TE_DTYPE_E5M2 is OCP
  *            E5M2 (max 57344).  Any pairing of the two is accepted.
  *  Accumulation policy.  Every GEMM takes an explicit te_accum_t; it is
@@ -31,11 +32,13 @@
  *              TE_ACCUM_FULL_FP32: each 128-deep block is reduced by the
  *                matrix cores from zero and promoted into the fp32
  *                accumulator with its scale product in vector fp32 FMA.
- *              TE_ACCUM_FAST: blocks whose two scales are powers of two
- *                (the TE_CAST_POW2_SCALE cast produces only such scales)
- *                are scaled inside the matrix-core instruction and accumulate
- *                in one chain with no vector work; any other block falls back
- *                to the FULL update, so the result is correct for any input.
+ *              TE_ACCUM_FAST: an output tile whose row and column scales
+ *                over its contraction range are all powers of two (the
+ *                TE_CAST_POW2_SCALE cast produces only such scales) has the
+ *                scales applied inside the matrix-core instruction and
+ *                accumulates in one chain with no vector work; any other tile
+ *                falls back to the FULL update, so the result is correct for
+ *                any input.
  *  Ownership. Every pointer is device memory owned by the caller, except
  *            group_k, which is host memory read during the call.  The
  *            library allocates nothing, never synchronises, and enqueues its

@@ -67,6 +67,7 @@ def wgrad(lib, a=A, sa=S, da=1, b=B, sb=S, db=1, M=256, N=256, K=512, out=O, ld=
 @pytest.mark.parametrize("kw,status", [
     (dict(a=0), INV), (dict(sb=0), INV), (dict(out=0), INV),
     (dict(M=0), INV), (dict(N=-3), INV), (dict(K=0), INV), (dict(K=100), INV), (dict(K=200), INV),
+    (dict(K=(1 << 22) + 128), INV),
     (dict(da=3), INV), (dict(db=4), INV), (dict(da=0), INV),
     (dict(accum=0), INV), (dict(accum=3), INV),
     (dict(ld=255), INV), (dict(ld=258), MISAL),
