@@ -12,29 +12,36 @@
 // gradient kernels for dense and MoE models".
 //
 // Design for CDNA4 (gfx950):
-//  * Workgroup tile 256 x 256, eight waves (2 along M x 4 along N), each wave
-//    owning 128 x 64 outputs = 8 x 4 matrix-core tiles of 16 x 16.  Eight
-//    waves give two waves per SIMD so that one wave's matrix-core work can
-//    overlap the other's vector work (the FULL promotion and the epilogue).
+//  * Workgroup tile 256 x 256, eight waves (4 along M x 2 along N), each wave
+//    owning 64 x 128 outputs = 4 x 8 matrix-core tiles of 16 x 16 in VGPRs.
+//    Two waves per SIMD: one wave's matrix-core work overlaps the other's
+//    vector work (the FULL promotion, the epilogue) and LDS waits.
 //  * One 128-deep contraction block is one v_mfma_f32_16x16x128_f8f6f4, which
-//    is exactly one scale block: FULL starts it from zero and promotes
-//    acc += P * (sA * sB) in fp32 FMA; FAST passes the two E8M0 exponents of
-//    power-of-two scales to v_mfma_scale_f32_16x16x128_f8f6f4 and chains the
-//    accumulator through the matrix core (no vector work), falling back to
-//    the FULL update for any block whose scales are not powers of two.
+//    is exactly one scale block.  FULL starts each block's product from zero
+//    and promotes acc += P * (sA * sB) in fp32 FMA.  FAST, on a tile whose
+//    scales over the whole contraction are powers of two, passes their E8M0
+//    exponents to v_mfma_scale_f32_16x16x128_f8f6f4 and chains the
+//    accumulator through the matrix core with no vector work; any other tile
+//    is promoted like FULL.
 //  * The B tile is the instruction's first operand, so each lane's four
 //    accumulator registers are four consecutive n of one row m: stores are
 //    16-byte (fp32) / 8-byte (bf16) vectors along the output row.
-//  * Operands stream global -> LDS with global_load_lds_dwordx4 (no register
-//    staging), double-buffered: while the matrix cores consume stage s, the
-//    loads for stage s+1 are in flight (restrict-qualified stage pointers keep
-//    the compiler from making this stage's reads wait for them, and the
-//    barrier carries no fence that would drain them).  Each 128-byte LDS row stores its
-//    16-byte chunk c at slot c ^ ((row >> 1) & 7), so the 16 rows read by one
-//    16-lane group of a ds_read_b128 fall in 16 distinct 16-byte bank groups.
-//    The two scale vectors of the block ride along in the same stage.
-//  * Edge tiles clamp their load rows to the last valid row (no faults, the
-//    values are unused) and mask their stores.
+//  * Operands stream global -> LDS with buffer_load ... lds (no register
+//    staging) into two stages.  Each 128-byte LDS row stores its 16-byte chunk
+//    c at slot c ^ ((row >> 1) & 7), so the 16 rows read by one 16-lane group
+//    of a ds_read_b128 fall in 16 distinct bank groups.  The two scale vectors
+//    of the block ride along in the same stage.
+//  * Software pipeline inside a block: a wave keeps its four A fragments in
+//    registers and streams its eight B column groups two groups ahead; in the
+//    FULL loop each matrix-core product is promoted one instruction later, so
+//    the vector unit works on product t-1 while the matrix core computes t.
+//    The single barrier of a block sits after the last read of the current
+//    stage: past it the copies of block +2 go into the current stage and the
+//    next block's first fragments are read from the other one, so a block
+//    starts with its operands already in registers.  Slots are fenced with
+//    scheduling barriers so the compiler keeps this order.
+//  * Tiles past the last row read zero (buffer ranges end at the last valid
+//    row) and their stores are masked.
 //  * K-grouped launches carry up to 128 (kb_off, kb_len, out) descriptors by
 //    value; blocks are ordered longest group first.
 #include <hip/hip_runtime.h>
@@ -51,21 +58,21 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kBM = 256, kBN = 256, kBK = 128;
-constexpr int kWavesM = 2, kWavesN = 4;
-constexpr int kThreads = 64 * kWavesM * kWavesN;  // 512
-constexpr int kWM = kBM / kWavesM;                // 128
-constexpr int kWN = kBN / kWavesN;                // 64
-constexpr int kTM = kWM / 16;                     // 8
-constexpr int kTN = kWN / 16;                     // 4
 constexpr int kTileA = kBM * kBK;                 // 32 KiB
 constexpr int kTileB = kBN * kBK;                 // 32 KiB
 constexpr int kStageBytes = kTileA + kTileB + (kBM + kBN) * 4;
-constexpr int kStages = 2;
 constexpr int kGroupM = 8;                        // tile rows per raster group
 
-static_assert(kBM * kBK / 16 == kThreads * 4, "A tile = four 16-byte loads per thread");
-static_assert(kBN * kBK / 16 == kThreads * 4, "B tile = four 16-byte loads per thread");
-static_assert(kBM + kBN == kThreads, "one scale per thread per stage");
+constexpr int kWavesM = 4, kWavesN = 2;
+constexpr int kWaves = kWavesM * kWavesN;
+constexpr int kThreads = 64 * kWaves;             // 512
+constexpr int kWM = kBM / kWavesM;                // 64 rows per wave
+constexpr int kWN = kBN / kWavesN;                // 128 columns per wave
+constexpr int kTM = kWM / 16;                     // 4 A fragments
+constexpr int kTN = kWN / 16;                     // 8 B column groups
+constexpr int kOpPerWave = (kBM / 8) / kWaves;    // 1 KiB copies of A (and of B) per wave
+constexpr int kBarrierGroup = kTN - 2;            // the block's barrier precedes this column group
+static_assert(kTM == 4 && kTN == 8 && kWaves * 64 == kBM + kBN, "layout assumed below");
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
@@ -91,14 +98,27 @@ __device__ __forceinline__ TileSrc tile_src(const GemmArgs& p, int64_t m0, int64
     return s;
 }
 
+// The same tile with empty ranges: every copy reads zero and touches no
+// memory.  Used for the copies past the last block so that the loop body is
+// one straight-line block (no branch for the scheduler to sink work across).
+__device__ __forceinline__ TileSrc select_src(const TileSrc& s, bool live)
+{
+    TileSrc e;
+    e.a = live ? s.a : __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, 0x00020000);
+    e.b = live ? s.b : e.a;
+    e.sa = live ? s.sa : e.a;
+    e.sb = live ? s.sb : e.a;
+    return e;
+}
+
 // Issue the global -> LDS copies of one 128-deep stage (A tile, B tile, scales).
 __device__ __forceinline__ void load_stage(const GemmArgs& p, const TileSrc& src, uint8_t* stage, int kb, int wave,
                                            int lane)
 {
     const int kcol = kb * kBK;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int blk = wave * 4 + t;                 // 1 KiB block = 8 rows of 128 bytes
+    for (int t = 0; t < kOpPerWave; ++t) {
+        const int blk = wave * kOpPerWave + t;        // 1 KiB block = 8 rows of 128 bytes
         const int ci = blk * 64 + lane;               // 16-byte chunk index within the tile
         const int row = ci >> 3;
         const int chunk = (ci & 7) ^ ((row >> 1) & 7);
@@ -107,22 +127,69 @@ __device__ __forceinline__ void load_stage(const GemmArgs& p, const TileSrc& src
         __builtin_amdgcn_raw_ptr_buffer_load_lds(src.b, (lds_ptr_t)(stage + kTileA + blk * 1024), 16,
                                                  (uint32_t)(row * p.ldb + chunk * 16), kcol, 0, 0);
     }
-    // scales: waves 0-3 fetch sA for the 256 tile rows, waves 4-7 sB for the 256 tile columns
+    // scales: waves 0-3 carry sA for the 256 tile rows, waves 4-7 sB for the 256 tile columns
     const bool is_a = wave < 4;
     const int r = (is_a ? wave : wave - 4) * 64 + lane;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? src.sa : src.sb, (lds_ptr_t)(stage + kTileA + kTileB + wave * 256),
-                                             4, (uint32_t)(r * (is_a ? p.lsa : p.lsb) * 4), kb * 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? src.sa : src.sb,
+                                             (lds_ptr_t)(stage + kTileA + kTileB + wave * 256), 4,
+                                             (uint32_t)(r * (is_a ? p.lsa : p.lsb) * 4), kb * 4, 0, 0);
 }
 
-__device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int q4)
+// This lane's byte offsets inside a stage.
+struct LaneOff {
+    int a_lo, a_hi;   // A fragment halves of row group 0 (row group i: + i * 2048)
+    int b_lo, b_hi;   // B fragment halves of column group 0 (column group j: + j * 2048)
+    int sa;           // sA of row r16 of row group 0 (+ i * 64)
+    int sb_row;       // sB of column r16 of column group 0 (+ j * 64): matrix-core scale operand
+    int sb_vec;       // sB of the lane's four output columns of column group 0 (+ j * 64)
+};
+
+__device__ __forceinline__ LaneOff lane_offsets(int wave, int lane)
 {
-    const uint4 lo = *reinterpret_cast<const uint4*>(tile + swz(row, q4));
-    const uint4 hi = *reinterpret_cast<const uint4*>(tile + swz(row, q4 + 4));
+    const int wm = wave / kWavesN, wn = wave % kWavesN;
+    const int r16 = lane & 15, q4 = lane >> 4;
+    LaneOff o;
+    // adding 16 rows leaves the swizzle term unchanged, so fragment i / j is a constant offset
+    o.a_lo = swz(wm * kWM + r16, q4);
+    o.a_hi = swz(wm * kWM + r16, q4 + 4);
+    o.b_lo = kTileA + swz(wn * kWN + r16, q4);
+    o.b_hi = kTileA + swz(wn * kWN + r16, q4 + 4);
+    o.sa = kTileA + kTileB + (wm * kWM + r16) * 4;
+    o.sb_row = kTileA + kTileB + kBM * 4 + (wn * kWN + r16) * 4;
+    o.sb_vec = kTileA + kTileB + kBM * 4 + (wn * kWN + q4 * 4) * 4;
+    // Opaque to the compiler: otherwise it splits the stage-region constants
+    // out of these sums and, past the 16-bit immediate offset of ds_read,
+    // keeps one address register per fragment instead of one per field.
+    asm volatile("" : "+v"(o.a_lo), "+v"(o.a_hi), "+v"(o.b_lo), "+v"(o.b_hi), "+v"(o.sa), "+v"(o.sb_row),
+                 "+v"(o.sb_vec));
+    return o;
+}
+
+// Fragment layout of the 16x16x128 fp8 operand: lane (r16, q4) holds row r16,
+// bytes k = 16 q4 .. 16 q4 + 15 in registers 0-3 and k = 64 + 16 q4 .. in 4-7.
+__device__ __forceinline__ void lds_half(v8i& f, int h, const uint8_t* addr)
+{
+    const uint4 v = *reinterpret_cast<const uint4*>(addr);
+    f[4 * h + 0] = (int)v.x;
+    f[4 * h + 1] = (int)v.y;
+    f[4 * h + 2] = (int)v.z;
+    f[4 * h + 3] = (int)v.w;
+}
+
+__device__ __forceinline__ v8i lds_frag(const uint8_t* st, int lo, int hi, int off)
+{
     v8i f;
-    f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
-    f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+    lds_half(f, 0, st + lo + off);
+    lds_half(f, 1, st + hi + off);
     return f;
 }
+
+__device__ __forceinline__ uint32_t lds_u32(const uint8_t* addr) { return *reinterpret_cast<const uint32_t*>(addr); }
+__device__ __forceinline__ float lds_f32(const uint8_t* addr) { return *reinterpret_cast<const float*>(addr); }
+__device__ __forceinline__ float4 lds_f32x4(const uint8_t* addr) { return *reinterpret_cast<const float4*>(addr); }
+
+// E8M0 exponent of a positive normal power of two = its fp32 exponent field
+__device__ __forceinline__ int e8m0(uint32_t bits) { return (int)(bits >> 23); }
 
 __device__ __forceinline__ bool is_pow2_scale(float s)
 {
@@ -167,167 +234,194 @@ __device__ __forceinline__ float dgelu(float z)
     return fmaf(2.0f * kGeluC * z * s * one_minus_s, fmaf(3.0f * kGeluA, z2, 1.0f), s);
 }
 
-// Workgroup barrier without a memory fence: callers wait for their own
-// global->LDS copies explicitly; this waits for the wave's own LDS reads and
-// syncs.  (A fenced __syncthreads() would also drain the next stage's copies.)
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// One contraction block, held in `stage`; the copies of the next block go to
-// `other`.  The two stages are restrict-qualified so the compiler knows the
-// copies into `other` do not feed the reads of `stage` and does not make
-// those reads wait for them: the next block's copies overlap this block's
-// matrix-core work.  kChain: every scale is a power of two and the block
-// scales ride in the matrix-core instruction; otherwise each block's product
-// starts from zero and is promoted in fp32.
-template <int kFmtA, int kFmtB, bool kChain>
-__device__ __forceinline__ void block_step(const GemmArgs& p, uint8_t* __restrict__ stage,
-                                           uint8_t* __restrict__ other, v4f (&acc)[kTM][kTN], const TileSrc& src,
-                                           int kb0, int it, int nkb, int wave, int lane)
+// The block barrier: this wave's copies have landed and its LDS reads are
+// done, then every wave syncs.  No memory fence: a fenced __syncthreads()
+// would also wait for copies that are meant to stay in flight.
+__device__ __forceinline__ void stage_barrier()
 {
-    const int wm = wave / kWavesN, wn = wave % kWavesN;
-    const int r16 = lane & 15, q4 = lane >> 4;
-    // this block's copies (the only ones in flight) have landed everywhere, and
-    // every wave is done reading `other` (the previous block)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    lds_barrier();
-    if (it + 1 < nkb) load_stage(p, src, other, kb0 + it + 1, wave, lane);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
-    const uint8_t* As = stage;
-    const uint8_t* Bs = stage + kTileA;
-    const float* sAs = reinterpret_cast<const float*>(stage + kTileA + kTileB);
-    const float* sBs = sAs + kBM;
+__device__ __forceinline__ void promote(v4f& acc, const v4f& P, float s_a, const float4& s_b)
+{
+    acc[0] = fmaf(P[0], s_a * s_b.x, acc[0]);
+    acc[1] = fmaf(P[1], s_a * s_b.y, acc[1]);
+    acc[2] = fmaf(P[2], s_a * s_b.z, acc[2]);
+    acc[3] = fmaf(P[3], s_a * s_b.w, acc[3]);
+}
 
-    v8i bf[kTN];
+// Workgroup-wide AND.  Built on the kernel's own LDS array: a separate LDS
+// variable (as __syncthreads_and uses) makes the compiler rewrite the alias
+// scopes of every LDS access, and the stage reads would then wait for copies
+// into the other stage.
+__device__ __forceinline__ bool workgroup_all(bool v, uint32_t* slots, int wave, int lane)
+{
+    const bool w = __all(v);
+    if (lane == 0) slots[wave] = w ? 1u : 0u;
+    __syncthreads();
+    bool r = true;
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) bf[j] = read_frag(Bs, wn * kWN + j * 16 + r16, q4);
+    for (int i = 0; i < kWaves; ++i) r = r && slots[i] != 0;
+    return r;
+}
 
+// A scheduling group of n LDS reads (n folds to a constant once the slot loops are unrolled).
+__device__ __forceinline__ void sched_ds_reads(int n)
+{
+    if (n == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (n == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    if (n == 4) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+}
+
+// Registers a wave carries from block to block.  B column group j lives in
+// slot j & 3 (streamed two groups ahead); A fragments are resident, the next
+// block's copy replacing fragment i right after its last use.  Scales of the
+// A rows are double-buffered by stage parity.
+struct Pipe {
+    v8i ac[kTM];
+    v8i bq[4];
+    float sa[2][kTM];     // FULL: sA values
+    uint32_t ea[2][kTM];  // chain: raw sA bits
+    float4 sbq[4];        // FULL: the lane's 4 sB values per column group
+    uint32_t ebq[4];      // chain: raw sB bits of column r16
+    v4f P[2];             // FULL: products waiting for promotion
+};
+
+// One contraction block held in stage S (`cur`); the next block is in `nxt`.
+// The two come from main_loop's restrict-qualified stage pointers.
+template <int S, bool kChain, int kFmtA, int kFmtB>
+__device__ __forceinline__ void block_body(const GemmArgs& p, uint8_t* cur, uint8_t* nxt,
+                                           v4f (&acc)[kTM][kTN], Pipe& q, const LaneOff& o, const TileSrc& src,
+                                           int kb_next2, bool has_next2, int wave, int lane)
+{
+    int ea[kTM];
     if (kChain) {
-        // E8M0 exponent of a positive normal power of two = its fp32 exponent field
-        int eb[kTN];
 #pragma unroll
-        for (int j = 0; j < kTN; ++j) eb[j] = (int)(__builtin_bit_cast(uint32_t, sBs[wn * kWN + j * 16 + r16]) >> 23);
-        v8i afq[3];
-        int eaq[3];
+        for (int i = 0; i < kTM; ++i) ea[i] = e8m0(q.ea[S][i]);
+    }
 #pragma unroll
-        for (int d = 0; d < 3 - 1; ++d) {
-            afq[d] = read_frag(As, wm * kWM + d * 16 + r16, q4);
-            eaq[d] = (int)(__builtin_bit_cast(uint32_t, sAs[wm * kWM + d * 16 + r16]) >> 23);
+    for (int j = 0; j < kTN; ++j) {
+        if (j == kBarrierGroup) {
+            // every read of `cur` has been issued (B groups up to 7 were read two groups ago)
+            stage_barrier();
+            load_stage(p, select_src(src, has_next2), cur, kb_next2, wave, lane);
         }
+        const int eb = kChain ? e8m0(q.ebq[j & 3]) : 0;
 #pragma unroll
         for (int i = 0; i < kTM; ++i) {
-            if (i + 3 - 1 < kTM) {
-                afq[(i + 3 - 1) % 3] = read_frag(As, wm * kWM + (i + 3 - 1) * 16 + r16, q4);
-                eaq[(i + 3 - 1) % 3] = (int)(__builtin_bit_cast(uint32_t, sAs[wm * kWM + (i + 3 - 1) * 16 + r16]) >> 23);
+            const int t = j * kTM + i;
+            if (kChain) {
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.bq[j & 3], q.ac[i], acc[i][j], kFmtB,
+                                                                             kFmtA, 0, eb, 0, ea[i]);
+            } else {
+                q.P[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.bq[j & 3], q.ac[i],
+                                                                              v4f{0.f, 0.f, 0.f, 0.f}, kFmtB, kFmtA,
+                                                                              0, 0, 0, 0);
+                // promote the previous slot's product (slot -1 is the previous block's last)
+                const int tp = (t + kTM * kTN - 1) % (kTM * kTN);
+                const int ip = tp % kTM, jp = tp / kTM;
+                promote(acc[ip][jp], q.P[(t + 1) & 1], t == 0 ? q.sa[1 - S][ip] : q.sa[S][ip], q.sbq[jp & 3]);
+                // pin the update to this slot (otherwise it is sunk to the end of the block and every
+                // product of the block stays live)
+                asm volatile("" : "+v"(acc[ip][jp]));
             }
-            const v8i af = afq[i % 3];
-            const int ea = eaq[i % 3];
+            // LDS reads of this slot
+            if (j < kBarrierGroup) {
+                const int jb = j + 2;  // column group prefetched from this stage
+                if (i == 0) lds_half(q.bq[jb & 3], 0, cur + o.b_lo + jb * 2048);
+                if (i == 1) lds_half(q.bq[jb & 3], 1, cur + o.b_hi + jb * 2048);
+                if (i == 2) {
+                    if (kChain) q.ebq[jb & 3] = lds_u32(cur + o.sb_row + jb * 64);
+                    else q.sbq[jb & 3] = lds_f32x4(cur + o.sb_vec + jb * 64);
+                }
+            } else if (j == kBarrierGroup) {
+                // the next block's first two column groups and its A-row scales
+                if (i == 0) q.bq[0] = lds_frag(nxt, o.b_lo, o.b_hi, 0);
+                if (i == 1) {
+                    if (kChain) q.ebq[0] = lds_u32(nxt + o.sb_row);
+                    else q.sbq[0] = lds_f32x4(nxt + o.sb_vec);
+                    lds_half(q.bq[1], 0, nxt + o.b_lo + 2048);
+                }
+                if (i == 2) {
+                    lds_half(q.bq[1], 1, nxt + o.b_hi + 2048);
+                    if (kChain) q.ebq[1] = lds_u32(nxt + o.sb_row + 64);
+                    else q.sbq[1] = lds_f32x4(nxt + o.sb_vec + 64);
+                }
+                if (i == 3) {
 #pragma unroll
-            for (int j = 0; j < kTN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], kFmtB, kFmtA, 0,
-                                                                             eb[j], 0, ea);
-        }
-    } else {
-        float4 sb[kTN];
-#pragma unroll
-        for (int j = 0; j < kTN; ++j) sb[j] = *reinterpret_cast<const float4*>(sBs + wn * kWN + j * 16 + q4 * 4);
-        v8i afq[3];
-        float saq[3];
-#pragma unroll
-        for (int d = 0; d < 3 - 1; ++d) {
-            afq[d] = read_frag(As, wm * kWM + d * 16 + r16, q4);
-            saq[d] = sAs[wm * kWM + d * 16 + r16];
-        }
-#pragma unroll
-        for (int i = 0; i < kTM; ++i) {
-            if (i + 3 - 1 < kTM) {
-                afq[(i + 3 - 1) % 3] = read_frag(As, wm * kWM + (i + 3 - 1) * 16 + r16, q4);
-                saq[(i + 3 - 1) % 3] = sAs[wm * kWM + (i + 3 - 1) * 16 + r16];
+                    for (int r = 0; r < kTM; ++r) {
+                        if (kChain) q.ea[1 - S][r] = lds_u32(nxt + o.sa + r * 64);
+                        else q.sa[1 - S][r] = lds_f32(nxt + o.sa + r * 64);
+                    }
+                }
+            } else {
+                // last column group: A fragment i is dead after this slot's instruction
+                q.ac[i] = lds_frag(nxt, o.a_lo, o.a_hi, i * 2048);
             }
-            const v8i af = afq[i % 3];
-            const float sa = saq[i % 3];
-#pragma unroll
-            for (int j = 0; j < kTN; ++j) {
-                const v4f P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, v4f{0.f, 0.f, 0.f, 0.f},
-                                                                               kFmtB, kFmtA, 0, 0, 0, 0);
-                acc[i][j][0] = fmaf(P[0], sa * sb[j].x, acc[i][j][0]);
-                acc[i][j][1] = fmaf(P[1], sa * sb[j].y, acc[i][j][1]);
-                acc[i][j][2] = fmaf(P[2], sa * sb[j].z, acc[i][j][2]);
-                acc[i][j][3] = fmaf(P[3], sa * sb[j].w, acc[i][j][3]);
-            }
+            // Ask the scheduler for this slot's order: the matrix-core op, the
+            // promotion of the previous product, then the slot's LDS reads.
+            const int n_ds = j < kBarrierGroup ? (i < 3 ? 1 : 0) : (j == kBarrierGroup && i == 3 ? kTM : 2);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (!kChain) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            sched_ds_reads(n_ds);
         }
     }
 }
 
-// The contraction loop over a double-buffered pair of stages; stage 0 has
-// been issued by the caller.
-template <int kFmtA, int kFmtB, bool kChain>
-__device__ __forceinline__ void main_loop(const GemmArgs& p, uint8_t* smem, v4f (&acc)[kTM][kTN],
-                                          const TileSrc& src, int kb0, int nkb, int wave, int lane)
+// Stage 0 of the block range has landed and stage 1 is in flight when this is
+// called.  The two stages are restrict-qualified so the compiler knows the
+// copies into one do not feed reads of the other and does not make those
+// reads wait for them (every copy is issued from code outside this scope or
+// from block_body, so none of them carries a scope the reads could alias).
+template <bool kChain, int kFmtA, int kFmtB>
+__device__ __forceinline__ void main_loop(const GemmArgs& p, uint8_t* __restrict__ s0, uint8_t* __restrict__ s1,
+                                          v4f (&acc)[kTM][kTN], const LaneOff& o, const TileSrc& src, int kb0,
+                                          int nkb, int wave, int lane)
 {
-    for (int it = 0; it < nkb; ++it) {
-        uint8_t* cur = smem + (it & 1) * kStageBytes;
-        uint8_t* oth = smem + ((it + 1) & 1) * kStageBytes;
-        block_step<kFmtA, kFmtB, kChain>(p, cur, oth, acc, src, kb0, it, nkb, wave, lane);
+    Pipe q;
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+        q.ac[i] = lds_frag(s0, o.a_lo, o.a_hi, i * 2048);
+        if (kChain) q.ea[0][i] = lds_u32(s0 + o.sa + i * 64);
+        else q.sa[0][i] = lds_f32(s0 + o.sa + i * 64);
+        q.sa[1][i] = 0.f;
+        q.ea[1][i] = 0;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        q.bq[j] = lds_frag(s0, o.b_lo, o.b_hi, j * 2048);
+        if (kChain) q.ebq[j] = lds_u32(s0 + o.sb_row + j * 64);
+        else q.sbq[j] = lds_f32x4(s0 + o.sb_vec + j * 64);
+    }
+    // the first slot promotes a zero product with zero scales
+    q.P[1] = v4f{0.f, 0.f, 0.f, 0.f};
+    q.sbq[3] = make_float4(0.f, 0.f, 0.f, 0.f);
+    q.sbq[2] = q.sbq[3];
+    q.ebq[2] = q.ebq[3] = 0;
+    q.bq[2] = q.bq[3] = q.bq[0];
+
+    int it = 0;
+    for (; it + 2 <= nkb; it += 2) {
+        block_body<0, kChain, kFmtA, kFmtB>(p, s0, s1, acc, q, o, src, kb0 + it + 2, it + 2 < nkb, wave, lane);
+        block_body<1, kChain, kFmtA, kFmtB>(p, s1, s0, acc, q, o, src, kb0 + it + 3, it + 3 < nkb, wave, lane);
+    }
+    if (it < nkb) block_body<0, kChain, kFmtA, kFmtB>(p, s0, s1, acc, q, o, src, 0, false, wave, lane);
+    // the trailing copies (empty ranges) still write LDS: let them land
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (!kChain) {
+        // the last product of the last block
+        const float s_a = (nkb & 1) ? q.sa[0][kTM - 1] : q.sa[1][kTM - 1];
+        promote(acc[kTM - 1][kTN - 1], q.P[1], s_a, q.sbq[(kTN - 1) & 3]);
     }
 }
 
-template <int kFmtA, int kFmtB, bool kFast, int kEpi>
-__global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p)
+// Epilogue: lane holds D[m][n..n+3] for every (i, j).
+template <int kEpi>
+__device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM][kTN], int64_t m0, int64_t n0,
+                                         int64_t out_off, int wave, int lane)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / kWavesN, wn = wave % kWavesN;
     const int r16 = lane & 15, q4 = lane >> 4;
-
-    // ---- which group and tile this workgroup owns
-    const int64_t tiles_m = (p.M + kBM - 1) / kBM;
-    const int64_t tiles_n = (p.N + kBN - 1) / kBN;
-    const int64_t tiles_per_group = tiles_m * tiles_n;
-    const int gslot = (int)(blockIdx.x / tiles_per_group);
-    int64_t t = blockIdx.x - (int64_t)gslot * tiles_per_group;
-    const int64_t per_band = (int64_t)kGroupM * tiles_n;
-    const int64_t band = t / per_band;
-    const int64_t first_m = band * kGroupM;
-    const int64_t band_rows = min((int64_t)kGroupM, tiles_m - first_m);
-    t -= band * per_band;
-    const int64_t m0 = (first_m + t % band_rows) * kBM;
-    const int64_t n0 = (t / band_rows) * kBN;
-
-    const Group grp = p.groups[gslot];
-    const int kb0 = grp.kb_off, nkb = grp.kb_len;
-
-    v4f acc[kTM][kTN];
-#pragma unroll
-    for (int i = 0; i < kTM; ++i)
-#pragma unroll
-        for (int j = 0; j < kTN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    const TileSrc src = tile_src(p, m0, n0);
-    load_stage(p, src, smem, kb0, wave, lane);
-
-    if (kFast) {
-        // The scaled matrix-core chain is exact only for power-of-two scales:
-        // take it when every scale of this tile's rows and columns over the
-        // contraction range is one, otherwise promote like FULL.
-        const int tid = threadIdx.x;
-        const float* srow = tid < kBM ? p.sa + min(m0 + tid, p.M - 1) * p.lsa
-                                      : p.sb + min(n0 + (tid - kBM), p.N - 1) * p.lsb;
-        // independent loads (no short-circuit), so they are all in flight at once
-        bool ok = true;
-        for (int kb = kb0; kb < kb0 + nkb; ++kb) ok &= is_pow2_scale(srow[kb]);
-        if (__syncthreads_and(ok)) {
-            main_loop<kFmtA, kFmtB, true>(p, smem, acc, src, kb0, nkb, wave, lane);
-        } else {
-            main_loop<kFmtA, kFmtB, false>(p, smem, acc, src, kb0, nkb, wave, lane);
-        }
-    } else {
-        main_loop<kFmtA, kFmtB, false>(p, smem, acc, src, kb0, nkb, wave, lane);
-    }
-
-    // ---- epilogue: lane holds D[m][n..n+3] for every (i, j)
-    const int64_t out_off = (int64_t)grp.out_idx * p.out_group_stride;
     float colsum[kTN][4];
     if (kEpi == (int)Epi::Dgrad) {
 #pragma unroll
@@ -453,6 +547,75 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p)
     }
 }
 
+template <int kFmtA, int kFmtB, bool kFast, int kEpi>
+__global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageBytes + kWaves * 4];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    // ---- which group and tile this workgroup owns
+    const int64_t tiles_m = (p.M + kBM - 1) / kBM;
+    const int64_t tiles_n = (p.N + kBN - 1) / kBN;
+    const int64_t tiles_per_group = tiles_m * tiles_n;
+    const int gslot = (int)(blockIdx.x / tiles_per_group);
+    int64_t t = blockIdx.x - (int64_t)gslot * tiles_per_group;
+    const int64_t per_band = (int64_t)kGroupM * tiles_n;
+    const int64_t band = t / per_band;
+    const int64_t first_m = band * kGroupM;
+    const int64_t band_rows = min((int64_t)kGroupM, tiles_m - first_m);
+    t -= band * per_band;
+    const int64_t m0 = (first_m + t % band_rows) * kBM;
+    const int64_t n0 = (t / band_rows) * kBN;
+
+    const Group grp = p.groups[gslot];
+    const int kb0 = grp.kb_off, nkb = grp.kb_len;
+
+    v4f acc[kTM][kTN];
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t out_off = (int64_t)grp.out_idx * p.out_group_stride;
+    const TileSrc src = tile_src(p, m0, n0);
+    const LaneOff o = lane_offsets(wave, lane);
+    load_stage(p, src, smem, kb0, wave, lane);
+
+    bool chain = false;
+    if (kFast) {
+        // The scaled matrix-core chain is exact only for power-of-two scales:
+        // take it when every scale of this tile's rows and columns over the
+        // contraction range is one.  Independent loads (no short-circuit), so
+        // they are all in flight at once; consecutive lanes read consecutive
+        // blocks of one row.
+        bool ok = true;
+        const int total = (kBM + kBN) * nkb;
+        for (int e = threadIdx.x; e < total; e += kThreads) {
+            const int r = e / nkb, kb = kb0 + e % nkb;
+            const float* s = r < kBM ? p.sa + min(m0 + r, p.M - 1) * p.lsa : p.sb + min(n0 + (r - kBM), p.N - 1) * p.lsb;
+            ok &= is_pow2_scale(s[kb]);
+        }
+        chain = workgroup_all(ok, reinterpret_cast<uint32_t*>(smem + 2 * kStageBytes), wave, lane);
+    }
+    // Stage 1 sits past the 16-bit immediate offset of ds_read: hide its
+    // distance from the compiler so each lane offset gets one base register
+    // per stage instead of one per fragment.
+    // (Both stage offsets are hidden: a pointer the compiler can fold to a
+    // constant loses its restrict scope once main_loop is inlined.)
+    int s0_off = 0, s1_off = kStageBytes;
+    asm volatile("" : "+s"(s0_off), "+s"(s1_off));
+    stage_barrier();
+    load_stage(p, select_src(src, nkb > 1), smem + s1_off, kb0 + 1, wave, lane);
+    if (chain) {
+        main_loop<true, kFmtA, kFmtB>(p, smem + s0_off, smem + s1_off, acc, o, src, kb0, nkb, wave, lane);
+    } else {
+        main_loop<false, kFmtA, kFmtB>(p, smem + s0_off, smem + s1_off, acc, o, src, kb0, nkb, wave, lane);
+    }
+    epilogue<kEpi>(p, acc, m0, n0, out_off, wave, lane);
+}
+
 __global__ void zero_f32_kernel(float* p, int64_t n)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -482,7 +645,12 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream, LaunchInfo* info)
 {
     const int64_t tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
     const int64_t blocks = tiles * a.num_groups;
-    if (info) { info->tile_m = kBM; info->tile_n = kBN; info->threads = kThreads; info->grid = blocks; }
+    if (info) {
+        info->tile_m = kBM;
+        info->tile_n = kBN;
+        info->threads = kThreads;
+        info->grid = blocks;
+    }
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks);
