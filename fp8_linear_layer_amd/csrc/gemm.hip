@@ -47,6 +47,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "internal.h"
 #include "te_fp8.h"
 
@@ -62,6 +64,7 @@ constexpr int kTileA = kBM * kBK;                 // 32 KiB
 constexpr int kTileB = kBN * kBK;                 // 32 KiB
 constexpr int kStageBytes = kTileA + kTileB + (kBM + kBN) * 4;
 constexpr int kGroupM = 8;                        // tile rows per raster group
+constexpr int kXcds = 8;                          // accelerator complex dies (each with its own L2)
 
 constexpr int kWavesM = 4, kWavesN = 2;
 constexpr int kWaves = kWavesM * kWavesN;
@@ -547,73 +550,135 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
     }
 }
 
+// One output tile: its corner, contraction range and output matrix.
+struct TileCtx {
+    int64_t m0, n0, out_off;
+    int kb0, nkb;
+    TileSrc src;
+};
+
+// Tiles of a group are rastered in bands of kGroupM tile rows, column by
+// column inside a band, so the tiles in flight at once share A rows and B
+// columns.
+__device__ __forceinline__ TileCtx tile_ctx(const GemmArgs& p, int64_t tile)
+{
+    const int64_t tiles_m = (p.M + kBM - 1) / kBM;
+    const int64_t tiles_n = (p.N + kBN - 1) / kBN;
+    const int64_t tiles_per_group = tiles_m * tiles_n;
+    const int gslot = (int)(tile / tiles_per_group);
+    int64_t t = tile - (int64_t)gslot * tiles_per_group;
+    const int64_t per_band = (int64_t)kGroupM * tiles_n;
+    const int64_t band = t / per_band;
+    const int64_t first_m = band * kGroupM;
+    const int64_t band_rows = min((int64_t)kGroupM, tiles_m - first_m);
+    t -= band * per_band;
+    const Group grp = p.groups[gslot];
+    TileCtx c;
+    c.m0 = (first_m + t % band_rows) * kBM;
+    c.n0 = (t / band_rows) * kBN;
+    c.out_off = (int64_t)grp.out_idx * p.out_group_stride;
+    c.kb0 = grp.kb_off;
+    c.nkb = grp.kb_len;
+    c.src = tile_src(p, c.m0, c.n0);
+    return c;
+}
+
+// This thread's share of the FAST test: are the scales of one tile row (A) or
+// column (B) over the tile's contraction range all powers of two?  Thread r
+// takes row r of the 256 A rows and 256 B rows; the loads are batched so they
+// are in flight together.
+__device__ __forceinline__ bool row_scales_pow2(const GemmArgs& p, const TileCtx& c)
+{
+    const int r = threadIdx.x;
+    const float* s = r < kBM ? p.sa + min(c.m0 + r, p.M - 1) * p.lsa : p.sb + min(c.n0 + (r - kBM), p.N - 1) * p.lsb;
+    s += c.kb0;
+    bool ok = true;
+    if ((reinterpret_cast<uintptr_t>(s) & 15) == 0 && (c.nkb & 3) == 0) {
+        for (int kb = 0; kb < c.nkb; kb += 32) {
+            float4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                v[u] = kb + 4 * u < c.nkb ? *reinterpret_cast<const float4*>(s + kb + 4 * u) : make_float4(1.f, 1.f, 1.f, 1.f);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                ok = ok && is_pow2_scale(v[u].x) && is_pow2_scale(v[u].y) && is_pow2_scale(v[u].z) && is_pow2_scale(v[u].w);
+        }
+    } else {
+        for (int kb = 0; kb < c.nkb; kb += 16) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = kb + u < c.nkb ? s[kb + u] : 1.f;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) ok = ok && is_pow2_scale(v[u]);
+        }
+    }
+    return ok;
+}
+
+// Persistent kernel: workgroup w takes tiles w, w + G, w + 2G, ... (G = grid
+// size).  While a tile's epilogue runs, the first stage of the workgroup's
+// next tile is already being copied in.
 template <int kFmtA, int kFmtB, bool kFast, int kEpi>
-__global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p)
+__global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p, int64_t total_tiles)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageBytes + kWaves * 4];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    // ---- which group and tile this workgroup owns
-    const int64_t tiles_m = (p.M + kBM - 1) / kBM;
-    const int64_t tiles_n = (p.N + kBN - 1) / kBN;
-    const int64_t tiles_per_group = tiles_m * tiles_n;
-    const int gslot = (int)(blockIdx.x / tiles_per_group);
-    int64_t t = blockIdx.x - (int64_t)gslot * tiles_per_group;
-    const int64_t per_band = (int64_t)kGroupM * tiles_n;
-    const int64_t band = t / per_band;
-    const int64_t first_m = band * kGroupM;
-    const int64_t band_rows = min((int64_t)kGroupM, tiles_m - first_m);
-    t -= band * per_band;
-    const int64_t m0 = (first_m + t % band_rows) * kBM;
-    const int64_t n0 = (t / band_rows) * kBN;
+    // Workgroups are handed to the eight XCDs round-robin; renumber them so
+    // that the tiles one XCD runs at the same time are neighbours (each XCD
+    // has its own L2).
+    const int64_t G = gridDim.x;
+    const int64_t per_xcd = G / kXcds;
+    int64_t tile = blockIdx.x;
+    if (tile < per_xcd * kXcds) tile = (tile % kXcds) * per_xcd + tile / kXcds;
 
-    const Group grp = p.groups[gslot];
-    const int kb0 = grp.kb_off, nkb = grp.kb_len;
-
-    v4f acc[kTM][kTN];
-#pragma unroll
-    for (int i = 0; i < kTM; ++i)
-#pragma unroll
-        for (int j = 0; j < kTN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    const int64_t out_off = (int64_t)grp.out_idx * p.out_group_stride;
-    const TileSrc src = tile_src(p, m0, n0);
     const LaneOff o = lane_offsets(wave, lane);
-    load_stage(p, src, smem, kb0, wave, lane);
-
-    bool chain = false;
-    if (kFast) {
-        // The scaled matrix-core chain is exact only for power-of-two scales:
-        // take it when every scale of this tile's rows and columns over the
-        // contraction range is one.  Independent loads (no short-circuit), so
-        // they are all in flight at once; consecutive lanes read consecutive
-        // blocks of one row.
-        bool ok = true;
-        const int total = (kBM + kBN) * nkb;
-        for (int e = threadIdx.x; e < total; e += kThreads) {
-            const int r = e / nkb, kb = kb0 + e % nkb;
-            const float* s = r < kBM ? p.sa + min(m0 + r, p.M - 1) * p.lsa : p.sb + min(n0 + (r - kBM), p.N - 1) * p.lsb;
-            ok &= is_pow2_scale(s[kb]);
-        }
-        chain = workgroup_all(ok, reinterpret_cast<uint32_t*>(smem + 2 * kStageBytes), wave, lane);
-    }
-    // Stage 1 sits past the 16-bit immediate offset of ds_read: hide its
-    // distance from the compiler so each lane offset gets one base register
-    // per stage instead of one per fragment.
     // (Both stage offsets are hidden: a pointer the compiler can fold to a
     // constant loses its restrict scope once main_loop is inlined.)
     int s0_off = 0, s1_off = kStageBytes;
     asm volatile("" : "+s"(s0_off), "+s"(s1_off));
-    stage_barrier();
-    load_stage(p, select_src(src, nkb > 1), smem + s1_off, kb0 + 1, wave, lane);
-    if (chain) {
-        main_loop<true, kFmtA, kFmtB>(p, smem + s0_off, smem + s1_off, acc, o, src, kb0, nkb, wave, lane);
-    } else {
-        main_loop<false, kFmtA, kFmtB>(p, smem + s0_off, smem + s1_off, acc, o, src, kb0, nkb, wave, lane);
+    uint32_t* slots = reinterpret_cast<uint32_t*>(smem + 2 * kStageBytes);
+
+    TileCtx c = tile_ctx(p, tile);
+    load_stage(p, c.src, smem + s0_off, c.kb0, wave, lane);
+    bool ok = kFast ? row_scales_pow2(p, c) : false;
+    for (;;) {
+        // The scaled matrix-core chain is exact only for power-of-two scales:
+        // take it when every scale of this tile's rows and columns over the
+        // contraction range is one.
+        const bool chain = kFast && workgroup_all(ok, slots, wave, lane);
+        stage_barrier();
+        load_stage(p, select_src(c.src, c.nkb > 1), smem + s1_off, c.kb0 + 1, wave, lane);
+
+        v4f acc[kTM][kTN];
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+            for (int j = 0; j < kTN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        if (chain) {
+            main_loop<true, kFmtA, kFmtB>(p, smem + s0_off, smem + s1_off, acc, o, c.src, c.kb0, c.nkb, wave, lane);
+        } else {
+            main_loop<false, kFmtA, kFmtB>(p, smem + s0_off, smem + s1_off, acc, o, c.src, c.kb0, c.nkb, wave, lane);
+        }
+
+        // every wave is done reading the stages: start the next tile's copies
+        // (and its scale test), then write this tile out
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const int64_t next = tile + G;
+        const bool more = next < total_tiles;
+        TileCtx cn = c;
+        if (more) {
+            cn = tile_ctx(p, next);
+            load_stage(p, cn.src, smem + s0_off, cn.kb0, wave, lane);
+            if (kFast) ok = row_scales_pow2(p, cn);
+        }
+        epilogue<kEpi>(p, acc, c.m0, c.n0, c.out_off, wave, lane);
+        if (!more) break;
+        tile = next;
+        c = cn;
     }
-    epilogue<kEpi>(p, acc, m0, n0, out_off, wave, lane);
 }
 
 __global__ void zero_f32_kernel(float* p, int64_t n)
@@ -623,28 +688,44 @@ __global__ void zero_f32_kernel(float* p, int64_t n)
 }
 
 template <int kFmtA, int kFmtB, bool kFast>
-hipError_t launch_epi(const GemmArgs& a, dim3 grid, hipStream_t s)
+hipError_t launch_epi(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s)
 {
     switch (a.epi) {
-    case Epi::Wgrad: gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Wgrad><<<grid, kThreads, 0, s>>>(a); break;
-    case Epi::Fwd: gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Fwd><<<grid, kThreads, 0, s>>>(a); break;
-    case Epi::Dgrad: gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Dgrad><<<grid, kThreads, 0, s>>>(a); break;
+    case Epi::Wgrad: gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Wgrad><<<grid, kThreads, 0, s>>>(a, tiles); break;
+    case Epi::Fwd: gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Fwd><<<grid, kThreads, 0, s>>>(a, tiles); break;
+    case Epi::Dgrad: gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Dgrad><<<grid, kThreads, 0, s>>>(a, tiles); break;
     }
     return hipGetLastError();
 }
 
 template <int kFmtA, int kFmtB>
-hipError_t launch_policy(const GemmArgs& a, dim3 grid, hipStream_t s)
+hipError_t launch_policy(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s)
 {
-    return a.fast ? launch_epi<kFmtA, kFmtB, true>(a, grid, s) : launch_epi<kFmtA, kFmtB, false>(a, grid, s);
+    return a.fast ? launch_epi<kFmtA, kFmtB, true>(a, grid, tiles, s)
+                  : launch_epi<kFmtA, kFmtB, false>(a, grid, tiles, s);
+}
+
+// Compute units of the current device (one persistent workgroup each: the
+// two stages fill most of a CU's LDS).
+int device_cus()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream, LaunchInfo* info)
 {
-    const int64_t tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
-    const int64_t blocks = tiles * a.num_groups;
+    const int64_t tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN) * a.num_groups;
+    const int64_t blocks = std::min<int64_t>(tiles, device_cus());
     if (info) {
         info->tile_m = kBM;
         info->tile_n = kBN;
@@ -652,12 +733,11 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream, LaunchInfo* info)
         info->grid = blocks;
     }
     if (blocks <= 0) return hipSuccess;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks);
-    if (a.fmt_a == FMT_E4M3 && a.fmt_b == FMT_E4M3) return launch_policy<FMT_E4M3, FMT_E4M3>(a, grid, stream);
-    if (a.fmt_a == FMT_E5M2 && a.fmt_b == FMT_E4M3) return launch_policy<FMT_E5M2, FMT_E4M3>(a, grid, stream);
-    if (a.fmt_a == FMT_E4M3 && a.fmt_b == FMT_E5M2) return launch_policy<FMT_E4M3, FMT_E5M2>(a, grid, stream);
-    return launch_policy<FMT_E5M2, FMT_E5M2>(a, grid, stream);
+    if (a.fmt_a == FMT_E4M3 && a.fmt_b == FMT_E4M3) return launch_policy<FMT_E4M3, FMT_E4M3>(a, grid, tiles, stream);
+    if (a.fmt_a == FMT_E5M2 && a.fmt_b == FMT_E4M3) return launch_policy<FMT_E5M2, FMT_E4M3>(a, grid, tiles, stream);
+    if (a.fmt_a == FMT_E4M3 && a.fmt_b == FMT_E5M2) return launch_policy<FMT_E4M3, FMT_E5M2>(a, grid, tiles, stream);
+    return launch_policy<FMT_E5M2, FMT_E5M2>(a, grid, tiles, stream);
 }
 
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream)
