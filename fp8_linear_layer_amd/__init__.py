@@ -36,7 +36,7 @@ TE_EPI_BGRAD = 16
 TE_CAST_POW2_SCALE = 1
 
 EXPORTED = ("te_cast_fp8_per_token", "te_fp8_gemm_fwd", "te_fp8_gemm_dgrad", "te_fp8_wgrad_accum",
-            "te_fp8_kgrouped_wgrad", "te_status_string", "te_last_error_message")
+            "te_fp8_kgrouped_wgrad", "te_status_string", "te_last_error_message", "te_scale_ld")
 
 
 class TeFp8Error(RuntimeError):
@@ -61,6 +61,8 @@ def load_library():
     lib.te_status_string.argtypes = [I]
     lib.te_last_error_message.restype = ctypes.c_char_p
     lib.te_last_error_message.argtypes = []
+    lib.te_scale_ld.restype = I64
+    lib.te_scale_ld.argtypes = [I64]
     lib.te_cast_fp8_per_token.restype = I
     lib.te_cast_fp8_per_token.argtypes = [P, I64, I64, I64, I, U32, P, I64, P, P]
     lib.te_fp8_gemm_fwd.restype = I
@@ -97,14 +99,29 @@ def _cols(t):
 
 
 # --------------------------------------------------------------- entry points
+def scale_ld(rows: int) -> int:
+    """Leading dimension of the block-major scales of an operand with `rows` rows (te_scale_ld)."""
+    return int(load_library().te_scale_ld(int(rows)))
+
+
+def _scales_ok(t, rows, k, name):
+    """The kernels read scales of K/128 blocks at stride scale_ld(rows); refuse anything smaller."""
+    want = (k // 128, scale_ld(rows))
+    if t is None or t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != want:
+        raise TeFp8Error(1, f"{name}: expected contiguous fp32 scales of shape {want} "
+                         f"(got {None if t is None else (tuple(t.shape), t.dtype)})")
+
+
 def te_cast_fp8_per_token(x, out_dtype=TE_DTYPE_E4M3, flags=0, q=None, scales=None, stream=None):
-    """bf16 x [rows, cols] -> (q uint8 [rows, cols], scales fp32 [rows, cols/128])."""
+    """bf16 x [rows, cols] -> (q uint8 [rows, cols], scales fp32 [cols/128, scale_ld(rows)], block-major:
+    the scale of row r and 128-column block kb is scales[kb, r])."""
     assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
     rows, cols = x.shape
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     if scales is None:
-        scales = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device)
+        scales = torch.empty((cols // 128, scale_ld(rows)), dtype=torch.float32, device=x.device)
+    _scales_ok(scales, rows, cols, "scales")
     _check(load_library().te_cast_fp8_per_token(_ptr(x), rows, cols, x.stride(0), out_dtype, flags,
                                                 _ptr(q), q.stride(0), _ptr(scales), _stream(stream)))
     return q, scales
@@ -117,6 +134,8 @@ def te_fp8_gemm_fwd(x, x_scales, x_dtype, w, w_scales, w_dtype, bias=None, epilo
     N = w.shape[0]
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16 if y_dtype == TE_DTYPE_BF16 else torch.float32, device=x.device)
+    _scales_ok(x_scales, M, K, "x_scales")
+    _scales_ok(w_scales, N, K, "w_scales")
     _check(load_library().te_fp8_gemm_fwd(
         _ptr(x), _ptr(x_scales), x_dtype, _ptr(w), _ptr(w_scales), w_dtype, M, N, K,
         _ptr(bias), epilogue, _ptr(y), y_dtype, y.stride(0),
@@ -131,6 +150,8 @@ def te_fp8_gemm_dgrad(dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, epilogue
     N = wt.shape[0]
     if dx is None:
         dx = torch.empty((M, N), dtype=torch.bfloat16 if dx_dtype == TE_DTYPE_BF16 else torch.float32, device=dy.device)
+    _scales_ok(dy_scales, M, K, "dy_scales")
+    _scales_ok(wt_scales, N, K, "wt_scales")
     _check(load_library().te_fp8_gemm_dgrad(
         _ptr(dy), _ptr(dy_scales), dy_dtype, _ptr(wt), _ptr(wt_scales), wt_dtype, M, N, K, epilogue,
         _ptr(preact), preact.stride(0) if preact is not None else 0, _ptr(bias_grad),
@@ -142,6 +163,8 @@ def te_fp8_wgrad_accum(a, a_scales, a_dtype, b, b_scales, b_dtype, out, accum=TE
     """out[M,N] += A[M,K] B[N,K]^T in fp32; returns out."""
     M, K = a.shape
     N = b.shape[0]
+    _scales_ok(a_scales, M, K, "a_scales")
+    _scales_ok(b_scales, N, K, "b_scales")
     _check(load_library().te_fp8_wgrad_accum(
         _ptr(a), _ptr(a_scales), a_dtype, _ptr(b), _ptr(b_scales), b_dtype, M, N, K,
         _ptr(out), out.stride(0), accum, _stream(stream)))
@@ -154,6 +177,8 @@ def te_fp8_kgrouped_wgrad(a, a_scales, a_dtype, b, b_scales, b_dtype, group_k, o
     M = a.shape[0]
     N = b.shape[0]
     gk = (ctypes.c_int64 * len(group_k))(*[int(k) for k in group_k])
+    _scales_ok(a_scales, M, sum(gk), "a_scales")
+    _scales_ok(b_scales, N, sum(gk), "b_scales")
     _check(load_library().te_fp8_kgrouped_wgrad(
         _ptr(a), _ptr(a_scales), a_dtype, _ptr(b), _ptr(b_scales), b_dtype, M, N,
         ctypes.cast(gk, ctypes.c_void_p), len(group_k), _ptr(out), accum, _stream(stream)))

@@ -79,7 +79,7 @@ te_status_t check_operands(const char* fn, const void* a, const float* sa, te_dt
     if (accum != TE_ACCUM_FULL_FP32 && accum != TE_ACCUM_FAST)
         return fail(TE_ERR_INVALID_ARGUMENT, "%s: accum must be TE_ACCUM_FULL_FP32 or TE_ACCUM_FAST (got %d)", fn, (int)accum);
     if (!aligned(a, 16) || !aligned(b, 16)) return fail(TE_ERR_MISALIGNED, "%s: fp8 operands must be 16-byte aligned", fn);
-    if (!aligned(sa, 4) || !aligned(sb, 4)) return fail(TE_ERR_MISALIGNED, "%s: scales must be 4-byte aligned", fn);
+    if (!aligned(sa, 16) || !aligned(sb, 16)) return fail(TE_ERR_MISALIGNED, "%s: scales must be 16-byte aligned", fn);
     return TE_OK;
 }
 
@@ -109,8 +109,8 @@ tefp8::GemmArgs base_args(const void* a, const float* sa, te_dtype_t da, const v
     g.N = N;
     g.lda = K;
     g.ldb = K;
-    g.lsa = K / 128;
-    g.lsb = K / 128;
+    g.lsa = te_scale_ld(M);
+    g.lsb = te_scale_ld(N);
     g.fmt_a = to_fmt(da);
     g.fmt_b = to_fmt(db);
     g.fast = accum == TE_ACCUM_FAST;
@@ -152,6 +152,8 @@ const char* te_status_string(te_status_t s)
 
 const char* te_last_error_message(void) { return g_last_error.c_str(); }
 
+int64_t te_scale_ld(int64_t rows) { return rows > 0 ? (rows + 3) / 4 * 4 : 0; }
+
 te_status_t te_cast_fp8_per_token(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                                   te_dtype_t out_dtype, uint32_t flags, void* q, int64_t ld_q,
                                   float* scales, hipStream_t stream)
@@ -167,11 +169,11 @@ te_status_t te_cast_fp8_per_token(const void* x_bf16, int64_t rows, int64_t cols
         if (flags & ~(uint32_t)TE_CAST_POW2_SCALE) return fail(TE_ERR_INVALID_ARGUMENT, "%s: unknown flag bits 0x%x", fn, flags);
         if (!aligned(x_bf16, 16) || ld_x % 8 != 0) return fail(TE_ERR_MISALIGNED, "%s: x must be 16-byte aligned with ld_x a multiple of 8", fn);
         if (!aligned(q, 16) || ld_q % 16 != 0) return fail(TE_ERR_MISALIGNED, "%s: q must be 16-byte aligned with ld_q a multiple of 16", fn);
-        if (!aligned(scales, 4)) return fail(TE_ERR_MISALIGNED, "%s: scales must be 4-byte aligned", fn);
+        if (!aligned(scales, 16)) return fail(TE_ERR_MISALIGNED, "%s: scales must be 16-byte aligned", fn);
         tefp8::LaunchInfo info{};
         hipError_t e = tefp8::launch_cast(static_cast<const uint16_t*>(x_bf16), rows, cols, ld_x, to_fmt(out_dtype),
                                           (flags & TE_CAST_POW2_SCALE) != 0, static_cast<uint8_t*>(q), ld_q, scales,
-                                          stream, &info);
+                                          te_scale_ld(rows), stream, &info);
         if (log_enabled())
             std::fprintf(stderr, "[te_fp8] %s rows=%lld cols=%lld out=%s pow2=%d threads=%d grid=%lld\n", fn,
                          (long long)rows, (long long)cols, dtype_name(out_dtype), (flags & TE_CAST_POW2_SCALE) ? 1 : 0,

@@ -8,6 +8,9 @@
 // token before the GEMM; the 128-wide groups and the reading of s are this
 // library's definition (see te_fp8.h).
 //
+// Scales are written block-major, scales[group * ld_s + row], so that the GEMM
+// reads the scales of one 128-deep block as one contiguous vector.
+//
 // Memory-bound: 2 bytes read and 1 byte + 1/32 byte written per element.  One
 // group is handled by 8 consecutive lanes, 16 elements (32 bytes) each, so a
 // wave covers 8 groups = 2 KiB of contiguous input, with two 16-byte loads and
@@ -70,7 +73,7 @@ __device__ __forceinline__ uint2 encode8(const float (&v)[8], float fmax)
 template <int kFmt, bool kPow2>
 __global__ __launch_bounds__(kThreads) void cast_per_token_kernel(
     const uint16_t* __restrict__ x, int64_t groups_per_row, int64_t total_groups, int64_t ld_x,
-    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scales)
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scales, int64_t ld_s)
 {
     // FP8_MAX = 1.75 * 2^kMaxExp for both formats (448 and 57344).
     constexpr int kMaxExp = kFmt == FMT_E4M3 ? 8 : 15;
@@ -84,7 +87,8 @@ __global__ __launch_bounds__(kThreads) void cast_per_token_kernel(
     const bool active = group < total_groups;
     const int64_t g = active ? group : total_groups - 1;
     const int64_t row = g / groups_per_row;
-    const int64_t col = (g - row * groups_per_row) * 128 + part * 16;
+    const int64_t gcol = g - row * groups_per_row;
+    const int64_t col = gcol * 128 + part * 16;
 
     const u32x4* src = reinterpret_cast<const u32x4*>(x + row * ld_x + col);
     const u32x4 u0 = __builtin_nontemporal_load(src);
@@ -127,14 +131,14 @@ __global__ __launch_bounds__(kThreads) void cast_per_token_kernel(
     const uint2 c1 = encode8<kFmt>(s1, fmax);
     if (active) {
         *reinterpret_cast<uint4*>(q + row * ld_q + col) = make_uint4(c0.x, c0.y, c1.x, c1.y);
-        if (part == 0) scales[g] = scale;
+        if (part == 0) scales[gcol * ld_s + row] = scale;  // block-major: [cols/128][ld_s]
     }
 }
 
 }  // namespace
 
 hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
-                       bool pow2, uint8_t* q, int64_t ld_q, float* scales, hipStream_t stream,
+                       bool pow2, uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s, hipStream_t stream,
                        LaunchInfo* info)
 {
     const int64_t gpr = cols / 128;
@@ -145,11 +149,11 @@ hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     dim3 grid((unsigned)blocks), block(kThreads);
     if (fmt == FMT_E4M3) {
-        if (pow2) cast_per_token_kernel<FMT_E4M3, true><<<grid, block, 0, stream>>>(x, gpr, total, ld_x, q, ld_q, scales);
-        else cast_per_token_kernel<FMT_E4M3, false><<<grid, block, 0, stream>>>(x, gpr, total, ld_x, q, ld_q, scales);
+        if (pow2) cast_per_token_kernel<FMT_E4M3, true><<<grid, block, 0, stream>>>(x, gpr, total, ld_x, q, ld_q, scales, ld_s);
+        else cast_per_token_kernel<FMT_E4M3, false><<<grid, block, 0, stream>>>(x, gpr, total, ld_x, q, ld_q, scales, ld_s);
     } else {
-        if (pow2) cast_per_token_kernel<FMT_E5M2, true><<<grid, block, 0, stream>>>(x, gpr, total, ld_x, q, ld_q, scales);
-        else cast_per_token_kernel<FMT_E5M2, false><<<grid, block, 0, stream>>>(x, gpr, total, ld_x, q, ld_q, scales);
+        if (pow2) cast_per_token_kernel<FMT_E5M2, true><<<grid, block, 0, stream>>>(x, gpr, total, ld_x, q, ld_q, scales, ld_s);
+        else cast_per_token_kernel<FMT_E5M2, false><<<grid, block, 0, stream>>>(x, gpr, total, ld_x, q, ld_q, scales, ld_s);
     }
     return hipGetLastError();
 }

@@ -62,7 +62,9 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 constexpr int kBM = 256, kBN = 256, kBK = 128;
 constexpr int kTileA = kBM * kBK;                 // 32 KiB
 constexpr int kTileB = kBN * kBK;                 // 32 KiB
-constexpr int kStageBytes = kTileA + kTileB + (kBM + kBN) * 4;
+constexpr int kScaleBytes = (kBM + kBN) * 4;
+constexpr int kSinkBytes = 1024;                  // target of the scale copies of waves that have none
+constexpr int kStageBytes = kTileA + kTileB + kScaleBytes + kSinkBytes;
 constexpr int kGroupM = 8;                        // tile rows per raster group
 constexpr int kXcds = 8;                          // accelerator complex dies (each with its own L2)
 
@@ -82,7 +84,10 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((ch
 // Per-tile buffer resources: bases at the tile's first row, ranges cut at the
 // last valid row (rows past it read as zero: no clamping, no faults).
 struct TileSrc {
-    __amdgpu_buffer_rsrc_t a, b, sa, sb;
+    __amdgpu_buffer_rsrc_t a, b;
+    const float* sa;   // the tile's first row in block 0 of the block-major scales
+    const float* sb;
+    int sa_bytes, sb_bytes;  // valid scale bytes of one block (rows past the scale array's width read zero)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes)
@@ -96,8 +101,10 @@ __device__ __forceinline__ TileSrc tile_src(const GemmArgs& p, int64_t m0, int64
     TileSrc s;
     s.a = make_rsrc(p.a + m0 * p.lda, min((int64_t)kBM, p.M - m0) * p.lda);
     s.b = make_rsrc(p.b + n0 * p.ldb, min((int64_t)kBN, p.N - n0) * p.ldb);
-    s.sa = make_rsrc(p.sa + m0 * p.lsa, min((int64_t)kBM, p.M - m0) * p.lsa * 4);
-    s.sb = make_rsrc(p.sb + n0 * p.lsb, min((int64_t)kBN, p.N - n0) * p.lsb * 4);
+    s.sa = p.sa + m0;
+    s.sb = p.sb + n0;
+    s.sa_bytes = (int)(min((int64_t)kBM, p.lsa - m0) * 4);
+    s.sb_bytes = (int)(min((int64_t)kBN, p.lsb - n0) * 4);
     return s;
 }
 
@@ -106,11 +113,11 @@ __device__ __forceinline__ TileSrc tile_src(const GemmArgs& p, int64_t m0, int64
 // one straight-line block (no branch for the scheduler to sink work across).
 __device__ __forceinline__ TileSrc select_src(const TileSrc& s, bool live)
 {
-    TileSrc e;
+    TileSrc e = s;
     e.a = live ? s.a : __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, 0x00020000);
     e.b = live ? s.b : e.a;
-    e.sa = live ? s.sa : e.a;
-    e.sb = live ? s.sb : e.a;
+    e.sa_bytes = live ? s.sa_bytes : 0;
+    e.sb_bytes = live ? s.sb_bytes : 0;
     return e;
 }
 
@@ -130,12 +137,16 @@ __device__ __forceinline__ void load_stage(const GemmArgs& p, const TileSrc& src
         __builtin_amdgcn_raw_ptr_buffer_load_lds(src.b, (lds_ptr_t)(stage + kTileA + blk * 1024), 16,
                                                  (uint32_t)(row * p.ldb + chunk * 16), kcol, 0, 0);
     }
-    // scales: waves 0-3 carry sA for the 256 tile rows, waves 4-7 sB for the 256 tile columns
-    const bool is_a = wave < 4;
-    const int r = (is_a ? wave : wave - 4) * 64 + lane;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? src.sa : src.sb,
-                                             (lds_ptr_t)(stage + kTileA + kTileB + wave * 256), 4,
-                                             (uint32_t)(r * (is_a ? p.lsa : p.lsb) * 4), kb * 4, 0, 0);
+    // scales of this block: the 256 tile rows' (wave 0) and columns' (wave 1)
+    // scales are contiguous in the block-major layout, one 1 KiB copy each.
+    // The other waves issue an empty copy into the stage's sink (no branch in
+    // the loop body).
+    const bool is_a = wave == 0, is_b = wave == 1;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(is_a ? src.sa + kb * p.lsa : src.sb + kb * p.lsb,
+                                               is_a ? src.sa_bytes : (is_b ? src.sb_bytes : 0));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (lds_ptr_t)(stage + kTileA + kTileB + (is_a ? 0 : (is_b ? 1024 : kScaleBytes))), 16, (uint32_t)(lane * 16),
+        0, 0, 0);
 }
 
 // This lane's byte offsets inside a stage.
@@ -585,32 +596,22 @@ __device__ __forceinline__ TileCtx tile_ctx(const GemmArgs& p, int64_t tile)
 
 // This thread's share of the FAST test: are the scales of one tile row (A) or
 // column (B) over the tile's contraction range all powers of two?  Thread r
-// takes row r of the 256 A rows and 256 B rows; the loads are batched so they
-// are in flight together.
+// takes row r of the 256 A rows and 256 B rows (consecutive threads read
+// consecutive scales of a block); the loads are batched so they are in flight
+// together.
 __device__ __forceinline__ bool row_scales_pow2(const GemmArgs& p, const TileCtx& c)
 {
     const int r = threadIdx.x;
-    const float* s = r < kBM ? p.sa + min(c.m0 + r, p.M - 1) * p.lsa : p.sb + min(c.n0 + (r - kBM), p.N - 1) * p.lsb;
-    s += c.kb0;
+    const int64_t ld = r < kBM ? p.lsa : p.lsb;
+    const float* s = r < kBM ? p.sa + min(c.m0 + r, p.M - 1) : p.sb + min(c.n0 + (r - kBM), p.N - 1);
+    s += (int64_t)c.kb0 * ld;
     bool ok = true;
-    if ((reinterpret_cast<uintptr_t>(s) & 15) == 0 && (c.nkb & 3) == 0) {
-        for (int kb = 0; kb < c.nkb; kb += 32) {
-            float4 v[8];
+    for (int kb = 0; kb < c.nkb; kb += 16) {
+        float v[16];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                v[u] = kb + 4 * u < c.nkb ? *reinterpret_cast<const float4*>(s + kb + 4 * u) : make_float4(1.f, 1.f, 1.f, 1.f);
+        for (int u = 0; u < 16; ++u) v[u] = kb + u < c.nkb ? s[(int64_t)(kb + u) * ld] : 1.f;
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                ok = ok && is_pow2_scale(v[u].x) && is_pow2_scale(v[u].y) && is_pow2_scale(v[u].z) && is_pow2_scale(v[u].w);
-        }
-    } else {
-        for (int kb = 0; kb < c.nkb; kb += 16) {
-            float v[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) v[u] = kb + u < c.nkb ? s[kb + u] : 1.f;
-#pragma unroll
-            for (int u = 0; u < 16; ++u) ok = ok && is_pow2_scale(v[u]);
-        }
+        for (int u = 0; u < 16; ++u) ok = ok && is_pow2_scale(v[u]);
     }
     return ok;
 }

@@ -28,12 +28,12 @@ constexpr int kMaxGroupsPerLaunch = 128;
 
 struct GemmArgs {
     const uint8_t* a;      // [M][lda] fp8
-    const float* sa;       // [M][lsa]
+    const float* sa;       // [K/128][lsa]
     const uint8_t* b;      // [N][ldb] fp8
-    const float* sb;       // [N][lsb]
+    const float* sb;       // [K/128][lsb]
     int64_t M, N;
     int64_t lda, ldb;      // bytes
-    int64_t lsa, lsb;      // floats
+    int64_t lsa, lsb;      // floats between consecutive 128-deep blocks of sa / sb (block-major scales)
     int fmt_a, fmt_b;      // Fmt
     bool fast;             // accumulation policy
     Epi epi;
@@ -61,7 +61,7 @@ struct LaunchInfo {
 hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream, LaunchInfo* info);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
-                       bool pow2, uint8_t* q, int64_t ld_q, float* scales, hipStream_t stream,
+                       bool pow2, uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s, hipStream_t stream,
                        LaunchInfo* info);
 
 }  // namespace tefp8

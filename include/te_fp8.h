@@ -20,10 +20,14 @@
  *            bias vector always has length N, the output-feature count.
  *  Scales.   Operands are fp8 with one fp32 dequantisation scale per row and
  *            per 128 consecutive contraction elements ("1x128" groups): the
- *            value of element (r, k) is dec(q[r][k]) * s[r][k/128].  Scales
- *            are row-major [rows][K/128], contiguous.  K must be a multiple of
- *            128 and at most 2^22 (for the K-grouped call: the sum of the
- *            groups' K).
+ *            value of element (r, k) is dec(q[r][k]) * s(r, k/128).  Scales
+ *            are stored contraction-block-major, like the transposed,
+ *            16-byte-aligned scale layout of the DeepGEMM weight-gradient
+ *            kernels: s(r, kb) = scales[kb * te_scale_ld(rows) + r], i.e. an
+ *            array [K/128][te_scale_ld(rows)] whose row kb holds the scales of
+ *            all rows for block kb (entries r >= rows are padding, never
+ *            used).  K must be a multiple of 128 and at most 2^22 (for the
+ *            K-grouped call: the sum of the groups' K).
  *  Formats.  TE_DTYPE_E4M3 is OCP E4M3FN (max 448), TE_DTYPE_E5M2 is OCP
  *            E5M2 (max 57344).  Any pairing of the two is accepted.
  *  Accumulation policy.  Every GEMM takes an explicit te_accum_t; it is
@@ -53,8 +57,8 @@
  *            surface at the caller's next synchronisation.  No C++ exception
  *            crosses this interface.  Calls are thread-safe; calls that
  *            overlap on one stream are ordered by it.
- *  Alignment. fp8 and bf16 base pointers must be 16-byte aligned, fp32
- *            scale and output pointers 4-byte aligned.
+ *  Alignment. fp8, bf16 and scale base pointers must be 16-byte aligned,
+ *            other fp32 pointers 4-byte aligned.
  *  Logging.  With the environment variable TE_FP8_LOG=1 every call prints one
  *            line to stderr (operation, sizes, formats, policy, epilogue,
  *            tile, grid).  Logging never changes results.
@@ -116,6 +120,13 @@ enum {
 };
 
 /*
+ * Leading dimension, in floats, of the scale array of an operand with `rows`
+ * rows: rows rounded up to a multiple of 4, so every block's scales start on
+ * a 16-byte boundary.  Returns 0 for rows <= 0.
+ */
+int64_t te_scale_ld(int64_t rows);
+
+/*
  * Per-token 1x128 cast of a bf16 matrix to fp8 with fp32 scales.
  *
  * The pages name this step (the wgrad example casts both operands with a
@@ -135,7 +146,8 @@ enum {
  *  out_dtype TE_DTYPE_E4M3 or TE_DTYPE_E5M2
  *  flags    0 or TE_CAST_POW2_SCALE
  *  q        [rows][ld_q] bytes, ld_q >= cols, ld_q % 16 == 0
- *  scales   [rows][cols/128] fp32, contiguous
+ *  scales   [cols/128][te_scale_ld(rows)] fp32 (block-major, see Scales);
+ *           padding entries are left untouched
  */
 te_status_t te_cast_fp8_per_token(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                                   te_dtype_t out_dtype, uint32_t flags, void* q, int64_t ld_q,
@@ -148,8 +160,8 @@ te_status_t te_cast_fp8_per_token(const void* x_bf16, int64_t rows, int64_t cols
  *   y = GELU(z)                if TE_EPI_GELU, else z
  *   preact[m][n] = bf16(z)     if TE_EPI_AUX_PREACT (requires TE_EPI_GELU)
  *
- *  x, x_scales   [M][K] fp8, [M][K/128] fp32
- *  w, w_scales   [N][K] fp8, [N][K/128] fp32
+ *  x, x_scales   [M][K] fp8, [K/128][te_scale_ld(M)] fp32
+ *  w, w_scales   [N][K] fp8, [K/128][te_scale_ld(N)] fp32
  *  bias_bf16     [N] bf16, required iff TE_EPI_BIAS
  *  y             [M][ld_y], y_dtype TE_DTYPE_BF16 or TE_DTYPE_F32, ld_y >= N
  *                (ld_y % 8 == 0 for bf16, % 4 == 0 for fp32)
@@ -175,8 +187,8 @@ te_status_t te_fp8_gemm_fwd(const void* x, const float* x_scales, te_dtype_t x_d
  * dGELU is applied before the bias gradient.  The bias-gradient sum is formed
  * with atomic fp32 additions, so its last bits may vary from run to run.
  *
- *  dy, dy_scales [M][K] fp8 (typically E5M2), [M][K/128]
- *  wt, wt_scales [N][K] fp8 (W^T re-cast along the out dimension), [N][K/128]
+ *  dy, dy_scales [M][K] fp8 (typically E5M2), [K/128][te_scale_ld(M)]
+ *  wt, wt_scales [N][K] fp8 (W^T re-cast along the out dimension), [K/128][te_scale_ld(N)]
  *  preact_bf16   [M][ld_preact] bf16, required iff TE_EPI_DGELU
  *  bias_grad     [N] fp32, required iff TE_EPI_BGRAD
  *  dx            [M][ld_dx], dx_dtype TE_DTYPE_BF16 or TE_DTYPE_F32
@@ -195,8 +207,8 @@ te_status_t te_fp8_gemm_dgrad(const void* dy, const float* dy_scales, te_dtype_t
  * rounding of the sum), as the gradient of a weight accumulates over
  * micro-batches.  A second identical call adds the product again.
  *
- *  a, a_scales   [M][K] fp8 (dY^T, cast along tokens), [M][K/128]
- *  b, b_scales   [N][K] fp8 (X^T, cast along tokens), [N][K/128]
+ *  a, a_scales   [M][K] fp8 (dY^T, cast along tokens), [K/128][te_scale_ld(M)]
+ *  b, b_scales   [N][K] fp8 (X^T, cast along tokens), [K/128][te_scale_ld(N)]
  *  out           [M][ld_out] fp32, ld_out >= N, read and written
  */
 te_status_t te_fp8_wgrad_accum(const void* a, const float* a_scales, te_dtype_t a_dtype,
@@ -212,8 +224,8 @@ te_status_t te_fp8_wgrad_accum(const void* a, const float* a_scales, te_dtype_t 
  *   out[g][m][n] += sum_{k in group g} a[m][k] b[n][k].
  * A group with K_g = 0 leaves out[g] untouched.
  *
- *  a, a_scales   [M][sumK] fp8, [M][sumK/128]
- *  b, b_scales   [N][sumK] fp8, [N][sumK/128]
+ *  a, a_scales   [M][sumK] fp8, [sumK/128][te_scale_ld(M)]
+ *  b, b_scales   [N][sumK] fp8, [sumK/128][te_scale_ld(N)]
  *  group_k       HOST array of G int64, each >= 0 and a multiple of 128,
  *                sumK = their sum >= 128
  *  G             1 .. 1024

@@ -70,10 +70,33 @@ def check_bf16(got, want, mag, what=""):
                            f"{np.argwhere(bad)[0]} got {got[bad][0]} want {want[bad][0]}")
 
 
+def scale_ld(rows):
+    """Leading dimension of block-major scales, as the library reports it."""
+    import fp8_linear_layer_amd as te
+    return te.scale_ld(rows)
+
+
+def sdev(s, fill=0.0):
+    """Row-major oracle scales [rows][K/128] -> block-major device array [K/128][scale_ld(rows)].
+
+    The padding rows carry `fill`, so a kernel that read them would show it.
+    """
+    s = np.asarray(s, np.float32)
+    rows, nkb = s.shape
+    bm = np.full((nkb, scale_ld(rows)), fill, np.float32)
+    bm[:, :rows] = s.T
+    return dev(bm)
+
+
+def shost(t, rows):
+    """Block-major device scales -> row-major numpy [rows][K/128] (the padding is dropped)."""
+    return t.cpu().numpy()[:, :rows].T.copy()
+
+
 def cast_host(bits, fmt, pow2=False):
     """Oracle cast on the host -> (q, s) numpy."""
     return oracle.cast_per_token(bits, fmt, pow2)
 
 
 def to_dev_operand(q, s):
-    return dev(q), dev(s)
+    return dev(q), sdev(s)

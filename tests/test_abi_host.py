@@ -10,6 +10,7 @@ import os
 import re
 
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "te_fp8.h")
@@ -72,6 +73,7 @@ def wgrad(lib, a=A, sa=S, da=1, b=B, sb=S, db=1, M=256, N=256, K=512, out=O, ld=
     (dict(accum=0), INV), (dict(accum=3), INV),
     (dict(ld=255), INV), (dict(ld=258), MISAL),
     (dict(a=MIS), MISAL), (dict(b=MIS), MISAL), (dict(out=MIS), MISAL), (dict(sa=S + 2), MISAL),
+    (dict(sa=S + 4), MISAL), (dict(sb=S + 8), MISAL),   # block-major scales are copied 16 bytes at a time
 ])
 def test_wgrad_rejects(lib, kw, status):
     assert wgrad(lib, **kw) == status
@@ -149,9 +151,24 @@ def cast(lib, x=A, rows=4, cols=256, ldx=256, dt=1, flags=0, q=B, ldq=256, s=S):
     (dict(cols=100), INV), (dict(cols=0), INV), (dict(ldx=128), INV), (dict(ldq=128), INV),
     (dict(dt=3), INV), (dict(flags=2), INV),
     (dict(x=MIS), MISAL), (dict(ldx=260), MISAL), (dict(q=MIS), MISAL), (dict(ldq=264), MISAL), (dict(s=S + 1), MISAL),
+    (dict(s=S + 4), MISAL),
 ])
 def test_cast_rejects(lib, kw, status):
     assert cast(lib, **kw) == status
+
+
+@pytest.mark.parametrize("rows,ld", [(0, 0), (1, 4), (3, 4), (4, 4), (5, 8), (7168, 7168), (2113, 2116)])
+def test_scale_ld(lib, rows, ld):
+    assert lib.te_scale_ld(rows) == ld
+    assert te.scale_ld(rows) == ld
+
+
+def test_binding_checks_scale_shape(lib):
+    q = torch.zeros((8, 256), dtype=torch.uint8)
+    with pytest.raises(te.TeFp8Error, match="x_scales"):
+        te.te_fp8_gemm_fwd(q, torch.zeros((8, 2)), 1, q, torch.zeros((2, 8)), 1)
+    with pytest.raises(te.TeFp8Error, match="b_scales"):
+        te.te_fp8_wgrad_accum(q, torch.zeros((2, 8)), 1, q, torch.zeros((2, 4)), 1, torch.zeros((8, 8)))
 
 
 def test_status_strings(lib):

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import workloads as W
-from parity import bf16_dev, host
+from parity import bf16_dev, host, scale_ld, shost
 
 te = pytest.importorskip("fp8_linear_layer_amd")
 pytestmark = pytest.mark.gpu
@@ -30,12 +30,14 @@ def gpu_cast(bits, dt, pow2, ld_x=None, ld_q=None):
     xb[:, :cols] = bits
     x = bf16_dev(xb)[:, :cols]
     qfull = torch.full((rows, ld_q), 0xA5, dtype=torch.uint8, device="cuda")
-    s = torch.full((rows, cols // 128), -7.0, dtype=torch.float32, device="cuda")
+    s = torch.full((cols // 128, scale_ld(rows)), -7.0, dtype=torch.float32, device="cuda")
     te.te_cast_fp8_per_token(x, dt, te.TE_CAST_POW2_SCALE if pow2 else 0, q=qfull[:, :cols], scales=s)
     torch.cuda.synchronize()
     qh = host(qfull).numpy()
     assert (qh[:, cols:] == 0xA5).all(), "cast wrote past cols"
-    return qh[:, :cols], host(s).numpy()
+    sh = host(s).numpy()
+    assert (sh[:, rows:] == -7.0).all(), "cast wrote into the scale padding"
+    return qh[:, :cols], shost(s, rows)
 
 
 def assert_same(bits, dt, pow2, **kw):

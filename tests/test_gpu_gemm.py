@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads as W
-from parity import GELU_LIP, bf16_dev, bf16_host_f64, check_bf16, check_f32, dev, host
+from parity import GELU_LIP, bf16_dev, bf16_host_f64, check_bf16, check_f32, dev, host, sdev
 
 te = pytest.importorskip("fp8_linear_layer_amd")
 pytestmark = pytest.mark.gpu
@@ -66,7 +66,7 @@ def test_wgrad_small(accum, pow2, da, db, M, N, K):
     buf = torch.full((M + 1, ld), 1234.5, dtype=torch.float32, device="cuda")
     buf[:M, :N] = dev(out0)
     out = buf[:M, :N]
-    te.te_fp8_wgrad_accum(dev(qa), dev(sa), da, dev(qb), dev(sb), db, out, accum)
+    te.te_fp8_wgrad_accum(dev(qa), sdev(sa), da, dev(qb), sdev(sb), db, out, accum)
     torch.cuda.synchronize()
     b = host(buf).numpy()
     assert (b[:M, N:] == 1234.5).all() and (b[M:] == 1234.5).all(), "wrote outside out"
@@ -82,15 +82,15 @@ def test_wgrad_pages_ones_example():
     qy, sy = oracle.cast_per_token(y, oracle.E4M3)
     ref = (W.bf16_bits_to_f32(x) @ W.bf16_bits_to_f32(y).T).astype(np.float32)
     out1 = dev(ref)
-    te.te_fp8_wgrad_accum(dev(qx), dev(sx), E4, dev(qy), dev(sy), E4, out1, FULL)
+    te.te_fp8_wgrad_accum(dev(qx), sdev(sx), E4, dev(qy), sdev(sy), E4, out1, FULL)
     r = host(out1).numpy() / ref
     assert np.all(np.abs(r - 2.0) < 2e-3), (r.min(), r.max())
     out0 = torch.zeros((m, n), dtype=torch.float32, device="cuda")
-    te.te_fp8_wgrad_accum(dev(qx), dev(sx), E4, dev(qy), dev(sy), E4, out0, FULL)
+    te.te_fp8_wgrad_accum(dev(qx), sdev(sx), E4, dev(qy), sdev(sy), E4, out0, FULL)
     r0 = host(out0).numpy() / ref
     assert np.all(np.abs(r0 - 1.0) < 2e-3)
     # a second call doubles
-    te.te_fp8_wgrad_accum(dev(qx), dev(sx), E4, dev(qy), dev(sy), E4, out0, FULL)
+    te.te_fp8_wgrad_accum(dev(qx), sdev(sx), E4, dev(qy), sdev(sy), E4, out0, FULL)
     assert np.allclose(host(out0).numpy() / ref, 2 * r0, rtol=1e-6)
 
 
@@ -101,7 +101,7 @@ def test_wgrad_deterministic(accum):
     outs = []
     for _ in range(2):
         out = torch.zeros((384, 640), dtype=torch.float32, device="cuda")
-        te.te_fp8_wgrad_accum(dev(qa), dev(sa), E4, dev(qb), dev(sb), E4, out, accum)
+        te.te_fp8_wgrad_accum(dev(qa), sdev(sa), E4, dev(qb), sdev(sb), E4, out, accum)
         outs.append(host(out).numpy())
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
 
@@ -113,7 +113,7 @@ def test_wgrad_dense_workload(accum, pow2):
     qa, sa = oracle.cast_per_token(inp["a"], oracle.E4M3, pow2)
     qb, sb = oracle.cast_per_token(inp["b"], oracle.E4M3, pow2)
     out = dev(inp["out0"])
-    te.te_fp8_wgrad_accum(dev(qa), dev(sa), E4, dev(qb), dev(sb), E4, out, accum)
+    te.te_fp8_wgrad_accum(dev(qa), sdev(sa), E4, dev(qb), sdev(sb), E4, out, accum)
     got = host(out).numpy()
     rows, cols = sample_idx(sh["M"], 40, 1), sample_idx(sh["N"], 40, 2)
     o, d = grid_entries(qa, sa, oracle.E4M3, qb, sb, oracle.E4M3, rows, cols)
@@ -151,7 +151,7 @@ def test_fwd_small(accum, pow2, epi, ydt, M, N, K):
     if epi & te.TE_EPI_AUX_PREACT:
         prebuf = torch.full((M, ld), 55.0, dtype=torch.bfloat16, device="cuda")
         pre = prebuf[:, :N]
-    te.te_fp8_gemm_fwd(dev(qx), dev(sx), E4, dev(qw), dev(sw), E4,
+    te.te_fp8_gemm_fwd(dev(qx), sdev(sx), E4, dev(qw), sdev(sw), E4,
                        bias=bf16_dev(b) if epi & te.TE_EPI_BIAS else None, epilogue=epi,
                        y=yv, y_dtype=ydt, preact=pre, accum=accum)
     torch.cuda.synchronize()
@@ -175,12 +175,12 @@ def test_fwd_tiny_workload():
     o, d = oracle.gemm_nt(qx, sx, oracle.E4M3, qw, sw, oracle.E4M3)
     y, z, zmag = oracle.fwd_epilogue(o, d, inp["b"], True)
     for accum in (FULL, FAST):
-        yg = te.te_fp8_gemm_fwd(dev(qx), dev(sx), E4, dev(qw), dev(sw), E4, bias=bf16_dev(inp["b"]),
+        yg = te.te_fp8_gemm_fwd(dev(qx), sdev(sx), E4, dev(qw), sdev(sw), E4, bias=bf16_dev(inp["b"]),
                                 epilogue=te.TE_EPI_BIAS | te.TE_EPI_GELU, y_dtype=te.TE_DTYPE_F32, accum=accum)
         check_f32(host(yg).numpy(), y, zmag * GELU_LIP, "tiny fwd")
     want, mag = oracle.wgrad(o, d, inp["out0"])
     out = dev(inp["out0"])
-    te.te_fp8_wgrad_accum(dev(qx), dev(sx), E4, dev(qw), dev(sw), E4, out, FULL)
+    te.te_fp8_wgrad_accum(dev(qx), sdev(sx), E4, dev(qw), sdev(sw), E4, out, FULL)
     check_f32(host(out).numpy(), want, mag, "tiny wgrad")
 
 
@@ -192,7 +192,7 @@ def test_fwd_workload(accum, pow2):
     qw, sw = oracle.cast_per_token(inp["w"], oracle.E4M3, pow2)
     epi = te.TE_EPI_BIAS | te.TE_EPI_GELU | te.TE_EPI_AUX_PREACT
     pre = torch.empty((sh["M"], sh["N"]), dtype=torch.bfloat16, device="cuda")
-    yg = te.te_fp8_gemm_fwd(dev(qx), dev(sx), E4, dev(qw), dev(sw), E4, bias=bf16_dev(inp["b"]), epilogue=epi,
+    yg = te.te_fp8_gemm_fwd(dev(qx), sdev(sx), E4, dev(qw), sdev(sw), E4, bias=bf16_dev(inp["b"]), epilogue=epi,
                             y_dtype=te.TE_DTYPE_BF16, preact=pre, accum=accum)
     rows, cols = sample_idx(sh["M"], 24, 3), sample_idx(sh["N"], 40, 4)
     o, d = grid_entries(qx, sx, oracle.E4M3, qw, sw, oracle.E4M3, rows, cols)
@@ -221,7 +221,7 @@ def test_dgrad_small(accum, pow2, epi, dxdt, M, N, K):
     bg = torch.full((N + 4,), 3.0, dtype=torch.float32, device="cuda") if epi & te.TE_EPI_BGRAD else None
     zpad = np.zeros((M, ld), np.uint16)
     zpad[:, :N] = zb
-    te.te_fp8_gemm_dgrad(dev(qa), dev(sa), E5, dev(qb), dev(sb), E4, epilogue=epi,
+    te.te_fp8_gemm_dgrad(dev(qa), sdev(sa), E5, dev(qb), sdev(sb), E4, epilogue=epi,
                          preact=bf16_dev(zpad)[:, :N] if epi & te.TE_EPI_DGELU else None,
                          bias_grad=bg[:N] if bg is not None else None, dx=dxbuf[:, :N], dx_dtype=dxdt, accum=accum)
     torch.cuda.synchronize()
@@ -244,7 +244,7 @@ def test_dgrad_workload_dx(accum):
     inp = W.dgrad_inputs()
     qa, sa = oracle.cast_per_token(inp["dy"], oracle.E5M2)
     qb, sb = oracle.cast_per_token(inp["wt"], oracle.E4M3)
-    dx = te.te_fp8_gemm_dgrad(dev(qa), dev(sa), E5, dev(qb), dev(sb), E4, accum=accum)
+    dx = te.te_fp8_gemm_dgrad(dev(qa), sdev(sa), E5, dev(qb), sdev(sb), E4, accum=accum)
     rows, cols = sample_idx(sh["M"], 24, 5), sample_idx(sh["N"], 40, 6)
     o, d = grid_entries(qa, sa, oracle.E5M2, qb, sb, oracle.E4M3, rows, cols)
     check_bf16(bf16_host_f64(dx)[np.ix_(rows, cols)], o, d, "dgrad dX")
@@ -259,7 +259,7 @@ def test_dgrad_workload_dgelu_bgrad():
     qb, sb = oracle.cast_per_token(inp["w2t"], oracle.E4M3)
     z = inp["z"]
     bg = torch.empty((N,), dtype=torch.float32, device="cuda")
-    dz = te.te_fp8_gemm_dgrad(dev(qa), dev(sa), E5, dev(qb), dev(sb), E4,
+    dz = te.te_fp8_gemm_dgrad(dev(qa), sdev(sa), E5, dev(qb), sdev(sb), E4,
                               epilogue=te.TE_EPI_DGELU | te.TE_EPI_BGRAD, preact=bf16_dev(z), bias_grad=bg,
                               accum=FULL)
     rows, cols = sample_idx(M, 16, 7), sample_idx(N, 24, 8)
@@ -282,7 +282,7 @@ def test_kgrouped_small(accum, pow2):
     init = W.normal_f32(np.random.SeedSequence(33), (len(gk), M, N))
     want, mag = oracle.kgrouped_wgrad(qa, sa, oracle.E4M3, qb, sb, oracle.E4M3, gk, init)
     out = dev(init)
-    te.te_fp8_kgrouped_wgrad(dev(qa), dev(sa), E4, dev(qb), dev(sb), E4, gk.tolist(), out, accum)
+    te.te_fp8_kgrouped_wgrad(dev(qa), sdev(sa), E4, dev(qb), sdev(sb), E4, gk.tolist(), out, accum)
     got = host(out).numpy()
     for g in range(len(gk)):
         if gk[g] == 0:
@@ -302,7 +302,7 @@ def test_kgrouped_many_groups():
     init = W.normal_f32(np.random.SeedSequence(43), (len(gk), M, N))
     want, mag = oracle.kgrouped_wgrad(qa, sa, oracle.E4M3, qb, sb, oracle.E4M3, gk, init)
     out = dev(init)
-    te.te_fp8_kgrouped_wgrad(dev(qa), dev(sa), E4, dev(qb), dev(sb), E4, gk.tolist(), out, FULL)
+    te.te_fp8_kgrouped_wgrad(dev(qa), sdev(sa), E4, dev(qb), sdev(sb), E4, gk.tolist(), out, FULL)
     check_f32(host(out).numpy(), want, mag, "300 groups")
 
 
@@ -313,7 +313,7 @@ def test_kgrouped_workload():
     qa, sa = oracle.cast_per_token(inp["a"], oracle.E4M3)
     qb, sb = oracle.cast_per_token(inp["b"], oracle.E4M3)
     out = dev(inp["out0"])
-    te.te_fp8_kgrouped_wgrad(dev(qa), dev(sa), E4, dev(qb), dev(sb), E4, gk.tolist(), out, FULL)
+    te.te_fp8_kgrouped_wgrad(dev(qa), sdev(sa), E4, dev(qb), sdev(sb), E4, gk.tolist(), out, FULL)
     got = host(out).numpy()
     offs = np.concatenate([[0], np.cumsum(gk)])
     for g in range(sh["G"]):
