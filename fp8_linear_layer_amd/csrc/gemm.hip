@@ -24,8 +24,10 @@
 //    accumulator through the matrix core with no vector work; any other tile
 //    is promoted like FULL.
 //  * The B tile is the instruction's first operand, so each lane's four
-//    accumulator registers are four consecutive n of one row m: stores are
-//    16-byte (fp32) / 8-byte (bf16) vectors along the output row.
+//    accumulator registers are four consecutive n of one row m.  The wgrad
+//    update reads and writes them as one 16-byte vector; the Linear-layer
+//    epilogues first pair neighbouring column groups across lanes so that
+//    every lane owns eight consecutive columns (16-byte bf16 runs).
 //  * Operands stream global -> LDS with buffer_load ... lds (no register
 //    staging) into two stages.  Each 128-byte LDS row stores its 16-byte chunk
 //    c at slot c ^ ((row >> 1) & 7), so the 16 rows read by one 16-lane group
@@ -429,133 +431,228 @@ __device__ __forceinline__ void main_loop(const GemmArgs& p, uint8_t* __restrict
     }
 }
 
-// Epilogue: lane holds D[m][n..n+3] for every (i, j).
+__device__ __forceinline__ void unpack_bf16x8(const uint4 w, float (&f)[8])
+{
+    f[0] = bf16_to_f32(w.x & 0xFFFF); f[1] = bf16_to_f32(w.x >> 16);
+    f[2] = bf16_to_f32(w.y & 0xFFFF); f[3] = bf16_to_f32(w.y >> 16);
+    f[4] = bf16_to_f32(w.z & 0xFFFF); f[5] = bf16_to_f32(w.z >> 16);
+    f[6] = bf16_to_f32(w.w & 0xFFFF); f[7] = bf16_to_f32(w.w >> 16);
+}
+
+// Eight bf16 values to dst[0..7]: one 16-byte store, or element by element
+// up to `left` when the run crosses the last column.
+__device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&v)[8], bool full, int64_t left)
+{
+    if (full) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16),
+                                                    bf16_rne(v[2]) | (bf16_rne(v[3]) << 16),
+                                                    bf16_rne(v[4]) | (bf16_rne(v[5]) << 16),
+                                                    bf16_rne(v[6]) | (bf16_rne(v[7]) << 16));
+    } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) if (r < left) dst[r] = (uint16_t)bf16_rne(v[r]);
+    }
+}
+
+// Epilogue.  Lane (r16, q4) holds D[m][n..n+3] of every (i, j), with m = 16 i
+// + r16 and n = 16 j + 4 q4 in the wave's frame.  Wgrad adds those four
+// columns into out in place.  The Linear-layer epilogues pair column groups
+// j, j + 1: one v_permlane16_swap per register pair exchanges the odd 16-lane
+// rows of group j with the even rows of group j + 1, after which every lane
+// holds eight consecutive columns of its row (group j + (q4 & 1), columns
+// 8 (q4 >> 1) .. +7).  Each bf16 load and store is then a 16-byte run, and
+// four lanes cover 64 contiguous bytes of a row.
 template <int kEpi>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM][kTN], int64_t m0, int64_t n0,
                                          int64_t out_off, int wave, int lane)
 {
     const int wm = wave / kWavesN, wn = wave % kWavesN;
+    // (the lane index is re-derived here so that its address arithmetic is not
+    // hoisted out of the tile loop and held in registers across the K loop)
+    asm volatile("" : "+v"(lane));
     const int r16 = lane & 15, q4 = lane >> 4;
-    float colsum[kTN][4];
+
+    if (kEpi == (int)Epi::Wgrad) {
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            const int64_t n = n0 + wn * kWN + j * 16 + q4 * 4;
+            const bool full4 = n + 3 < p.N;
+#pragma unroll
+            for (int i = 0; i < kTM; ++i) {
+                const int64_t m = m0 + wm * kWM + i * 16 + r16;
+                if (m >= p.M || n >= p.N) continue;
+                float* o = reinterpret_cast<float*>(p.out) + out_off + m * p.ld_out + n;
+                if (full4) {
+                    float4 cur = *reinterpret_cast<float4*>(o);
+                    cur.x += acc[i][j][0]; cur.y += acc[i][j][1]; cur.z += acc[i][j][2]; cur.w += acc[i][j][3];
+                    *reinterpret_cast<float4*>(o) = cur;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) if (n + r < p.N) o[r] += acc[i][j][r];
+                }
+            }
+        }
+        return;
+    }
+
     if (kEpi == (int)Epi::Dgrad) {
+        // The arithmetic stays in the accumulator layout (four columns per
+        // lane); the memory side uses the paired layout.  The swap is its own
+        // inverse: the 16-byte run of Z a lane loads for its paired columns
+        // swaps back into the bf16 pairs of its own columns, and the packed
+        // results swap forward into the run it stores.  Positions past M or N
+        // hold zero products (their operand rows read as zero), so only the
+        // loads and stores are masked.
+        const bool has_dgelu = (p.flags & TE_EPI_DGELU) != 0;
+        const bool has_bgrad = (p.flags & TE_EPI_BGRAD) != 0;
+        float colsum[kTN][4];
 #pragma unroll
         for (int j = 0; j < kTN; ++j) colsum[j][0] = colsum[j][1] = colsum[j][2] = colsum[j][3] = 0.f;
+#pragma unroll
+        for (int jp = 0; jp < kTN / 2; ++jp) {
+            const int j0 = 2 * jp, j1 = 2 * jp + 1;
+            const int64_t np = n0 + wn * kWN + (j0 + (q4 & 1)) * 16 + (q4 >> 1) * 8;  // this lane's run
+            const bool fullp = np + 7 < p.N;
+#pragma unroll
+            for (int i = 0; i < kTM; ++i) {
+                const int64_t m = m0 + wm * kWM + i * 16 + r16;
+                const bool live = m < p.M && np < p.N;
+                float v0[4] = {acc[i][j0][0], acc[i][j0][1], acc[i][j0][2], acc[i][j0][3]};
+                float v1[4] = {acc[i][j1][0], acc[i][j1][1], acc[i][j1][2], acc[i][j1][3]};
+                if (has_dgelu) {
+                    uint32_t zw[4] = {0u, 0u, 0u, 0u};
+                    const uint16_t* z = p.preact + m * p.ld_aux + np;
+                    if (live && fullp) {
+                        const uint4 t = *reinterpret_cast<const uint4*>(z);
+                        zw[0] = t.x; zw[1] = t.y; zw[2] = t.z; zw[3] = t.w;
+                    } else if (live) {
+#pragma unroll
+                        for (int r = 0; r < 8; ++r)
+                            if (np + r < p.N) zw[r >> 1] |= (uint32_t)z[r] << (16 * (r & 1));
+                    }
+                    const auto lo = __builtin_amdgcn_permlane16_swap(zw[0], zw[2], false, false);
+                    const auto hi = __builtin_amdgcn_permlane16_swap(zw[1], zw[3], false, false);
+                    const uint32_t a0 = lo[0], b0 = lo[1], a1 = hi[0], b1 = hi[1];
+                    v0[0] *= dgelu(bf16_to_f32(a0 & 0xFFFF)); v0[1] *= dgelu(bf16_to_f32(a0 >> 16));
+                    v0[2] *= dgelu(bf16_to_f32(a1 & 0xFFFF)); v0[3] *= dgelu(bf16_to_f32(a1 >> 16));
+                    v1[0] *= dgelu(bf16_to_f32(b0 & 0xFFFF)); v1[1] *= dgelu(bf16_to_f32(b0 >> 16));
+                    v1[2] *= dgelu(bf16_to_f32(b1 & 0xFFFF)); v1[3] *= dgelu(bf16_to_f32(b1 >> 16));
+                }
+                if (has_bgrad) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        colsum[j0][r] += v0[r];
+                        colsum[j1][r] += v1[r];
+                    }
+                }
+                if (p.out_bf16) {
+                    const auto lo = __builtin_amdgcn_permlane16_swap(bf16_rne(v0[0]) | (bf16_rne(v0[1]) << 16),
+                                                                     bf16_rne(v1[0]) | (bf16_rne(v1[1]) << 16),
+                                                                     false, false);
+                    const auto hi = __builtin_amdgcn_permlane16_swap(bf16_rne(v0[2]) | (bf16_rne(v0[3]) << 16),
+                                                                     bf16_rne(v1[2]) | (bf16_rne(v1[3]) << 16),
+                                                                     false, false);
+                    uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + out_off + m * p.ld_out + np;
+                    const uint32_t w[4] = {(uint32_t)lo[0], (uint32_t)hi[0], (uint32_t)lo[1], (uint32_t)hi[1]};
+                    if (live && fullp) {
+                        *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
+                    } else if (live) {
+#pragma unroll
+                        for (int r = 0; r < 8; ++r)
+                            if (np + r < p.N) o[r] = (uint16_t)(w[r >> 1] >> (16 * (r & 1)));
+                    }
+                } else {
+                    // fp32: the accumulator layout already gives 16-byte runs
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const float* v = h ? v1 : v0;
+                        const int64_t n = n0 + wn * kWN + (j0 + h) * 16 + q4 * 4;
+                        if (m >= p.M || n >= p.N) continue;
+                        float* o = reinterpret_cast<float*>(p.out) + out_off + m * p.ld_out + n;
+                        if (n + 3 < p.N) {
+                            *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) if (n + r < p.N) o[r] = v[r];
+                        }
+                    }
+                }
+            }
+        }
+        if (has_bgrad) {
+            // column sums: reduce over the 16 lanes that share q4 (different m), one atomic per column
+#pragma unroll
+            for (int j = 0; j < kTN; ++j) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float t = colsum[j][r];
+                    t += __shfl_xor(t, 1);
+                    t += __shfl_xor(t, 2);
+                    t += __shfl_xor(t, 4);
+                    t += __shfl_xor(t, 8);
+                    colsum[j][r] = t;
+                }
+                const int64_t n = n0 + wn * kWN + j * 16 + q4 * 4;
+                if (r16 == 0) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < p.N) unsafeAtomicAdd(p.bias_grad + n + r, colsum[j][r]);
+                }
+            }
+        }
+        return;
     }
+
+    // forward: pair column groups so that each lane owns eight consecutive columns
     const bool has_bias = (p.flags & TE_EPI_BIAS) != 0;
     const bool has_gelu = (p.flags & TE_EPI_GELU) != 0;
     const bool has_aux = (p.flags & TE_EPI_AUX_PREACT) != 0;
-    const bool has_dgelu = (p.flags & TE_EPI_DGELU) != 0;
-    const bool has_bgrad = (p.flags & TE_EPI_BGRAD) != 0;
-
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) {
-        const int64_t n = n0 + wn * kWN + j * 16 + q4 * 4;
-        const bool full4 = n + 3 < p.N;
-        float bias[4] = {0.f, 0.f, 0.f, 0.f};
-        if (kEpi == (int)Epi::Fwd && has_bias) {
-            if (full4) {
-                const uint2 bv = *reinterpret_cast<const uint2*>(p.bias + n);
-                bias[0] = bf16_to_f32(bv.x & 0xFFFF); bias[1] = bf16_to_f32(bv.x >> 16);
-                bias[2] = bf16_to_f32(bv.y & 0xFFFF); bias[3] = bf16_to_f32(bv.y >> 16);
+    for (int jp = 0; jp < kTN / 2; ++jp) {
+        const int64_t n = n0 + wn * kWN + (2 * jp + (q4 & 1)) * 16 + (q4 >> 1) * 8;
+        const bool full8 = n + 7 < p.N;
+        float bias[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (has_bias) {
+            if (full8) {
+                unpack_bf16x8(*reinterpret_cast<const uint4*>(p.bias + n), bias);
             } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) if (n + r < p.N) bias[r] = bf16_to_f32(p.bias[n + r]);
+                for (int r = 0; r < 8; ++r) if (n + r < p.N) bias[r] = bf16_to_f32(p.bias[n + r]);
             }
         }
 #pragma unroll
         for (int i = 0; i < kTM; ++i) {
+            // (every lane takes part in the swap, before any lane drops out;
+            // __float_as_uint, not __builtin_bit_cast, which reads element 0
+            // when handed an element of a vector register)
+            float v[8];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[i][2 * jp][c]),
+                                                                 __float_as_uint(acc[i][2 * jp + 1][c]), false, false);
+                v[c] = __uint_as_float(sw[0]);
+                v[4 + c] = __uint_as_float(sw[1]);
+            }
             const int64_t m = m0 + wm * kWM + i * 16 + r16;
             if (m >= p.M || n >= p.N) continue;
-            float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-            if (kEpi == (int)Epi::Wgrad) {
-                float* o = reinterpret_cast<float*>(p.out) + out_off + m * p.ld_out + n;
-                if (full4) {
-                    float4 cur = *reinterpret_cast<float4*>(o);
-                    cur.x += v[0]; cur.y += v[1]; cur.z += v[2]; cur.w += v[3];
-                    *reinterpret_cast<float4*>(o) = cur;
-                } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) if (n + r < p.N) o[r] += v[r];
-                }
-                continue;
+            for (int r = 0; r < 8; ++r) v[r] += bias[r];
+            if (has_aux) store_bf16x8(p.aux + m * p.ld_aux + n, v, full8, p.N - n);
+            if (has_gelu) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) v[r] = gelu(v[r]);
             }
-            if (kEpi == (int)Epi::Fwd) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] += bias[r];
-                if (has_aux) {
-                    uint16_t* a = p.aux + m * p.ld_aux + n;
-                    if (full4) {
-                        *reinterpret_cast<uint2*>(a) = make_uint2(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16),
-                                                                  bf16_rne(v[2]) | (bf16_rne(v[3]) << 16));
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) if (n + r < p.N) a[r] = (uint16_t)bf16_rne(v[r]);
-                    }
-                }
-                if (has_gelu) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) v[r] = gelu(v[r]);
-                }
-            } else {  // Dgrad
-                if (has_dgelu) {
-                    const uint16_t* z = p.preact + m * p.ld_aux + n;
-                    float zf[4];
-                    if (full4) {
-                        const uint2 zv = *reinterpret_cast<const uint2*>(z);
-                        zf[0] = bf16_to_f32(zv.x & 0xFFFF); zf[1] = bf16_to_f32(zv.x >> 16);
-                        zf[2] = bf16_to_f32(zv.y & 0xFFFF); zf[3] = bf16_to_f32(zv.y >> 16);
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) zf[r] = n + r < p.N ? bf16_to_f32(z[r]) : 0.f;
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) v[r] *= dgelu(zf[r]);
-                }
-                if (has_bgrad) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) colsum[j][r] += v[r];
-                }
-            }
-            // store y / dx
             if (p.out_bf16) {
-                uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + out_off + m * p.ld_out + n;
-                if (full4) {
-                    *reinterpret_cast<uint2*>(o) = make_uint2(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16),
-                                                              bf16_rne(v[2]) | (bf16_rne(v[3]) << 16));
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) if (n + r < p.N) o[r] = (uint16_t)bf16_rne(v[r]);
-                }
+                store_bf16x8(reinterpret_cast<uint16_t*>(p.out) + out_off + m * p.ld_out + n, v, full8, p.N - n);
             } else {
                 float* o = reinterpret_cast<float*>(p.out) + out_off + m * p.ld_out + n;
-                if (full4) {
-                    *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+                if (full8) {
+                    reinterpret_cast<float4*>(o)[0] = make_float4(v[0], v[1], v[2], v[3]);
+                    reinterpret_cast<float4*>(o)[1] = make_float4(v[4], v[5], v[6], v[7]);
                 } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) if (n + r < p.N) o[r] = v[r];
+                    for (int r = 0; r < 8; ++r) if (n + r < p.N) o[r] = v[r];
                 }
-            }
-        }
-    }
-
-    if (kEpi == (int)Epi::Dgrad && has_bgrad) {
-        // column sums: reduce over the 16 lanes that share q4 (different m), one atomic per column
-#pragma unroll
-        for (int j = 0; j < kTN; ++j) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float s = colsum[j][r];
-                s += __shfl_xor(s, 1);
-                s += __shfl_xor(s, 2);
-                s += __shfl_xor(s, 4);
-                s += __shfl_xor(s, 8);
-                colsum[j][r] = s;
-            }
-            const int64_t n = n0 + wn * kWN + j * 16 + q4 * 4;
-            if (r16 == 0) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (n + r < p.N) unsafeAtomicAdd(p.bias_grad + n + r, colsum[j][r]);
             }
         }
     }
