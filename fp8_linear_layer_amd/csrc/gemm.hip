@@ -691,31 +691,46 @@ __device__ __forceinline__ TileCtx tile_ctx(const GemmArgs& p, int64_t tile)
     return c;
 }
 
-// This thread's share of the FAST test: are the scales of one tile row (A) or
-// column (B) over the tile's contraction range all powers of two?  Thread r
-// takes row r of the 256 A rows and 256 B rows (consecutive threads read
-// consecutive scales of a block); the loads are batched so they are in flight
-// together.
+// This thread's share of the FAST test: are the scales of the tile's rows (A)
+// and columns (B) over its contraction range all powers of two?  Per block the
+// tile has 2 x 64 runs of four consecutive scales (16-byte aligned: tile
+// corners are multiples of 256, the leading dimension a multiple of 4); thread
+// t takes runs t, t + 512, ... eight at a time, so its loads are in flight
+// together.  Scales past the last row or column (the padding up to the leading
+// dimension) are ignored.
 __device__ __forceinline__ bool row_scales_pow2(const GemmArgs& p, const TileCtx& c)
 {
-    const int r = threadIdx.x;
-    const int64_t ld = r < kBM ? p.lsa : p.lsb;
-    const float* s = r < kBM ? p.sa + min(c.m0 + r, p.M - 1) : p.sb + min(c.n0 + (r - kBM), p.N - 1);
-    s += (int64_t)c.kb0 * ld;
+    const int t = threadIdx.x;
+    const int runs = c.nkb * 2 * (kBM / 4);
     bool ok = true;
-    for (int kb = 0; kb < c.nkb; kb += 16) {
-        float v[16];
+    for (int f0 = 0; f0 < runs; f0 += kThreads * 8) {
+        float4 v[8];
+        int64_t left[8];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = kb + u < c.nkb ? s[(int64_t)(kb + u) * ld] : 1.f;
+        for (int u = 0; u < 8; ++u) {
+            const int f = f0 + u * kThreads + t;
+            const int kb = c.kb0 + (f >> 7), w = f & 127;
+            const bool is_a = w < kBM / 4;
+            const int64_t r = (int64_t)(w & (kBM / 4 - 1)) * 4;
+            left[u] = f < runs ? (is_a ? p.M - c.m0 : p.N - c.n0) - r : 0;
+            v[u] = make_float4(1.f, 1.f, 1.f, 1.f);
+            if (left[u] > 0)
+                v[u] = *reinterpret_cast<const float4*>(is_a ? p.sa + (int64_t)kb * p.lsa + c.m0 + r
+                                                             : p.sb + (int64_t)kb * p.lsb + c.n0 + r);
+        }
 #pragma unroll
-        for (int u = 0; u < 16; ++u) ok = ok && is_pow2_scale(v[u]);
+        for (int u = 0; u < 8; ++u) {
+            ok = ok && is_pow2_scale(v[u].x) && (left[u] < 2 || is_pow2_scale(v[u].y)) &&
+                 (left[u] < 3 || is_pow2_scale(v[u].z)) && (left[u] < 4 || is_pow2_scale(v[u].w));
+        }
     }
     return ok;
 }
 
 // Persistent kernel: workgroup w takes tiles w, w + G, w + 2G, ... (G = grid
 // size).  While a tile's epilogue runs, the first stage of the workgroup's
-// next tile is already being copied in.
+// next tile is already being copied in; the next tile's FAST test follows the
+// epilogue.
 template <int kFmtA, int kFmtB, bool kFast, int kEpi>
 __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p, int64_t total_tiles)
 {
@@ -770,10 +785,11 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p, int
         if (more) {
             cn = tile_ctx(p, next);
             load_stage(p, cn.src, smem + s0_off, cn.kb0, wave, lane);
-            if (kFast) ok = row_scales_pow2(p, cn);
         }
         epilogue<kEpi>(p, acc, c.m0, c.n0, c.out_off, wave, lane);
         if (!more) break;
+        // (after the epilogue: the scale reads overlap its stores)
+        if (kFast) ok = row_scales_pow2(p, cn);
         tile = next;
         c = cn;
     }
