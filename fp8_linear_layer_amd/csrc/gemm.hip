@@ -462,7 +462,7 @@ __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&v)[8],
 // holds eight consecutive columns of its row (group j + (q4 & 1), columns
 // 8 (q4 >> 1) .. +7).  Each bf16 load and store is then a 16-byte run, and
 // four lanes cover 64 contiguous bytes of a row.
-template <int kEpi>
+template <int kEpi, bool kFull>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM][kTN], int64_t m0, int64_t n0,
                                          int64_t out_off, int wave, int lane)
 {
@@ -472,15 +472,44 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
     asm volatile("" : "+v"(lane));
     const int r16 = lane & 15, q4 = lane >> 4;
 
+    // A tile inside the matrix: no bounds checks, and every load is issued
+    // before the first store.  Stores count in the same vmcnt as loads, so a
+    // load issued after a store cannot be waited for without also waiting for
+    // that store to complete.
+    if (kFull && kEpi == (int)Epi::Wgrad) {
+        // Two halves of the column groups, each read in one batch, added and
+        // written: two waits for the whole tile instead of one per fragment.
+        float* o = reinterpret_cast<float*>(p.out) + out_off + (m0 + wm * kWM + r16) * p.ld_out + n0 + wn * kWN + q4 * 4;
+        constexpr int kH = kTN / 2;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float4 c[kTM][kH];
+#pragma unroll
+            for (int jj = 0; jj < kH; ++jj)
+#pragma unroll
+                for (int i = 0; i < kTM; ++i)
+                    c[i][jj] = *reinterpret_cast<const float4*>(o + i * 16 * p.ld_out + (h * kH + jj) * 16);
+#pragma unroll
+            for (int jj = 0; jj < kH; ++jj)
+#pragma unroll
+                for (int i = 0; i < kTM; ++i) {
+                    const v4f& a = acc[i][h * kH + jj];
+                    c[i][jj].x += a[0]; c[i][jj].y += a[1]; c[i][jj].z += a[2]; c[i][jj].w += a[3];
+                    *reinterpret_cast<float4*>(o + i * 16 * p.ld_out + (h * kH + jj) * 16) = c[i][jj];
+                }
+        }
+        return;
+    }
+
     if (kEpi == (int)Epi::Wgrad) {
 #pragma unroll
         for (int j = 0; j < kTN; ++j) {
             const int64_t n = n0 + wn * kWN + j * 16 + q4 * 4;
-            const bool full4 = n + 3 < p.N;
+            const bool full4 = kFull || n + 3 < p.N;
 #pragma unroll
             for (int i = 0; i < kTM; ++i) {
                 const int64_t m = m0 + wm * kWM + i * 16 + r16;
-                if (m >= p.M || n >= p.N) continue;
+                if (!kFull && (m >= p.M || n >= p.N)) continue;
                 float* o = reinterpret_cast<float*>(p.out) + out_off + m * p.ld_out + n;
                 if (full4) {
                     float4 cur = *reinterpret_cast<float4*>(o);
@@ -508,21 +537,33 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
         float colsum[kTN][4];
 #pragma unroll
         for (int j = 0; j < kTN; ++j) colsum[j][0] = colsum[j][1] = colsum[j][2] = colsum[j][3] = 0.f;
+        uint4 zq[kTN / 2][kTM];
+        if (kFull && has_dgelu) {
+#pragma unroll
+            for (int jp = 0; jp < kTN / 2; ++jp)
+#pragma unroll
+                for (int i = 0; i < kTM; ++i)
+                    zq[jp][i] = *reinterpret_cast<const uint4*>(
+                        p.preact + (m0 + wm * kWM + i * 16 + r16) * p.ld_aux + n0 + wn * kWN + (2 * jp + (q4 & 1)) * 16 +
+                        (q4 >> 1) * 8);
+        }
 #pragma unroll
         for (int jp = 0; jp < kTN / 2; ++jp) {
             const int j0 = 2 * jp, j1 = 2 * jp + 1;
             const int64_t np = n0 + wn * kWN + (j0 + (q4 & 1)) * 16 + (q4 >> 1) * 8;  // this lane's run
-            const bool fullp = np + 7 < p.N;
+            const bool fullp = kFull || np + 7 < p.N;
 #pragma unroll
             for (int i = 0; i < kTM; ++i) {
                 const int64_t m = m0 + wm * kWM + i * 16 + r16;
-                const bool live = m < p.M && np < p.N;
+                const bool live = kFull || (m < p.M && np < p.N);
                 float v0[4] = {acc[i][j0][0], acc[i][j0][1], acc[i][j0][2], acc[i][j0][3]};
                 float v1[4] = {acc[i][j1][0], acc[i][j1][1], acc[i][j1][2], acc[i][j1][3]};
                 if (has_dgelu) {
                     uint32_t zw[4] = {0u, 0u, 0u, 0u};
                     const uint16_t* z = p.preact + m * p.ld_aux + np;
-                    if (live && fullp) {
+                    if (kFull) {
+                        zw[0] = zq[jp][i].x; zw[1] = zq[jp][i].y; zw[2] = zq[jp][i].z; zw[3] = zq[jp][i].w;
+                    } else if (live && fullp) {
                         const uint4 t = *reinterpret_cast<const uint4*>(z);
                         zw[0] = t.x; zw[1] = t.y; zw[2] = t.z; zw[3] = t.w;
                     } else if (live) {
@@ -567,9 +608,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
                     for (int h = 0; h < 2; ++h) {
                         const float* v = h ? v1 : v0;
                         const int64_t n = n0 + wn * kWN + (j0 + h) * 16 + q4 * 4;
-                        if (m >= p.M || n >= p.N) continue;
+                        if (!kFull && (m >= p.M || n >= p.N)) continue;
                         float* o = reinterpret_cast<float*>(p.out) + out_off + m * p.ld_out + n;
-                        if (n + 3 < p.N) {
+                        if (kFull || n + 3 < p.N) {
                             *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
                         } else {
 #pragma unroll
@@ -596,7 +637,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
                 if (r16 == 0) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (n + r < p.N) unsafeAtomicAdd(p.bias_grad + n + r, colsum[j][r]);
+                        if (kFull || n + r < p.N) unsafeAtomicAdd(p.bias_grad + n + r, colsum[j][r]);
                 }
             }
         }
@@ -607,13 +648,21 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
     const bool has_bias = (p.flags & TE_EPI_BIAS) != 0;
     const bool has_gelu = (p.flags & TE_EPI_GELU) != 0;
     const bool has_aux = (p.flags & TE_EPI_AUX_PREACT) != 0;
+    uint4 bw[kTN / 2];
+    if (kFull && has_bias) {
+#pragma unroll
+        for (int jp = 0; jp < kTN / 2; ++jp)
+            bw[jp] = *reinterpret_cast<const uint4*>(p.bias + n0 + wn * kWN + (2 * jp + (q4 & 1)) * 16 + (q4 >> 1) * 8);
+    }
 #pragma unroll
     for (int jp = 0; jp < kTN / 2; ++jp) {
         const int64_t n = n0 + wn * kWN + (2 * jp + (q4 & 1)) * 16 + (q4 >> 1) * 8;
-        const bool full8 = n + 7 < p.N;
+        const bool full8 = kFull || n + 7 < p.N;
         float bias[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         if (has_bias) {
-            if (full8) {
+            if (kFull) {
+                unpack_bf16x8(bw[jp], bias);
+            } else if (full8) {
                 unpack_bf16x8(*reinterpret_cast<const uint4*>(p.bias + n), bias);
             } else {
 #pragma unroll
@@ -634,7 +683,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
                 v[4 + c] = __uint_as_float(sw[1]);
             }
             const int64_t m = m0 + wm * kWM + i * 16 + r16;
-            if (m >= p.M || n >= p.N) continue;
+            if (!kFull && (m >= p.M || n >= p.N)) continue;
 #pragma unroll
             for (int r = 0; r < 8; ++r) v[r] += bias[r];
             if (has_aux) store_bf16x8(p.aux + m * p.ld_aux + n, v, full8, p.N - n);
@@ -786,7 +835,12 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p, int
             cn = tile_ctx(p, next);
             load_stage(p, cn.src, smem + s0_off, cn.kb0, wave, lane);
         }
-        epilogue<kEpi>(p, acc, c.m0, c.n0, c.out_off, wave, lane);
+        // (a tile inside the matrix takes the copy of the epilogue without
+        // bounds checks: straight-line code lets its loads be in flight together)
+        if (c.m0 + kBM <= p.M && c.n0 + kBN <= p.N)
+            epilogue<kEpi, true>(p, acc, c.m0, c.n0, c.out_off, wave, lane);
+        else
+            epilogue<kEpi, false>(p, acc, c.m0, c.n0, c.out_off, wave, lane);
         if (!more) break;
         // (after the epilogue: the scale reads overlap its stores)
         if (kFast) ok = row_scales_pow2(p, cn);
