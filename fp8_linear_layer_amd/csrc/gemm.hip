@@ -214,12 +214,15 @@ __device__ __forceinline__ bool is_pow2_scale(float s)
     return (u & 0x007FFFFFu) == 0 && e != 0 && e < 255;  // positive normal power of two
 }
 
-__device__ __forceinline__ uint32_t bf16_rne(float f)
+// fp32 -> bf16, round to nearest even, by gfx950's v_cvt_pk_bf16_f32 (one
+// instruction per pair; the integer rounding sequence costs several per value).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
+__device__ __forceinline__ uint16_t bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __builtin_bit_cast(float, h << 16); }
 
@@ -444,13 +447,11 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4 w, float (&f)[8])
 __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&v)[8], bool full, int64_t left)
 {
     if (full) {
-        *reinterpret_cast<uint4*>(dst) = make_uint4(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16),
-                                                    bf16_rne(v[2]) | (bf16_rne(v[3]) << 16),
-                                                    bf16_rne(v[4]) | (bf16_rne(v[5]) << 16),
-                                                    bf16_rne(v[6]) | (bf16_rne(v[7]) << 16));
+        *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                    pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
     } else {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) if (r < left) dst[r] = (uint16_t)bf16_rne(v[r]);
+        for (int r = 0; r < 8; ++r) if (r < left) dst[r] = bf16_rne(v[r]);
     }
 }
 
@@ -587,11 +588,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
                     }
                 }
                 if (p.out_bf16) {
-                    const auto lo = __builtin_amdgcn_permlane16_swap(bf16_rne(v0[0]) | (bf16_rne(v0[1]) << 16),
-                                                                     bf16_rne(v1[0]) | (bf16_rne(v1[1]) << 16),
+                    const auto lo = __builtin_amdgcn_permlane16_swap(pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v1[0], v1[1]),
                                                                      false, false);
-                    const auto hi = __builtin_amdgcn_permlane16_swap(bf16_rne(v0[2]) | (bf16_rne(v0[3]) << 16),
-                                                                     bf16_rne(v1[2]) | (bf16_rne(v1[3]) << 16),
+                    const auto hi = __builtin_amdgcn_permlane16_swap(pack_bf16x2(v0[2], v0[3]), pack_bf16x2(v1[2], v1[3]),
                                                                      false, false);
                     uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + out_off + m * p.ld_out + np;
                     const uint32_t w[4] = {(uint32_t)lo[0], (uint32_t)hi[0], (uint32_t)lo[1], (uint32_t)hi[1]};
