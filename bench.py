@@ -70,18 +70,24 @@ def traffic_from_profile(kernel_key: str):
     return None if entry is None else entry.get("hbm_bytes_per_launch")
 
 
-def timed(fn, reps, warm=3):
+def timed(fn, reps, warm=3, rounds=3):
+    """Kernel time of fn (one launch): `reps` back-to-back launches between one
+    event pair on the launch stream, divided by reps (an event pair around a
+    single launch would also count the dispatch gap in front of it).  Median
+    and minimum over `rounds` such runs."""
     import torch
     for _ in range(warm):
         fn()
-    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
     times = []
-    for _ in range(reps):
-        st.record()
-        fn()
-        en.record()
+    for _ in range(rounds):
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.record(stream)
+        for _ in range(reps):
+            fn()
+        en.record(stream)
         en.synchronize()
-        times.append(st.elapsed_time(en))
+        times.append(st.elapsed_time(en) / reps)
     return float(np.median(times)), float(np.min(times))
 
 
@@ -221,7 +227,7 @@ def main():
     sb = torch.empty((K // 128, te.scale_ld(N)), dtype=torch.float32, device="cuda")
     E4 = te.TE_DTYPE_E4M3
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
 
     def step(i=None):
         te.te_cast_fp8_per_token(a, E4, q=qa, scales=sa)
@@ -231,6 +237,10 @@ def main():
         te.te_fp8_wgrad_accum(qa, sa, E4, qb, sb, E4, out, te.TE_ACCUM_FULL_FP32)
         if i is not None:
             ev[i][1].record(stream)
+
+    def cast_only():
+        te.te_cast_fp8_per_token(a, E4, q=qa, scales=sa)
+        te.te_cast_fp8_per_token(b, E4, q=qb, scales=sb)
 
     if args.ref_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -243,12 +253,18 @@ def main():
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     total = time.perf_counter() - t0
     ms_step = total * 1e3 / args.steps
+    # (after the timed region) the GEMM's time inside a step, event pair
+    # around its launch: includes the dispatch gap in front of it
+    for i in range(len(ev)):
+        step(i)
+    torch.cuda.synchronize()
     in_step_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    cast_ms, _ = timed(cast_only, args.kernel_reps)
     # The kernel's own duration: back-to-back launches between one event pair
     # on the launch stream (an event pair around a single launch also counts
     # the dispatch gap in front of it).
@@ -282,7 +298,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": traffic,
                      "kernel": "gemm_nt_kernel (wgrad, full)", "kernel_ms": round(gemm_ms, 5),
-                     "kernel_ms_in_step": round(in_step_ms, 5)},
+                     "kernel_ms_in_step": round(in_step_ms, 5),
+                     "casts_ms": round(cast_ms, 5)},
     }
     if not args.no_breakdown:
         rec["breakdown"] = breakdown(te, torch)
