@@ -478,27 +478,46 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
     // load issued after a store cannot be waited for without also waiting for
     // that store to complete.
     if (kFull && kEpi == (int)Epi::Wgrad) {
-        // Two halves of the column groups, each read in one batch, added and
-        // written: two waits for the whole tile instead of one per fragment.
+        // Four quarters of the column groups, each read in one batch and
+        // added.  A quarter's loads are issued before the previous quarter's
+        // stores: the load/store counter retires in issue order, so waiting
+        // for those loads does not wait for the stores behind them.
         float* o = reinterpret_cast<float*>(p.out) + out_off + (m0 + wm * kWM + r16) * p.ld_out + n0 + wn * kWN + q4 * 4;
-        constexpr int kH = kTN / 2;
+        constexpr int kQ = kTN / 4;
+        float4 c[2][kTM][kQ];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            float4 c[kTM][kH];
+        for (int h = 0; h < 4; ++h) {
 #pragma unroll
-            for (int jj = 0; jj < kH; ++jj)
+            for (int jj = 0; jj < kQ; ++jj)
 #pragma unroll
                 for (int i = 0; i < kTM; ++i)
-                    c[i][jj] = *reinterpret_cast<const float4*>(o + i * 16 * p.ld_out + (h * kH + jj) * 16);
+                    c[h & 1][i][jj] = *reinterpret_cast<const float4*>(o + i * 16 * p.ld_out + (h * kQ + jj) * 16);
+            if (h > 0) {
+                // (fences for the scheduler: each quarter's loads stay after
+                // the previous quarter's sums, so at most two quarters of the
+                // output are held in registers besides the accumulators)
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int jj = 0; jj < kH; ++jj)
+                for (int jj = 0; jj < kQ; ++jj)
+#pragma unroll
+                    for (int i = 0; i < kTM; ++i)
+                        *reinterpret_cast<float4*>(o + i * 16 * p.ld_out + ((h - 1) * kQ + jj) * 16) = c[(h - 1) & 1][i][jj];
+            }
+#pragma unroll
+            for (int jj = 0; jj < kQ; ++jj)
 #pragma unroll
                 for (int i = 0; i < kTM; ++i) {
-                    const v4f& a = acc[i][h * kH + jj];
-                    c[i][jj].x += a[0]; c[i][jj].y += a[1]; c[i][jj].z += a[2]; c[i][jj].w += a[3];
-                    *reinterpret_cast<float4*>(o + i * 16 * p.ld_out + (h * kH + jj) * 16) = c[i][jj];
+                    const v4f& a = acc[i][h * kQ + jj];
+                    float4& d = c[h & 1][i][jj];
+                    d.x += a[0]; d.y += a[1]; d.z += a[2]; d.w += a[3];
                 }
+            __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int jj = 0; jj < kQ; ++jj)
+#pragma unroll
+            for (int i = 0; i < kTM; ++i)
+                *reinterpret_cast<float4*>(o + i * 16 * p.ld_out + (3 * kQ + jj) * 16) = c[1][i][jj];
         return;
     }
 
