@@ -129,7 +129,16 @@ def breakdown(te, torch):
         out[name] = {"shape": [M, N, K], "ms": round(med, 4), "tflops": round(flop / med / 1e9, 1)}
     cast_bytes = M * K * 2 + M * K + M * (K // 128) * 4
     med, _ = timed(lambda: te.te_cast_fp8_per_token(x, E4, q=qx, scales=sx), 10)
-    out["cast_e4m3_8192x4096"] = {"ms": round(med, 4), "gbs": round(cast_bytes / med / 1e6, 1)}
+    out["cast_e4m3_8192x4096"] = {"ms": round(med, 4), "gbs": round(cast_bytes / med / 1e6, 1),
+                                  "frac_hbm": round(cast_bytes / med / 1e6 / HBM_PEAK_GBS, 3)}
+    # fused cast + cast-transpose of the same activation (fprop operand and wgrad operand from one read)
+    ct_bytes = M * K * 2 + 2 * M * K + 2 * M * (K // 128) * 4
+    qxt, sxt = torch.empty((K, M), dtype=torch.uint8, device=dev), torch.empty((M // 128, te.scale_ld(K)),
+                                                                                dtype=torch.float32, device=dev)
+    med, _ = timed(lambda: te.te_cast_fp8_per_token_transpose(x, E4, q=qx, scales=sx, qt=qxt, scales_t=sxt), 10)
+    out["cast_and_transpose_e4m3_8192x4096"] = {"ms": round(med, 4), "gbs": round(ct_bytes / med / 1e6, 1),
+                                                "frac_hbm": round(ct_bytes / med / 1e6 / HBM_PEAK_GBS, 3)}
+    del qxt, sxt
     del x, w, qw, sw, px, psx, pw, psw, y
 
     # dgrad: dX [8192 x 4096] = dY [8192 x 14336] (e5m2) W^T (e4m3)

@@ -35,7 +35,7 @@ TE_EPI_BGRAD = 16
 # cast flags
 TE_CAST_POW2_SCALE = 1
 
-EXPORTED = ("te_cast_fp8_per_token", "te_fp8_gemm_fwd", "te_fp8_gemm_dgrad", "te_fp8_wgrad_accum",
+EXPORTED = ("te_cast_fp8_per_token", "te_cast_fp8_per_token_transpose", "te_fp8_gemm_fwd", "te_fp8_gemm_dgrad", "te_fp8_wgrad_accum",
             "te_fp8_kgrouped_wgrad", "te_status_string", "te_last_error_message", "te_scale_ld")
 
 
@@ -65,6 +65,8 @@ def load_library():
     lib.te_scale_ld.argtypes = [I64]
     lib.te_cast_fp8_per_token.restype = I
     lib.te_cast_fp8_per_token.argtypes = [P, I64, I64, I64, I, U32, P, I64, P, P]
+    lib.te_cast_fp8_per_token_transpose.restype = I
+    lib.te_cast_fp8_per_token_transpose.argtypes = [P, I64, I64, I64, I, U32, P, I64, P, P, I64, P, P]
     lib.te_fp8_gemm_fwd.restype = I
     lib.te_fp8_gemm_fwd.argtypes = [P, P, I, P, P, I, I64, I64, I64, P, U32, P, I, I64, P, I64, I, P]
     lib.te_fp8_gemm_dgrad.restype = I
@@ -125,6 +127,32 @@ def te_cast_fp8_per_token(x, out_dtype=TE_DTYPE_E4M3, flags=0, q=None, scales=No
     _check(load_library().te_cast_fp8_per_token(_ptr(x), rows, cols, x.stride(0), out_dtype, flags,
                                                 _ptr(q), q.stride(0), _ptr(scales), _stream(stream)))
     return q, scales
+
+
+def te_cast_fp8_per_token_transpose(x, out_dtype=TE_DTYPE_E4M3, flags=0, rowwise=True, q=None, scales=None,
+                                    qt=None, scales_t=None, stream=None):
+    """bf16 x [rows, cols] -> (q, scales, qt, scales_t): the per-token cast of x (None, None when
+    rowwise is False) and of x^T, from one read of x.  qt is uint8 [cols, rows]; scales_t is
+    block-major fp32 [rows/128, scale_ld(cols)]."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    rows, cols = x.shape
+    if rowwise:
+        if q is None:
+            q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+        if scales is None:
+            scales = torch.empty((cols // 128, scale_ld(rows)), dtype=torch.float32, device=x.device)
+        _scales_ok(scales, rows, cols, "scales")
+    else:
+        q = scales = None
+    if qt is None:
+        qt = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    if scales_t is None:
+        scales_t = torch.empty((rows // 128, scale_ld(cols)), dtype=torch.float32, device=x.device)
+    _scales_ok(scales_t, cols, rows, "scales_t")
+    _check(load_library().te_cast_fp8_per_token_transpose(
+        _ptr(x), rows, cols, x.stride(0), out_dtype, flags, _ptr(q), q.stride(0) if q is not None else 0,
+        _ptr(scales), _ptr(qt), qt.stride(0), _ptr(scales_t), _stream(stream)))
+    return q, scales, qt, scales_t
 
 
 def te_fp8_gemm_fwd(x, x_scales, x_dtype, w, w_scales, w_dtype, bias=None, epilogue=TE_EPI_NONE,

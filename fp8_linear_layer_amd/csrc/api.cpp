@@ -185,6 +185,48 @@ te_status_t te_cast_fp8_per_token(const void* x_bf16, int64_t rows, int64_t cols
     }
 }
 
+te_status_t te_cast_fp8_per_token_transpose(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                            te_dtype_t out_dtype, uint32_t flags, void* q, int64_t ld_q,
+                                            float* scales, void* qt, int64_t ld_qt, float* scales_t,
+                                            hipStream_t stream)
+{
+    try {
+        const char* fn = "te_cast_fp8_per_token_transpose";
+        if (!x_bf16 || !qt || !scales_t) return fail(TE_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
+        if ((q == nullptr) != (scales == nullptr))
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: q and scales must both be given or both be null", fn);
+        if (rows < 128 || rows % 128 != 0 || rows >= kMaxDim)
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: rows must be a positive multiple of 128 (got %lld)", fn, (long long)rows);
+        if (q && (cols < 128 || cols % 128 != 0 || cols >= kMaxDim))
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: with the row-wise cast, cols must be a positive multiple of 128 (got %lld)",
+                        fn, (long long)cols);
+        if (!q && (cols < 8 || cols % 8 != 0 || cols >= kMaxDim))
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: cols must be a positive multiple of 8 (got %lld)", fn, (long long)cols);
+        if (ld_x < cols || (q && ld_q < cols) || ld_qt < rows)
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: ld_x and ld_q must be >= cols, ld_qt >= rows", fn);
+        if (!is_fp8(out_dtype)) return fail(TE_ERR_INVALID_ARGUMENT, "%s: out_dtype must be TE_DTYPE_E4M3 or TE_DTYPE_E5M2 (got %d)", fn, (int)out_dtype);
+        if (flags & ~(uint32_t)TE_CAST_POW2_SCALE) return fail(TE_ERR_INVALID_ARGUMENT, "%s: unknown flag bits 0x%x", fn, flags);
+        if (!aligned(x_bf16, 16) || ld_x % 8 != 0) return fail(TE_ERR_MISALIGNED, "%s: x must be 16-byte aligned with ld_x a multiple of 8", fn);
+        if (q && (!aligned(q, 16) || ld_q % 16 != 0)) return fail(TE_ERR_MISALIGNED, "%s: q must be 16-byte aligned with ld_q a multiple of 16", fn);
+        if (!aligned(qt, 16) || ld_qt % 16 != 0) return fail(TE_ERR_MISALIGNED, "%s: qt must be 16-byte aligned with ld_qt a multiple of 16", fn);
+        if ((scales && !aligned(scales, 16)) || !aligned(scales_t, 16))
+            return fail(TE_ERR_MISALIGNED, "%s: scales and scales_t must be 16-byte aligned", fn);
+        tefp8::LaunchInfo info{};
+        hipError_t e = tefp8::launch_cast_transpose(
+            static_cast<const uint16_t*>(x_bf16), rows, cols, ld_x, to_fmt(out_dtype), (flags & TE_CAST_POW2_SCALE) != 0,
+            static_cast<uint8_t*>(q), ld_q, scales, te_scale_ld(rows), static_cast<uint8_t*>(qt), ld_qt, scales_t,
+            te_scale_ld(cols), stream, &info);
+        if (log_enabled())
+            std::fprintf(stderr, "[te_fp8] %s rows=%lld cols=%lld out=%s pow2=%d rowwise=%d threads=%d grid=%lld\n", fn,
+                         (long long)rows, (long long)cols, dtype_name(out_dtype), (flags & TE_CAST_POW2_SCALE) ? 1 : 0,
+                         q ? 1 : 0, info.threads, (long long)info.grid);
+        if (e != hipSuccess) return fail(TE_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+        return ok();
+    } catch (...) {
+        return fail(TE_ERR_INTERNAL, "te_cast_fp8_per_token_transpose: internal error");
+    }
+}
+
 te_status_t te_fp8_gemm_fwd(const void* x, const float* x_scales, te_dtype_t x_dtype,
                             const void* w, const float* w_scales, te_dtype_t w_dtype,
                             int64_t M, int64_t N, int64_t K,

@@ -21,8 +21,19 @@
 // The group max is a 3-step DPP butterfly inside the 8 lanes.  The fp32 -> fp8
 // rounding is the hardware v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 on inputs
 // clamped to +-FP8_MAX (round to nearest even; the clamp gives saturation).
+//
+// The fused cast-transpose reads each 128 x 128 bf16 tile once (persistent
+// workgroups, the next tile's loads in flight during the current one).  The row-wise
+// cast works from the loaded registers (16 lanes per row, 8 elements each,
+// a 4-step DPP max over the 16 lanes); the tile also goes to LDS, from which
+// 8 lanes per column read 16 consecutive rows each for the cast of the
+// transpose.  Chunk c (16 bytes) of LDS row r sits at slot c ^ ((r >> 4) & 15),
+// so the 2-byte column reads of a wave (8 columns x 8 row segments 16 rows
+// apart) fall in distinct banks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "internal.h"
 
@@ -159,6 +170,129 @@ __global__ __launch_bounds__(kThreads) void cast_per_token_kernel(
     }
 }
 
+// ------------------------------------------------------------ cast-transpose
+constexpr int kCT = 128;              // tile side (one group in each direction)
+constexpr int kRowMirror = 0x140;      // lane i <-> 15-i within each 16-lane row
+
+// Load one 128 x 128 tile: 2048 chunks of 8 bf16, chunk u * 256 + t is row
+// 16 u + (t >> 4), chunk t & 15 of that row.  Columns past `cols` (only in the
+// last tile column, without the row-wise cast) read as zero.
+__device__ __forceinline__ void load_tile(u32x4 (&v)[8], const uint16_t* __restrict__ x, int64_t cols,
+                                          int64_t tiles_c, int64_t ld_x, int64_t tile)
+{
+    const int t = threadIdx.x, cc = t & 15;
+    const int64_t tr = tile / tiles_c;
+    const int64_t r0 = tr * kCT, c0 = (tile - tr * tiles_c) * kCT;
+    const bool chunk_in = c0 + cc * 8 < cols;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int r = 16 * u + (t >> 4);
+        v[u] = u32x4{0u, 0u, 0u, 0u};
+        if (chunk_in)
+            v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (r0 + r) * ld_x + c0 + cc * 8));
+    }
+}
+
+// Persistent: workgroup w casts tiles w, w + G, ...; the next tile's loads are
+// in flight while the current one is cast.
+template <int kFmt, bool kPow2, bool kRowwise>
+__global__ __launch_bounds__(kThreads) void cast_transpose_kernel(
+    const uint16_t* __restrict__ x, int64_t cols, int64_t tiles_c, int64_t total_tiles, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scales, int64_t ld_s, uint8_t* __restrict__ qt,
+    int64_t ld_qt, float* __restrict__ scales_t, int64_t ld_st)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kCT * kCT * 2];
+    const float fmax = kFmt == FMT_E4M3 ? 448.0f : 57344.0f;
+    const int t = threadIdx.x;
+    const int cc = t & 15;
+
+    int64_t id = blockIdx.x;
+    u32x4 v[8];
+    load_tile(v, x, cols, tiles_c, ld_x, id);
+    for (; id < total_tiles; id += gridDim.x) {
+        const int64_t tr = id / tiles_c;
+        const int64_t r0 = tr * kCT, c0 = (id - tr * tiles_c) * kCT;
+        const int64_t next = id + gridDim.x;
+        u32x4 vn[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) vn[u] = u32x4{0u, 0u, 0u, 0u};
+        if (next < total_tiles) load_tile(vn, x, cols, tiles_c, ld_x, next);
+
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int r = 16 * u + (t >> 4);
+            *reinterpret_cast<u32x4*>(tile + r * (kCT * 2) + ((cc ^ ((r >> 4) & 15)) << 4)) = v[u];
+        }
+
+        if (kRowwise) {
+            // row-wise groups: the 16 lanes of a DPP row hold one row's 128 columns
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int r = 16 * u + (t >> 4);
+                float f[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    f[2 * i] = bf16lo(v[u][i]);
+                    f[2 * i + 1] = bf16hi(v[u][i]);
+                }
+                float amax = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+                amax = max_with_dpp<kQuadXor1>(amax);
+                amax = max_with_dpp<kQuadXor2>(amax);
+                amax = max_with_dpp<kRowHalfMirror>(amax);
+                amax = max_with_dpp<kRowMirror>(amax);
+                float scale, mult;
+                group_scale<kFmt, kPow2>(amax, scale, mult);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) f[i] *= mult;
+                const uint2 c = encode8<kFmt>(f, fmax);
+                *reinterpret_cast<uint2*>(q + (r0 + r) * ld_q + c0 + cc * 8) = c;
+                if (cc == 0) scales[(c0 / kCT) * ld_s + r0 + r] = scale;
+            }
+        }
+        __syncthreads();
+
+        // transposed groups: 8 lanes per column, lane `part` takes rows 16 part .. 16 part + 15
+        const int part = t & 7;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int col = 32 * u + (t >> 3);
+            float f[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const int r = 16 * part + k;
+                const uint16_t h = *reinterpret_cast<const uint16_t*>(
+                    tile + r * (kCT * 2) + (((col >> 3) ^ ((r >> 4) & 15)) << 4) + (col & 7) * 2);
+                f[k] = __builtin_bit_cast(float, (uint32_t)h << 16);
+            }
+            float amax = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(f[k]));
+            amax = max_with_dpp<kQuadXor1>(amax);
+            amax = max_with_dpp<kQuadXor2>(amax);
+            amax = max_with_dpp<kRowHalfMirror>(amax);
+            float scale, mult;
+            group_scale<kFmt, kPow2>(amax, scale, mult);
+            float s0[8], s1[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                s0[i] = f[i] * mult;
+                s1[i] = f[8 + i] * mult;
+            }
+            const uint2 e0 = encode8<kFmt>(s0, fmax);
+            const uint2 e1 = encode8<kFmt>(s1, fmax);
+            if (c0 + col < cols) {
+                *reinterpret_cast<uint4*>(qt + (c0 + col) * ld_qt + r0 + part * 16) = make_uint4(e0.x, e0.y, e1.x, e1.y);
+                if (part == 0) scales_t[(r0 / kCT) * ld_st + c0 + col] = scale;
+            }
+        }
+        __syncthreads();  // the tile buffer is rewritten by the next iteration
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = vn[u];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
@@ -179,6 +313,32 @@ hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
         if (pow2) cast_per_token_kernel<FMT_E5M2, true><<<grid, block, 0, stream>>>(x, rows, gpr, tiles_c, ld_x, q, ld_q, scales, ld_s);
         else cast_per_token_kernel<FMT_E5M2, false><<<grid, block, 0, stream>>>(x, rows, gpr, tiles_c, ld_x, q, ld_q, scales, ld_s);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_cast_transpose(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int fmt, bool pow2,
+                                 uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s, uint8_t* qt, int64_t ld_qt,
+                                 float* scales_t, int64_t ld_st, hipStream_t stream, LaunchInfo* info)
+{
+    const int64_t tiles_c = (cols + kCT - 1) / kCT;
+    const int64_t tiles = (rows / kCT) * tiles_c;
+    // four resident workgroups per compute unit (32 KiB of LDS each)
+    const int64_t blocks = std::min<int64_t>(tiles, 4 * (int64_t)device_cus());
+    if (info) { info->tile_m = kCT; info->tile_n = kCT; info->threads = kThreads; info->grid = blocks; }
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (blocks <= 0) return hipSuccess;
+    const dim3 grid((unsigned)blocks), block(kThreads);
+#define TE_CT_LAUNCH(F, P, R) \
+    cast_transpose_kernel<F, P, R><<<grid, block, 0, stream>>>(x, cols, tiles_c, tiles, ld_x, q, ld_q, scales, ld_s, qt, ld_qt, scales_t, ld_st)
+    const bool rw = q != nullptr;
+    if (fmt == FMT_E4M3) {
+        if (pow2) { if (rw) TE_CT_LAUNCH(FMT_E4M3, true, true); else TE_CT_LAUNCH(FMT_E4M3, true, false); }
+        else { if (rw) TE_CT_LAUNCH(FMT_E4M3, false, true); else TE_CT_LAUNCH(FMT_E4M3, false, false); }
+    } else {
+        if (pow2) { if (rw) TE_CT_LAUNCH(FMT_E5M2, true, true); else TE_CT_LAUNCH(FMT_E5M2, true, false); }
+        else { if (rw) TE_CT_LAUNCH(FMT_E5M2, false, true); else TE_CT_LAUNCH(FMT_E5M2, false, false); }
+    }
+#undef TE_CT_LAUNCH
     return hipGetLastError();
 }
 

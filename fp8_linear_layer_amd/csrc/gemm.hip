@@ -891,8 +891,9 @@ hipError_t launch_policy(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_
                   : launch_epi<kFmtA, kFmtB, false>(a, grid, tiles, s);
 }
 
-// Compute units of the current device (one persistent workgroup each: the
-// two stages fill most of a CU's LDS).
+}  // namespace
+
+// Compute units of the current device (cached per device).
 int device_cus()
 {
     static int cached[64] = {0};
@@ -906,11 +907,10 @@ int device_cus()
     return cached[dev];
 }
 
-}  // namespace
-
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream, LaunchInfo* info)
 {
     const int64_t tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN) * a.num_groups;
+    // one persistent workgroup per compute unit (the two stages fill most of its LDS)
     const int64_t blocks = std::min<int64_t>(tiles, device_cus());
     if (info) {
         info->tile_m = kBM;

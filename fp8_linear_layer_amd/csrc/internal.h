@@ -58,10 +58,16 @@ struct LaunchInfo {
     int64_t grid;
 };
 
+int device_cus();  // compute units of the current device
 hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream, LaunchInfo* info);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
                        bool pow2, uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s, hipStream_t stream,
                        LaunchInfo* info);
+// Row-wise cast (q may be null) and cast of the transpose in one pass; rows a
+// multiple of 128, cols a multiple of 128 with the row-wise cast, else of 8.
+hipError_t launch_cast_transpose(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int fmt, bool pow2,
+                                 uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s, uint8_t* qt, int64_t ld_qt,
+                                 float* scales_t, int64_t ld_st, hipStream_t stream, LaunchInfo* info);
 
 }  // namespace tefp8

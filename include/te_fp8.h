@@ -2,7 +2,8 @@
  * te_fp8.h - C ABI of the MI355X (gfx950) scaled-FP8 Linear-layer GEMM library.
  *
  * Five operations make up the FP8 hot path of a transformer Linear layer in
- * training: the per-token fp8 cast that produces the operands, the forward
+ * training: the per-token fp8 cast that produces the operands (also fused
+ * with the transposed cast the weight gradient needs), the forward
  * GEMM with its bias/GELU epilogue, the data-gradient GEMM with its dGELU and
  * bias-gradient epilogue, the weight-gradient GEMM that accumulates into an
  * fp32 buffer, and its K-grouped (mixture-of-experts) variant.
@@ -152,6 +153,39 @@ int64_t te_scale_ld(int64_t rows);
 te_status_t te_cast_fp8_per_token(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                                   te_dtype_t out_dtype, uint32_t flags, void* q, int64_t ld_q,
                                   float* scales, hipStream_t stream);
+
+/*
+ * Fused per-token cast and cast-transpose: one read of a bf16 matrix X
+ * [rows][cols] produces the operand cast of X (as te_cast_fp8_per_token) and
+ * the operand cast of X^T, i.e. 1x128 groups running down the columns of X.
+ *
+ * Where it sits: for a Linear layer with X [tokens][in] and dY
+ * [tokens][out], the weight gradient contracts over tokens (A = dY^T,
+ * B = X^T in the NT form above), while the forward and data-gradient GEMMs
+ * contract over features (X and dY themselves).  The DeepGEMM weight-gradient
+ * page counts the separate per-token casts feeding its kernel among the costs
+ * that lower end-to-end performance; this call reads the activation or
+ * gradient once and writes both operands.
+ *
+ * Definition (bit-identical to two separate casts):
+ *     (q,  scales)   = te_cast_fp8_per_token(X)        if q != NULL
+ *     (qt, scales_t) = te_cast_fp8_per_token(X^T)
+ * with the same out_dtype and flags for both.
+ *
+ *  x_bf16    [rows][ld_x] bf16; rows >= 128 and a multiple of 128; cols a
+ *            positive multiple of 128 when q is given, else of 8 (the
+ *            transposed groups need only the rows to be whole groups);
+ *            ld_x >= cols, ld_x % 8 == 0
+ *  q         [rows][ld_q] bytes, ld_q >= cols, ld_q % 16 == 0, or NULL
+ *  scales    [cols/128][te_scale_ld(rows)] fp32; NULL iff q is NULL
+ *  qt        [cols][ld_qt] bytes, ld_qt >= rows, ld_qt % 16 == 0
+ *  scales_t  [rows/128][te_scale_ld(cols)] fp32
+ *  Errors as for te_cast_fp8_per_token.
+ */
+te_status_t te_cast_fp8_per_token_transpose(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                            te_dtype_t out_dtype, uint32_t flags, void* q, int64_t ld_q,
+                                            float* scales, void* qt, int64_t ld_qt, float* scales_t,
+                                            hipStream_t stream);
 
 /*
  * Forward GEMM of a Linear layer, Y = X * W^T + b, with fused epilogues.

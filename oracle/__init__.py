@@ -127,6 +127,18 @@ def cast_per_token(x_bf16_bits, fmt: int, pow2: bool = False):
     return q, s
 
 
+def cast_per_token_transpose(x_bf16_bits, fmt: int, pow2: bool = False):
+    """The per-token cast of x and of its transpose, by definition: (q, s) =
+    cast(x), (qt, st) = cast(x^T), where x^T's 1x128 groups run down the
+    columns of x (the weight gradient contracts over the token rows).
+    Returns (q, s, qt, st), scales row-major as in cast_per_token; q and s are
+    None when the column count is not a multiple of 128 (no row-wise groups)."""
+    x = _c(x_bf16_bits, np.uint16)
+    q, s = cast_per_token(x, fmt, pow2) if x.shape[1] % 128 == 0 else (None, None)
+    qt, st = cast_per_token(np.ascontiguousarray(x.T), fmt, pow2)
+    return q, s, qt, st
+
+
 # ------------------------------------------------------------------ GEMM
 def gemm_nt(qa, sa, fa, qb, sb, fb, k0: int = 0, K: int | None = None):
     """o[m,n] = sum_kb sA sB sum_k dec(qa[m,k]) dec(qb[n,k]); d = same with |terms|."""

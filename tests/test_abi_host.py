@@ -157,6 +157,34 @@ def test_cast_rejects(lib, kw, status):
     assert cast(lib, **kw) == status
 
 
+QT = 0x70000
+ST = 0x80000
+
+
+def cast_t(lib, x=A, rows=256, cols=384, ldx=384, dt=1, flags=0, q=B, ldq=384, s=S, qt=QT, ldqt=256, st=ST):
+    return lib.te_cast_fp8_per_token_transpose(p(x), rows, cols, ldx, dt, flags, p(q), ldq, p(s), p(qt), ldqt,
+                                               p(st), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=0), INV), (dict(qt=0), INV), (dict(st=0), INV), (dict(q=0), INV), (dict(s=0), INV),
+    (dict(rows=0), INV), (dict(rows=100), INV), (dict(rows=200), INV), (dict(cols=100), INV), (dict(cols=0), INV),
+    (dict(cols=264, ldx=264, ldq=272), INV), (dict(q=0, s=0, cols=100, ldx=104), INV), (dict(q=0, s=0, cols=0), INV),
+    (dict(ldx=256), INV), (dict(ldq=256), INV), (dict(ldqt=128), INV), (dict(dt=3), INV), (dict(flags=2), INV),
+    (dict(x=MIS), MISAL), (dict(ldx=388), MISAL), (dict(q=MIS), MISAL), (dict(ldq=392), MISAL),
+    (dict(qt=MIS), MISAL), (dict(ldqt=264), MISAL), (dict(s=S + 4), MISAL), (dict(st=ST + 4), MISAL),
+])
+def test_cast_transpose_rejects(lib, kw, status):
+    assert cast_t(lib, **kw) == status
+
+
+def test_cast_transpose_rowwise_is_optional_but_both_or_neither(lib):
+    # q and its scales are given together or not at all (ldq is then ignored)
+    assert cast_t(lib, q=0, s=0, ldq=0, x=MIS) == MISAL   # validation reaches the alignment checks
+    assert cast_t(lib, q=0, ldq=0) == INV
+    assert cast_t(lib, s=0) == INV
+
+
 @pytest.mark.parametrize("rows,ld", [(0, 0), (1, 4), (3, 4), (4, 4), (5, 8), (7168, 7168), (2113, 2116)])
 def test_scale_ld(lib, rows, ld):
     assert lib.te_scale_ld(rows) == ld

@@ -100,3 +100,81 @@ def test_cast_is_deterministic():
     a = gpu_cast(bits, te.TE_DTYPE_E4M3, False)
     b = gpu_cast(bits, te.TE_DTYPE_E4M3, False)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ------------------------------------------------------------ fused cast-transpose
+def gpu_cast_t(bits, dt, pow2, rowwise=True, ld_x=None, ld_q=None, ld_qt=None):
+    rows, cols = bits.shape
+    ld_x, ld_q, ld_qt = ld_x or cols, ld_q or cols, ld_qt or rows
+    xb = np.zeros((rows, ld_x), np.uint16)
+    xb[:, :cols] = bits
+    x = bf16_dev(xb)[:, :cols]
+    qfull = torch.full((rows, ld_q), 0xA5, dtype=torch.uint8, device="cuda")
+    s = torch.full((cols // 128, scale_ld(rows)), -7.0, dtype=torch.float32, device="cuda")
+    qtfull = torch.full((cols, ld_qt), 0x5A, dtype=torch.uint8, device="cuda")
+    st = torch.full((rows // 128, scale_ld(cols)), -9.0, dtype=torch.float32, device="cuda")
+    te.te_cast_fp8_per_token_transpose(x, dt, te.TE_CAST_POW2_SCALE if pow2 else 0, rowwise=rowwise,
+                                       q=qfull[:, :cols] if rowwise else None, scales=s if rowwise else None,
+                                       qt=qtfull[:, :rows], scales_t=st)
+    torch.cuda.synchronize()
+    qh, sh, qth, sth = host(qfull).numpy(), host(s).numpy(), host(qtfull).numpy(), host(st).numpy()
+    assert (qth[:, rows:] == 0x5A).all(), "cast-transpose wrote past rows"
+    assert (sth[:, cols:] == -9.0).all(), "cast-transpose wrote into the transposed scale padding"
+    if not rowwise:
+        assert (qh == 0xA5).all() and (sh == -7.0).all(), "row-wise outputs written although not requested"
+        return None, None, qth[:, :rows], shost(st, cols)
+    assert (qh[:, cols:] == 0xA5).all() and (sh[:, rows:] == -7.0).all()
+    return qh[:, :cols], shost(s, rows), qth[:, :rows], shost(st, cols)
+
+
+def assert_same_t(bits, dt, pow2, rowwise=True, **kw):
+    q, s, qt, st = gpu_cast_t(bits, dt, pow2, rowwise, **kw)
+    qo, so, qto, sto = oracle.cast_per_token_transpose(bits, FMT[dt], pow2)
+    bad = np.argwhere(qt != qto)
+    assert bad.size == 0, f"{len(bad)} transposed code mismatches, first {bad[0]}"
+    assert np.array_equal(st.view(np.uint32), sto.view(np.uint32)), "transposed scale mismatch"
+    if rowwise:
+        bad = np.argwhere(q != qo)
+        assert bad.size == 0, f"{len(bad)} row-wise code mismatches, first {bad[0]}"
+        assert np.array_equal(s.view(np.uint32), so.view(np.uint32)), "row-wise scale mismatch"
+
+
+@pytest.mark.parametrize("dt", [te.TE_DTYPE_E4M3, te.TE_DTYPE_E5M2])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_cast_transpose_edge_groups(dt, pow2):
+    # the edge-case groups as columns (transposed direction) next to normal data
+    sp = special_rows(dt)                                           # [9, 128]
+    extra = W.normal_bf16(np.random.SeedSequence(2), (128, 128 - sp.shape[0]))
+    assert_same_t(np.ascontiguousarray(np.concatenate([sp.T, extra], axis=1)), dt, pow2)
+    # and as rows (row-wise direction)
+    sp2 = np.concatenate([sp, W.normal_bf16(np.random.SeedSequence(3), (128 - sp.shape[0], 128))], axis=0)
+    assert_same_t(np.ascontiguousarray(np.concatenate([sp2, sp2[::-1]], axis=1)), dt, pow2)
+
+
+@pytest.mark.parametrize("dt", [te.TE_DTYPE_E4M3, te.TE_DTYPE_E5M2])
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("rowwise", [True, False])
+@pytest.mark.parametrize("rows,cols,ldx,ldq,ldqt", [(128, 128, None, None, None), (256, 384, None, None, None),
+                                                    (384, 1024, 1152, 1040, 400), (1024, 640, 648, None, 1040)])
+def test_cast_transpose_shapes_and_strides(dt, pow2, rowwise, rows, cols, ldx, ldq, ldqt):
+    bits = W.normal_bf16(np.random.SeedSequence(rows * 11 + cols), (rows, cols), 0.3)
+    assert_same_t(bits, dt, pow2, rowwise, ld_x=ldx, ld_q=ldq, ld_qt=ldqt)
+
+
+@pytest.mark.parametrize("dt", [te.TE_DTYPE_E4M3, te.TE_DTYPE_E5M2])
+@pytest.mark.parametrize("rows,cols,ldx,ldqt", [(128, 8, None, None), (256, 200, 208, None), (384, 1064, 1072, 400)])
+def test_cast_transpose_ragged_columns(dt, rows, cols, ldx, ldqt):
+    """Without the row-wise cast the column count needs only be a multiple of 8: the last tile
+    column is partial."""
+    bits = W.normal_bf16(np.random.SeedSequence(rows * 13 + cols), (rows, cols), 0.3)
+    assert_same_t(bits, dt, False, rowwise=False, ld_x=ldx, ld_qt=ldqt)
+
+
+@pytest.mark.parametrize("name,shape,std,dt", [
+    ("dense-wgrad dY (tokens x out)", (4096, 7168), 1.0, te.TE_DTYPE_E4M3),
+    ("dense-wgrad X (tokens x in)", (4096, 2112), 1.0, te.TE_DTYPE_E4M3),
+    ("fprop X (tokens x in)", (8192, 4096), 1.0, te.TE_DTYPE_E4M3),
+])
+def test_cast_transpose_workload_sizes(name, shape, std, dt):
+    bits = W.normal_bf16(np.random.SeedSequence(zlib.crc32(name.encode())), shape, std)
+    assert_same_t(bits, dt, False, rowwise=shape[1] % 128 == 0)

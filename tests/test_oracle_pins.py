@@ -170,6 +170,32 @@ def test_cast_invariants(fmt):
     assert np.all(err <= bound)
 
 
+@pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
+def test_cast_transpose_groups_run_down_the_columns(fmt):
+    """The transposed cast groups 128 consecutive rows of one column (the weight gradient's
+    contraction over tokens): its scale of (column c, row block rb) is that column segment's
+    amax / FP8_MAX, the segment's largest element lands on +-FP8_MAX, and the codes equal
+    torch's float8 conversion of the column segment times FP8_MAX / amax."""
+    rows, cols = 256, 384
+    xb = W.normal_bf16(np.random.SeedSequence(21), (rows, cols), 0.5)
+    xb[128:, 7] = 0                                  # an all-zero column segment
+    q, s, qt, st = oracle.cast_per_token_transpose(xb, fmt)
+    q1, s1 = oracle.cast_per_token(xb, fmt)
+    assert np.array_equal(q, q1) and np.array_equal(s, s1)
+    assert qt.shape == (cols, rows) and st.shape == (cols, rows // 128)
+    x = torch.from_numpy(W.bf16_bits_to_f32(xb))                       # [rows, cols]
+    seg = x.view(rows // 128, 128, cols).permute(2, 0, 1)               # [cols, row block, 128 rows]
+    amax = seg.abs().amax(-1, keepdim=True).clamp_min(2.0 ** -100)
+    fmax = torch.tensor(oracle.fp8_max(fmt), dtype=torch.float32)
+    assert torch.equal(torch.from_numpy(st).view(cols, rows // 128, 1), amax / fmax)
+    ref = (seg * (fmax / amax)).to(FMTS[fmt]).view(torch.uint8).reshape(cols, rows).numpy()
+    assert np.array_equal(qt, ref)
+    deq = torch_decode(qt, fmt).reshape(cols, rows // 128, 128)
+    top = np.take_along_axis(deq, seg.abs().argmax(-1, keepdim=True).numpy(), -1)[..., 0]
+    nz = seg.abs().amax(-1).numpy() > 0
+    assert np.all(np.abs(top[nz]) == float(fmax)) and (qt[7, 128:] == 0).all()
+
+
 def test_cast_rejects_non_finite():
     xb = bits(np.ones((1, 128)))
     xb[0, 5] = 0x7F80  # +inf
