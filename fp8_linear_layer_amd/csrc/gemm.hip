@@ -35,8 +35,9 @@
 //    of the block ride along in the same stage.
 //  * Software pipeline inside a block: a wave keeps its four A fragments in
 //    registers and streams its eight B column groups two groups ahead; in the
-//    FULL loop each matrix-core product is promoted one instruction later, so
-//    the vector unit works on product t-1 while the matrix core computes t.
+//    FULL loop each matrix-core product is promoted two instructions later
+//    (the promotion of product t-2 precedes instruction t, which reuses its
+//    register), so the vector unit never waits for the product just issued.
 //    The single barrier of a block sits after the last read of the current
 //    stage: past it the copies of block +2 go into the current stage and the
 //    next block's first fragments are read from the other one, so a block
@@ -333,16 +334,17 @@ __device__ __forceinline__ void block_body(const GemmArgs& p, uint8_t* cur, uint
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.bq[j & 3], q.ac[i], acc[i][j], kFmtB,
                                                                              kFmtA, 0, eb, 0, ea[i]);
             } else {
-                q.P[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.bq[j & 3], q.ac[i],
-                                                                              v4f{0.f, 0.f, 0.f, 0.f}, kFmtB, kFmtA,
-                                                                              0, 0, 0, 0);
-                // promote the previous slot's product (slot -1 is the previous block's last)
-                const int tp = (t + kTM * kTN - 1) % (kTM * kTN);
+                // promote the product of two slots back (slots -2 and -1 are the previous
+                // block's last two), then start this slot's product in the register it frees
+                const int tp = (t + kTM * kTN - 2) % (kTM * kTN);
                 const int ip = tp % kTM, jp = tp / kTM;
-                promote(acc[ip][jp], q.P[(t + 1) & 1], t == 0 ? q.sa[1 - S][ip] : q.sa[S][ip], q.sbq[jp & 3]);
+                promote(acc[ip][jp], q.P[t & 1], t < 2 ? q.sa[1 - S][ip] : q.sa[S][ip], q.sbq[jp & 3]);
                 // pin the update to this slot (otherwise it is sunk to the end of the block and every
                 // product of the block stays live)
                 asm volatile("" : "+v"(acc[ip][jp]));
+                q.P[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.bq[j & 3], q.ac[i],
+                                                                              v4f{0.f, 0.f, 0.f, 0.f}, kFmtB, kFmtA,
+                                                                              0, 0, 0, 0);
             }
             // LDS reads of this slot
             if (j < kBarrierGroup) {
@@ -377,11 +379,12 @@ __device__ __forceinline__ void block_body(const GemmArgs& p, uint8_t* cur, uint
                 // last column group: A fragment i is dead after this slot's instruction
                 q.ac[i] = lds_frag(nxt, o.a_lo, o.a_hi, i * 2048);
             }
-            // Ask the scheduler for this slot's order: the matrix-core op, the
-            // promotion of the previous product, then the slot's LDS reads.
+            // Ask the scheduler for this slot's order: (FULL) the promotion of
+            // the product from two slots back, the matrix-core op, then the
+            // slot's LDS reads.
             const int n_ds = j < kBarrierGroup ? (i < 3 ? 1 : 0) : (j == kBarrierGroup && i == 3 ? kTM : 2);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (!kChain) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             sched_ds_reads(n_ds);
         }
     }
@@ -412,8 +415,8 @@ __device__ __forceinline__ void main_loop(const GemmArgs& p, uint8_t* __restrict
         if (kChain) q.ebq[j] = lds_u32(s0 + o.sb_row + j * 64);
         else q.sbq[j] = lds_f32x4(s0 + o.sb_vec + j * 64);
     }
-    // the first slot promotes a zero product with zero scales
-    q.P[1] = v4f{0.f, 0.f, 0.f, 0.f};
+    // the first two slots promote zero products with zero scales
+    q.P[0] = q.P[1] = v4f{0.f, 0.f, 0.f, 0.f};
     q.sbq[3] = make_float4(0.f, 0.f, 0.f, 0.f);
     q.sbq[2] = q.sbq[3];
     q.ebq[2] = q.ebq[3] = 0;
@@ -428,9 +431,11 @@ __device__ __forceinline__ void main_loop(const GemmArgs& p, uint8_t* __restrict
     // the trailing copies (empty ranges) still write LDS: let them land
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (!kChain) {
-        // the last product of the last block
-        const float s_a = (nkb & 1) ? q.sa[0][kTM - 1] : q.sa[1][kTM - 1];
-        promote(acc[kTM - 1][kTN - 1], q.P[1], s_a, q.sbq[(kTN - 1) & 3]);
+        // the last two products of the last block (slots 30 and 31: registers P[0] and P[1])
+        const float s_a2 = (nkb & 1) ? q.sa[0][kTM - 2] : q.sa[1][kTM - 2];
+        const float s_a1 = (nkb & 1) ? q.sa[0][kTM - 1] : q.sa[1][kTM - 1];
+        promote(acc[kTM - 2][kTN - 1], q.P[0], s_a2, q.sbq[(kTN - 1) & 3]);
+        promote(acc[kTM - 1][kTN - 1], q.P[1], s_a1, q.sbq[(kTN - 1) & 3]);
     }
 }
 
