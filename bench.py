@@ -11,8 +11,10 @@ the GEMM kernel's roofline fraction against the FP8 dense matrix-core peak
 (kernel time from HIP events on the launch stream), the oracle's CPU
 throughput on a bounded sample, and per-kernel timings of the other
 workloads (fprop with bias+GELU at 8192 x 14336 x 4096 in both accumulation
-policies, dgrad at 8192 x 4096 x 14336 and its dGELU+bias-grad form, the
-e5m2 cast of the gradient, and the 8-expert K-grouped wgrad).
+policies, the fused cast + cast-transpose of the activation, dgrad at
+8192 x 4096 x 14336 and its dGELU+bias-grad form, the e5m2 cast of the
+gradient, the dense weight gradient fed from token-major sources through
+the cast-transpose, and the 8-expert K-grouped wgrad).
 """
 from __future__ import annotations
 
@@ -169,6 +171,27 @@ def breakdown(te, torch):
     out["dgrad_dz_dgelu_bgrad_full"] = {"shape": [M, N, K], "ms": round(med1, 4), "tflops": round(f / med1 / 1e9, 1),
                                         "epilogue_overhead": round(med1 / med0 - 1.0, 3)}
     del do, w2t, zz, qo, so, q2, s2, dz, bg
+
+    # the dense weight gradient from token-major sources: dY [4096 tokens x 7168] and X [4096 x 2112]
+    # are cast-transposed (1x128 groups along tokens) and fed to out += A B^T
+    T, M, N = 4096, 7168, 2112
+    dyt, xt = randn((T, M), 1.0, 11), randn((T, N), 1.0, 12)
+    qa = torch.empty((M, T), dtype=torch.uint8, device=dev)
+    sa = torch.empty((T // 128, te.scale_ld(M)), dtype=torch.float32, device=dev)
+    qb = torch.empty((N, T), dtype=torch.uint8, device=dev)
+    sb = torch.empty((T // 128, te.scale_ld(N)), dtype=torch.float32, device=dev)
+    o = torch.zeros((M, N), dtype=torch.float32, device=dev)
+
+    def wgrad_token_major():
+        te.te_cast_fp8_per_token_transpose(dyt, E4, rowwise=False, qt=qa, scales_t=sa)
+        te.te_cast_fp8_per_token_transpose(xt, E4, rowwise=False, qt=qb, scales_t=sb)
+        te.te_fp8_wgrad_accum(qa, sa, E4, qb, sb, E4, o, te.TE_ACCUM_FULL_FP32)
+
+    med, _ = timed(wgrad_token_major, 10)
+    out["wgrad_from_token_major_7168x2112x4096"] = {
+        "ms": round(med, 4), "tflops": round(2.0 * M * N * T / med / 1e9, 1),
+        "step": "cast-transpose dY and X (tokens x features, bf16) + out += A B^T"}
+    del dyt, xt, qa, sa, qb, sb, o
 
     # K-grouped wgrad: 8 experts, 2048 x 7168, per-expert K multinomial in blocks of 128 summing to 32768
     import workloads as W
