@@ -14,7 +14,8 @@ workloads (fprop with bias+GELU at 8192 x 14336 x 4096 in both accumulation
 policies, the fused cast + cast-transpose of the activation, dgrad at
 8192 x 4096 x 14336 and its dGELU+bias-grad form, the e5m2 cast of the
 gradient, the dense weight gradient fed from token-major sources through
-the cast-transpose, and the 8-expert K-grouped wgrad).
+the cast-transpose, and the 8-expert K-grouped wgrad with its group sizes
+on the host and on the device).
 """
 from __future__ import annotations
 
@@ -204,6 +205,10 @@ def breakdown(te, torch):
     med, _ = timed(lambda: te.te_fp8_kgrouped_wgrad(qa, sa, E4, qb, sb, E4, gk, o, te.TE_ACCUM_FULL_FP32), 10)
     f = 2.0 * M * N * S
     out["kgrouped_wgrad_full"] = {"group_k": gk, "ms": round(med, 4), "tflops": round(f / med / 1e9, 1)}
+    gk_dev = torch.tensor(gk, dtype=torch.int64, device=dev)
+    med, _ = timed(lambda: te.te_fp8_kgrouped_wgrad_device_sizes(qa, sa, E4, qb, sb, E4, gk_dev, o,
+                                                                 te.TE_ACCUM_FULL_FP32), 10)
+    out["kgrouped_wgrad_device_sizes_full"] = {"ms": round(med, 4), "tflops": round(f / med / 1e9, 1)}
     return out
 
 

@@ -36,7 +36,7 @@ TE_EPI_BGRAD = 16
 TE_CAST_POW2_SCALE = 1
 
 EXPORTED = ("te_cast_fp8_per_token", "te_cast_fp8_per_token_transpose", "te_fp8_gemm_fwd", "te_fp8_gemm_dgrad", "te_fp8_wgrad_accum",
-            "te_fp8_kgrouped_wgrad", "te_status_string", "te_last_error_message", "te_scale_ld")
+            "te_fp8_kgrouped_wgrad", "te_fp8_kgrouped_wgrad_device_sizes", "te_status_string", "te_last_error_message", "te_scale_ld")
 
 
 class TeFp8Error(RuntimeError):
@@ -75,6 +75,8 @@ def load_library():
     lib.te_fp8_wgrad_accum.argtypes = [P, P, I, P, P, I, I64, I64, I64, P, I64, I, P]
     lib.te_fp8_kgrouped_wgrad.restype = I
     lib.te_fp8_kgrouped_wgrad.argtypes = [P, P, I, P, P, I, I64, I64, P, I32, P, I, P]
+    lib.te_fp8_kgrouped_wgrad_device_sizes.restype = I
+    lib.te_fp8_kgrouped_wgrad_device_sizes.argtypes = [P, P, I, P, P, I, I64, I64, I64, P, I32, P, I, P]
     _lib = lib
     return lib
 
@@ -210,4 +212,21 @@ def te_fp8_kgrouped_wgrad(a, a_scales, a_dtype, b, b_scales, b_dtype, group_k, o
     _check(load_library().te_fp8_kgrouped_wgrad(
         _ptr(a), _ptr(a_scales), a_dtype, _ptr(b), _ptr(b_scales), b_dtype, M, N,
         ctypes.cast(gk, ctypes.c_void_p), len(group_k), _ptr(out), accum, _stream(stream)))
+    return out
+
+
+def te_fp8_kgrouped_wgrad_device_sizes(a, a_scales, a_dtype, b, b_scales, b_dtype, group_k, out,
+                                       accum=TE_ACCUM_FULL_FP32, stream=None):
+    """out[g] += A[:, off_g:off_g+K_g] B[:, off_g:off_g+K_g]^T with group_k an int64 tensor on the device
+    (read by the kernel; nothing is copied to the host)."""
+    M, S = a.shape
+    N = b.shape[0]
+    assert group_k.dtype == torch.int64 and group_k.is_cuda and group_k.dim() == 1 and group_k.is_contiguous()
+    G = group_k.numel()
+    assert out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (G, M, N)
+    _scales_ok(a_scales, M, S, "a_scales")
+    _scales_ok(b_scales, N, S, "b_scales")
+    _check(load_library().te_fp8_kgrouped_wgrad_device_sizes(
+        _ptr(a), _ptr(a_scales), a_dtype, _ptr(b), _ptr(b_scales), b_dtype, M, N, S, _ptr(group_k), G,
+        _ptr(out), accum, _stream(stream)))
     return out

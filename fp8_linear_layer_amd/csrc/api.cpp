@@ -389,4 +389,33 @@ te_status_t te_fp8_kgrouped_wgrad(const void* a, const float* a_scales, te_dtype
     }
 }
 
+te_status_t te_fp8_kgrouped_wgrad_device_sizes(const void* a, const float* a_scales, te_dtype_t a_dtype,
+                                               const void* b, const float* b_scales, te_dtype_t b_dtype,
+                                               int64_t M, int64_t N, int64_t sum_k, const int64_t* group_k_device,
+                                               int32_t G, float* out, te_accum_t accum, hipStream_t stream)
+{
+    try {
+        const char* fn = "te_fp8_kgrouped_wgrad_device_sizes";
+        if (!group_k_device) return fail(TE_ERR_INVALID_ARGUMENT, "%s: group_k_device is null", fn);
+        if (!aligned(group_k_device, 8)) return fail(TE_ERR_MISALIGNED, "%s: group_k_device must be 8-byte aligned", fn);
+        if (G < 1 || G > tefp8::kMaxDeviceGroups)
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: G must be in [1, %d] (got %d)", fn, tefp8::kMaxDeviceGroups, (int)G);
+        te_status_t st = check_operands(fn, a, a_scales, a_dtype, b, b_scales, b_dtype, M, N, sum_k, accum);
+        if (st != TE_OK) return st;
+        st = check_output(fn, "out", out, TE_DTYPE_F32, N, N);
+        if (st != TE_OK) return st;
+        tefp8::GemmArgs g = base_args(a, a_scales, a_dtype, b, b_scales, b_dtype, M, N, sum_k, accum);
+        g.epi = tefp8::Epi::Wgrad;
+        g.out = out;
+        g.ld_out = N;
+        g.out_group_stride = M * N;
+        g.num_groups = G;
+        g.group_k_dev = group_k_device;
+        g.sum_kb = sum_k / 128;
+        return launch(fn, g, stream, sum_k, a_dtype, b_dtype, accum, 0);
+    } catch (...) {
+        return fail(TE_ERR_INTERNAL, "te_fp8_kgrouped_wgrad_device_sizes: internal error");
+    }
+}
+
 }  // extern "C"

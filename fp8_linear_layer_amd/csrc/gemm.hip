@@ -46,7 +46,10 @@
 //  * Tiles past the last row read zero (buffer ranges end at the last valid
 //    row) and their stores are masked.
 //  * K-grouped launches carry up to 128 (kb_off, kb_len, out) descriptors by
-//    value; blocks are ordered longest group first.
+//    value; blocks are ordered longest group first.  With group sizes in
+//    device memory each tile derives its group's range from them instead
+//    (every group has the same M x N tiles, so the tile -> group mapping needs
+//    no sizes); a tile of an empty group does nothing.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -752,14 +755,27 @@ __device__ __forceinline__ TileCtx tile_ctx(const GemmArgs& p, int64_t tile)
     const int64_t first_m = band * kGroupM;
     const int64_t band_rows = min((int64_t)kGroupM, tiles_m - first_m);
     t -= band * per_band;
-    const Group grp = p.groups[gslot];
+    Group grp;
+    if (p.group_k_dev) {
+        // group sizes in device memory: the range of group gslot starts after
+        // the earlier groups; every offset and length is clamped to the
+        // operands' sum_kb blocks, so no value can move a read outside them
+        int64_t off = 0;
+        for (int h = 0; h < gslot; ++h) off += max(p.group_k_dev[h], (int64_t)0) / kBK;
+        off = min(off, p.sum_kb);
+        const int64_t len = min(max(p.group_k_dev[gslot], (int64_t)0) / kBK, p.sum_kb - off);
+        grp = Group{(int32_t)off, (int32_t)len, gslot, 0};
+    } else {
+        grp = p.groups[gslot];
+    }
     TileCtx c;
     c.m0 = (first_m + t % band_rows) * kBM;
     c.n0 = (t / band_rows) * kBN;
     c.out_off = (int64_t)grp.out_idx * p.out_group_stride;
     c.kb0 = grp.kb_off;
     c.nkb = grp.kb_len;
-    c.src = tile_src(p, c.m0, c.n0);
+    // an empty group's tile copies nothing and leaves its output untouched
+    c.src = select_src(tile_src(p, c.m0, c.n0), c.nkb > 0);
     return c;
 }
 
@@ -860,10 +876,12 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p, int
         }
         // (a tile inside the matrix takes the copy of the epilogue without
         // bounds checks: straight-line code lets its loads be in flight together)
-        if (c.m0 + kBM <= p.M && c.n0 + kBN <= p.N)
-            epilogue<kEpi, true>(p, acc, c.m0, c.n0, c.out_off, wave, lane);
-        else
-            epilogue<kEpi, false>(p, acc, c.m0, c.n0, c.out_off, wave, lane);
+        if (c.nkb > 0) {
+            if (c.m0 + kBM <= p.M && c.n0 + kBN <= p.N)
+                epilogue<kEpi, true>(p, acc, c.m0, c.n0, c.out_off, wave, lane);
+            else
+                epilogue<kEpi, false>(p, acc, c.m0, c.n0, c.out_off, wave, lane);
+        }
         if (!more) break;
         // (after the epilogue: the scale reads overlap its stores)
         if (kFast) ok = row_scales_pow2(p, cn);

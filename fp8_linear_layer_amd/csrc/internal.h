@@ -25,6 +25,7 @@ struct Group {
 };
 
 constexpr int kMaxGroupsPerLaunch = 128;
+constexpr int kMaxDeviceGroups = 256;  // groups of the device-sized K-grouped call
 
 struct GemmArgs {
     const uint8_t* a;      // [M][lda] fp8
@@ -51,6 +52,11 @@ struct GemmArgs {
     // groups
     int num_groups;
     Group groups[kMaxGroupsPerLaunch];
+    // K-grouped with group sizes in device memory: when set, groups[] is
+    // unused, group g's contraction range is read from group_k_dev (K per
+    // group, in elements) and clamped to the sum_kb blocks of the operands.
+    const int64_t* group_k_dev;
+    int64_t sum_kb;
 };
 
 struct LaunchInfo {

@@ -270,6 +270,31 @@ te_status_t te_fp8_kgrouped_wgrad(const void* a, const float* a_scales, te_dtype
                                   int64_t M, int64_t N, const int64_t* group_k, int32_t G,
                                   float* out, te_accum_t accum, hipStream_t stream);
 
+/*
+ * The same K-grouped weight gradient with the group sizes in device memory,
+ * e.g. the per-expert token counts a router produced on the GPU: nothing is
+ * read back to the host and the call does not synchronise (the pages' grouped
+ * kernel takes its per-group layout on the device, not from the host).
+ *
+ *  a, a_scales   [M][sum_k] fp8, [sum_k/128][te_scale_ld(M)]
+ *  b, b_scales   [N][sum_k] fp8, [sum_k/128][te_scale_ld(N)]
+ *  sum_k         the operands' contraction width: >= 128, a multiple of 128
+ *  group_k_device DEVICE array of G int64 (8-byte aligned), read by the
+ *                kernel when it runs: each >= 0 and a multiple of 128, summing
+ *                to at most sum_k (columns past the sum are not used).  Other
+ *                values give unspecified results, but every offset and length
+ *                is clamped to the operands, so no read leaves them.
+ *  G             1 .. 256
+ *  out           [G][M][N] fp32, contiguous; a group with K_g = 0 is left
+ *                untouched
+ * Tiles are scheduled in group order (the host-sized call orders groups
+ * longest first, which balances unequal groups better).
+ */
+te_status_t te_fp8_kgrouped_wgrad_device_sizes(const void* a, const float* a_scales, te_dtype_t a_dtype,
+                                               const void* b, const float* b_scales, te_dtype_t b_dtype,
+                                               int64_t M, int64_t N, int64_t sum_k, const int64_t* group_k_device,
+                                               int32_t G, float* out, te_accum_t accum, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* te_status_string(te_status_t status);
 

@@ -142,6 +142,22 @@ def test_kgrouped_null_group_k(lib):
     assert lib.te_fp8_kgrouped_wgrad(p(A), p(S), 1, p(B), p(S), 1, 256, 256, None, 2, p(O), 1, None) == INV
 
 
+GK = 0x90000  # dummy device address of the group sizes
+
+
+def kgrouped_dev(lib, gk=GK, G=4, sum_k=512, M=256, N=256, out=O, accum=1):
+    return lib.te_fp8_kgrouped_wgrad_device_sizes(p(A), p(S), 1, p(B), p(S), 1, M, N, sum_k, p(gk), G, p(out),
+                                                  accum, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(gk=0), INV), (dict(G=0), INV), (dict(G=257), INV), (dict(sum_k=0), INV), (dict(sum_k=200), INV),
+    (dict(M=0), INV), (dict(out=0), INV), (dict(accum=0), INV), (dict(gk=GK + 4), MISAL),
+])
+def test_kgrouped_device_sizes_rejects(lib, kw, status):
+    assert kgrouped_dev(lib, **kw) == status
+
+
 def cast(lib, x=A, rows=4, cols=256, ldx=256, dt=1, flags=0, q=B, ldq=256, s=S):
     return lib.te_cast_fp8_per_token(p(x), rows, cols, ldx, dt, flags, p(q), ldq, p(s), None)
 

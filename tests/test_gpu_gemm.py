@@ -306,6 +306,76 @@ def test_kgrouped_many_groups():
     check_f32(host(out).numpy(), want, mag, "300 groups")
 
 
+@pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
+def test_kgrouped_device_sizes_matches_host_sizes(accum, pow2):
+    """Group sizes read from device memory: bit-identical to the host-sized call (the tiles do the
+    same arithmetic; only their order differs), within tolerance of the oracle, empty groups untouched
+    (including the sign of zero), and columns past the groups' sum unused."""
+    gk = np.array([256, 0, 128, 384, 0, 128], np.int64)
+    M, N, S = 200, 300, int(gk.sum()) + 256          # 256 trailing columns belong to no group
+    qa, sa = operand(51, M, S, E4, pow2=pow2)
+    qb, sb = operand(52, N, S, E4, pow2=pow2)
+    init = W.normal_f32(np.random.SeedSequence(53), (len(gk), M, N))
+    init[1, :7, :5] = -0.0
+    cut = int(gk.sum())
+    qa_c, sa_c = np.ascontiguousarray(qa[:, :cut]), np.ascontiguousarray(sa[:, :cut // 128])
+    qb_c, sb_c = np.ascontiguousarray(qb[:, :cut]), np.ascontiguousarray(sb[:, :cut // 128])
+    want, mag = oracle.kgrouped_wgrad(qa_c, sa_c, oracle.E4M3, qb_c, sb_c, oracle.E4M3, gk, init)
+    out_d = dev(init)
+    te.te_fp8_kgrouped_wgrad_device_sizes(dev(qa), sdev(sa), E4, dev(qb), sdev(sb), E4,
+                                          torch.from_numpy(gk).cuda(), out_d, accum)
+    got = host(out_d).numpy()
+    # the host-sized call on the operands cut to the groups' columns
+    out_h = dev(init)
+    te.te_fp8_kgrouped_wgrad(dev(qa_c), sdev(sa_c), E4, dev(qb_c), sdev(sb_c), E4, gk.tolist(), out_h, accum)
+    assert np.array_equal(got.view(np.uint32), host(out_h).numpy().view(np.uint32))
+    for g in range(len(gk)):
+        if gk[g] == 0:
+            assert np.array_equal(got[g].view(np.uint32), init[g].view(np.uint32)), f"empty group {g} touched"
+        else:
+            check_f32(got[g], want[g], mag[g], f"group {g}")
+
+
+def test_kgrouped_device_sizes_follow_the_device_array():
+    """The sizes are read when the kernel runs: changing them on the device (no host copy) between two
+    calls changes which columns each group takes."""
+    M, N, S = 64, 96, 1024
+    qa, sa = operand(61, M, S, E4)
+    qb, sb = operand(62, N, S, E4)
+    A, SA, B, SB = dev(qa), sdev(sa), dev(qb), sdev(sb)
+    first, second = np.array([512, 512], np.int64), np.array([128, 768], np.int64)
+    gk = torch.from_numpy(first).cuda()
+    init = W.normal_f32(np.random.SeedSequence(63), (2, M, N))
+    out = dev(init)
+    te.te_fp8_kgrouped_wgrad_device_sizes(A, SA, E4, B, SB, E4, gk, out, FULL)
+    gk.copy_(torch.from_numpy(second).cuda())        # device-to-device update, stream-ordered
+    te.te_fp8_kgrouped_wgrad_device_sizes(A, SA, E4, B, SB, E4, gk, out, FULL)
+    o1, d1 = oracle.kgrouped_wgrad(qa, sa, oracle.E4M3, qb, sb, oracle.E4M3, first, init)
+    want, mag = oracle.kgrouped_wgrad(np.ascontiguousarray(qa[:, :896]), np.ascontiguousarray(sa[:, :7]), oracle.E4M3,
+                                      np.ascontiguousarray(qb[:, :896]), np.ascontiguousarray(sb[:, :7]), oracle.E4M3,
+                                      second, o1)
+    check_f32(host(out).numpy(), want, mag + d1, "two calls")
+
+
+def test_kgrouped_device_sizes_workload():
+    """The 8-expert workload with its multinomial token counts on the device."""
+    sh = W.KGROUPED.shapes
+    inp = W.kgrouped_inputs()
+    gk = inp["group_k"]
+    qa, sa = oracle.cast_per_token(inp["a"], oracle.E4M3)
+    qb, sb = oracle.cast_per_token(inp["b"], oracle.E4M3)
+    out = dev(inp["out0"])
+    te.te_fp8_kgrouped_wgrad_device_sizes(dev(qa), sdev(sa), E4, dev(qb), sdev(sb), E4,
+                                          torch.from_numpy(np.asarray(gk, np.int64)).cuda(), out, FULL)
+    got = host(out).numpy()
+    offs = np.concatenate([[0], np.cumsum(gk)])
+    for g in range(sh["G"]):
+        rows, cols = sample_idx(sh["M"], 8, 30 + g), sample_idx(sh["N"], 12, 40 + g)
+        o, d = grid_entries(qa, sa, oracle.E4M3, qb, sb, oracle.E4M3, rows, cols, int(offs[g]), int(gk[g]))
+        want, mag = oracle.wgrad(o, d, inp["out0"][g][np.ix_(rows, cols)])
+        check_f32(got[g][np.ix_(rows, cols)], want, mag, f"expert {g}")
+
+
 def test_kgrouped_workload():
     sh = W.KGROUPED.shapes
     inp = W.kgrouped_inputs()
