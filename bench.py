@@ -14,8 +14,8 @@ workloads (fprop with bias+GELU at 8192 x 14336 x 4096 in both accumulation
 policies, the fused cast + cast-transpose of the activation, dgrad at
 8192 x 4096 x 14336 and its dGELU+bias-grad form, the e5m2 cast of the
 gradient, the dense weight gradient fed from token-major sources through
-the cast-transpose, and the 8-expert K-grouped wgrad with its group sizes
-on the host and on the device).
+the cast-transpose, the 8-expert K-grouped wgrad with its group sizes on
+the host and on the device, and the 8-expert M-grouped forward).
 """
 from __future__ import annotations
 
@@ -209,6 +209,24 @@ def breakdown(te, torch):
     med, _ = timed(lambda: te.te_fp8_kgrouped_wgrad_device_sizes(qa, sa, E4, qb, sb, E4, gk_dev, o,
                                                                  te.TE_ACCUM_FULL_FP32), 10)
     out["kgrouped_wgrad_device_sizes_full"] = {"ms": round(med, 4), "tflops": round(f / med / 1e9, 1)}
+    del qa, sa, qb, sb, o, a, bm
+
+    # M-grouped expert forward: 8 experts x 1024 tokens (4 blocks of 256 rows each), N = 4096, K = 7168,
+    # bias + GELU, bf16 out
+    G, T, N, K = 8, 8192, 4096, 7168
+    xg, wg, bg = randn((T, K), 1.0, 13), randn((G * N, K), 0.02, 14), randn((G, N), 0.1, 15)
+    qx, sx = te.te_cast_fp8_per_token(xg, E4)
+    qw, sw = te.te_cast_fp8_per_token(wg, E4)
+    qw = qw.view(G, N, K)
+    # per-expert scale arrays in the [G][K/128][scale_ld(N)] layout (N is a multiple of 4)
+    sw = sw.view(K // 128, G, N).permute(1, 0, 2).contiguous()
+    blocks = torch.arange(T // 256, device=dev, dtype=torch.int32) // ((T // 256) // G)
+    yg = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    med, _ = timed(lambda: te.te_fp8_mgrouped_gemm_fwd(qx, sx, E4, qw, sw, E4, blocks, bias=bg,
+                                                       epilogue=te.TE_EPI_BIAS | te.TE_EPI_GELU, y=yg,
+                                                       accum=te.TE_ACCUM_FULL_FP32), 10)
+    out["mgrouped_fwd_bias_gelu_full_8x1024x4096x7168"] = {"ms": round(med, 4),
+                                                           "tflops": round(2.0 * T * N * K / med / 1e9, 1)}
     return out
 
 

@@ -36,7 +36,8 @@ TE_EPI_BGRAD = 16
 TE_CAST_POW2_SCALE = 1
 
 EXPORTED = ("te_cast_fp8_per_token", "te_cast_fp8_per_token_transpose", "te_fp8_gemm_fwd", "te_fp8_gemm_dgrad", "te_fp8_wgrad_accum",
-            "te_fp8_kgrouped_wgrad", "te_fp8_kgrouped_wgrad_device_sizes", "te_status_string", "te_last_error_message", "te_scale_ld")
+            "te_fp8_kgrouped_wgrad", "te_fp8_kgrouped_wgrad_device_sizes", "te_fp8_mgrouped_gemm_fwd",
+            "te_status_string", "te_last_error_message", "te_scale_ld")
 
 
 class TeFp8Error(RuntimeError):
@@ -77,6 +78,8 @@ def load_library():
     lib.te_fp8_kgrouped_wgrad.argtypes = [P, P, I, P, P, I, I64, I64, P, I32, P, I, P]
     lib.te_fp8_kgrouped_wgrad_device_sizes.restype = I
     lib.te_fp8_kgrouped_wgrad_device_sizes.argtypes = [P, P, I, P, P, I, I64, I64, I64, P, I32, P, I, P]
+    lib.te_fp8_mgrouped_gemm_fwd.restype = I
+    lib.te_fp8_mgrouped_gemm_fwd.argtypes = [P, P, I, P, P, I, I64, I64, I64, I32, P, P, U32, P, I, I64, P, I64, I, P]
     _lib = lib
     return lib
 
@@ -230,3 +233,27 @@ def te_fp8_kgrouped_wgrad_device_sizes(a, a_scales, a_dtype, b, b_scales, b_dtyp
         _ptr(a), _ptr(a_scales), a_dtype, _ptr(b), _ptr(b_scales), b_dtype, M, N, S, _ptr(group_k), G,
         _ptr(out), accum, _stream(stream)))
     return out
+
+
+def te_fp8_mgrouped_gemm_fwd(x, x_scales, x_dtype, w, w_scales, w_dtype, m_block_group, bias=None,
+                             epilogue=TE_EPI_NONE, y=None, y_dtype=TE_DTYPE_BF16, preact=None, accum=TE_ACCUM_FAST,
+                             stream=None):
+    """y[m] = epi(x[m] w[e]^T (+ bias[e])) for the rows m of every 256-row block whose expert
+    e = m_block_group[block] is in [0, G); w is [G, N, K] fp8 with scales [G, K/128, scale_ld(N)]."""
+    sum_m, K = x.shape
+    G, N, K2 = w.shape
+    assert K2 == K and w.is_contiguous()
+    assert m_block_group.dtype == torch.int32 and m_block_group.is_cuda and m_block_group.is_contiguous()
+    assert m_block_group.numel() * 256 == sum_m
+    want = (G, K // 128, scale_ld(N))
+    if w_scales.dtype != torch.float32 or not w_scales.is_contiguous() or tuple(w_scales.shape) != want:
+        raise TeFp8Error(1, f"w_scales: expected contiguous fp32 scales of shape {want}")
+    _scales_ok(x_scales, sum_m, K, "x_scales")
+    if y is None:
+        y = torch.empty((sum_m, N), dtype=torch.bfloat16 if y_dtype == TE_DTYPE_BF16 else torch.float32,
+                        device=x.device)
+    _check(load_library().te_fp8_mgrouped_gemm_fwd(
+        _ptr(x), _ptr(x_scales), x_dtype, _ptr(w), _ptr(w_scales), w_dtype, sum_m, N, K, G, _ptr(m_block_group),
+        _ptr(bias), epilogue, _ptr(y), y_dtype, y.stride(0),
+        _ptr(preact), preact.stride(0) if preact is not None else 0, accum, _stream(stream)))
+    return y

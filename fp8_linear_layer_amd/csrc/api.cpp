@@ -418,4 +418,59 @@ te_status_t te_fp8_kgrouped_wgrad_device_sizes(const void* a, const float* a_sca
     }
 }
 
+te_status_t te_fp8_mgrouped_gemm_fwd(const void* x, const float* x_scales, te_dtype_t x_dtype,
+                                     const void* w, const float* w_scales, te_dtype_t w_dtype,
+                                     int64_t sum_m, int64_t N, int64_t K, int32_t G, const int32_t* m_block_group,
+                                     const void* bias_bf16, uint32_t epilogue,
+                                     void* y, te_dtype_t y_dtype, int64_t ld_y,
+                                     void* preact_bf16, int64_t ld_preact,
+                                     te_accum_t accum, hipStream_t stream)
+{
+    try {
+        const char* fn = "te_fp8_mgrouped_gemm_fwd";
+        if (!m_block_group) return fail(TE_ERR_INVALID_ARGUMENT, "%s: m_block_group is null", fn);
+        if (!aligned(m_block_group, 4)) return fail(TE_ERR_MISALIGNED, "%s: m_block_group must be 4-byte aligned", fn);
+        if (G < 1 || G > 1024) return fail(TE_ERR_INVALID_ARGUMENT, "%s: G must be in [1, 1024] (got %d)", fn, (int)G);
+        if (sum_m < tefp8::kMGroupRows || sum_m % tefp8::kMGroupRows != 0)
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: sum_m must be a positive multiple of %d (got %lld)", fn,
+                        tefp8::kMGroupRows, (long long)sum_m);
+        te_status_t st = check_operands(fn, x, x_scales, x_dtype, w, w_scales, w_dtype, sum_m, N, K, accum);
+        if (st != TE_OK) return st;
+        const uint32_t allowed = TE_EPI_BIAS | TE_EPI_GELU | TE_EPI_AUX_PREACT;
+        if (epilogue & ~allowed) return fail(TE_ERR_INVALID_ARGUMENT, "%s: epilogue 0x%x has flags other than BIAS|GELU|AUX_PREACT", fn, epilogue);
+        if ((epilogue & TE_EPI_AUX_PREACT) && !(epilogue & TE_EPI_GELU))
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: TE_EPI_AUX_PREACT needs TE_EPI_GELU", fn);
+        if ((epilogue & TE_EPI_BIAS) && !bias_bf16) return fail(TE_ERR_INVALID_ARGUMENT, "%s: TE_EPI_BIAS needs bias_bf16", fn);
+        if (bias_bf16 && !(epilogue & TE_EPI_BIAS)) return fail(TE_ERR_INVALID_ARGUMENT, "%s: bias_bf16 given without TE_EPI_BIAS", fn);
+        if (bias_bf16 && !aligned(bias_bf16, 16)) return fail(TE_ERR_MISALIGNED, "%s: bias must be 16-byte aligned", fn);
+        if ((epilogue & TE_EPI_BIAS) && N % 8 != 0)
+            return fail(TE_ERR_MISALIGNED, "%s: with a bias, N must be a multiple of 8 (each expert's bias row 16-byte aligned)", fn);
+        st = check_output(fn, "y", y, y_dtype, ld_y, N);
+        if (st != TE_OK) return st;
+        if (epilogue & TE_EPI_AUX_PREACT) {
+            st = check_output(fn, "preact", preact_bf16, TE_DTYPE_BF16, ld_preact, N);
+            if (st != TE_OK) return st;
+        } else if (preact_bf16) {
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: preact given without TE_EPI_AUX_PREACT", fn);
+        }
+        tefp8::GemmArgs g = base_args(x, x_scales, x_dtype, w, w_scales, w_dtype, sum_m, N, K, accum);
+        g.epi = tefp8::Epi::Fwd;
+        g.flags = epilogue;
+        g.out = y;
+        g.out_bf16 = y_dtype == TE_DTYPE_BF16;
+        g.ld_out = ld_y;
+        g.bias = static_cast<const uint16_t*>(bias_bf16);
+        g.aux = static_cast<uint16_t*>(preact_bf16);
+        g.ld_aux = ld_preact;
+        g.m_block_group = m_block_group;
+        g.num_b_groups = G;
+        g.b_group_stride = N * K;
+        g.sb_group_stride = (K / 128) * te_scale_ld(N);
+        g.bias_group_stride = N;
+        return launch(fn, g, stream, K, x_dtype, w_dtype, accum, epilogue);
+    } catch (...) {
+        return fail(TE_ERR_INTERNAL, "te_fp8_mgrouped_gemm_fwd: internal error");
+    }
+}
+
 }  // extern "C"

@@ -50,6 +50,9 @@
 //    device memory each tile derives its group's range from them instead
 //    (every group has the same M x N tiles, so the tile -> group mapping needs
 //    no sizes); a tile of an empty group does nothing.
+//  * M-grouped launches (mixture-of-experts forward / data gradient) read the
+//    expert of each 256-row block of A from device memory and take that
+//    expert's B, B scales and bias; a block marked -1 is skipped.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -84,6 +87,7 @@ constexpr int kTN = kWN / 16;                     // 8 B column groups
 constexpr int kOpPerWave = (kBM / 8) / kWaves;    // 1 KiB copies of A (and of B) per wave
 constexpr int kBarrierGroup = kTN - 2;            // the block's barrier precedes this column group
 static_assert(kTM == 4 && kTN == 8 && kWaves * 64 == kBM + kBN, "layout assumed below");
+static_assert(kMGroupRows == kBM, "an M-grouped block is one tile row");
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
@@ -102,13 +106,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
                                              0x00020000);
 }
 
-__device__ __forceinline__ TileSrc tile_src(const GemmArgs& p, int64_t m0, int64_t n0)
+__device__ __forceinline__ TileSrc tile_src(const GemmArgs& p, int64_t m0, int64_t n0, int64_t bgrp)
 {
     TileSrc s;
     s.a = make_rsrc(p.a + m0 * p.lda, min((int64_t)kBM, p.M - m0) * p.lda);
-    s.b = make_rsrc(p.b + n0 * p.ldb, min((int64_t)kBN, p.N - n0) * p.ldb);
+    s.b = make_rsrc(p.b + bgrp * p.b_group_stride + n0 * p.ldb, min((int64_t)kBN, p.N - n0) * p.ldb);
     s.sa = p.sa + m0;
-    s.sb = p.sb + n0;
+    s.sb = p.sb + bgrp * p.sb_group_stride + n0;
     s.sa_bytes = (int)(min((int64_t)kBM, p.lsa - m0) * 4);
     s.sb_bytes = (int)(min((int64_t)kBN, p.lsb - n0) * 4);
     return s;
@@ -473,7 +477,7 @@ __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&v)[8],
 // four lanes cover 64 contiguous bytes of a row.
 template <int kEpi, bool kFull>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM][kTN], int64_t m0, int64_t n0,
-                                         int64_t out_off, int wave, int lane)
+                                         int64_t out_off, const uint16_t* bias_v, int wave, int lane)
 {
     const int wm = wave / kWavesN, wn = wave % kWavesN;
     // (the lane index is re-derived here so that its address arithmetic is not
@@ -678,7 +682,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
     if (kFull && has_bias) {
 #pragma unroll
         for (int jp = 0; jp < kTN / 2; ++jp)
-            bw[jp] = *reinterpret_cast<const uint4*>(p.bias + n0 + wn * kWN + (2 * jp + (q4 & 1)) * 16 + (q4 >> 1) * 8);
+            bw[jp] = *reinterpret_cast<const uint4*>(bias_v + n0 + wn * kWN + (2 * jp + (q4 & 1)) * 16 + (q4 >> 1) * 8);
     }
 #pragma unroll
     for (int jp = 0; jp < kTN / 2; ++jp) {
@@ -689,10 +693,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
             if (kFull) {
                 unpack_bf16x8(bw[jp], bias);
             } else if (full8) {
-                unpack_bf16x8(*reinterpret_cast<const uint4*>(p.bias + n), bias);
+                unpack_bf16x8(*reinterpret_cast<const uint4*>(bias_v + n), bias);
             } else {
 #pragma unroll
-                for (int r = 0; r < 8; ++r) if (n + r < p.N) bias[r] = bf16_to_f32(p.bias[n + r]);
+                for (int r = 0; r < 8; ++r) if (n + r < p.N) bias[r] = bf16_to_f32(bias_v[n + r]);
             }
         }
 #pragma unroll
@@ -736,6 +740,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
 // One output tile: its corner, contraction range and output matrix.
 struct TileCtx {
     int64_t m0, n0, out_off;
+    int64_t bgrp;  // expert of an M-grouped tile (0 otherwise)
     int kb0, nkb;
     TileSrc src;
 };
@@ -774,8 +779,14 @@ __device__ __forceinline__ TileCtx tile_ctx(const GemmArgs& p, int64_t tile)
     c.out_off = (int64_t)grp.out_idx * p.out_group_stride;
     c.kb0 = grp.kb_off;
     c.nkb = grp.kb_len;
-    // an empty group's tile copies nothing and leaves its output untouched
-    c.src = select_src(tile_src(p, c.m0, c.n0), c.nkb > 0);
+    c.bgrp = 0;
+    if (p.m_block_group) {
+        const int32_t e = p.m_block_group[c.m0 / kMGroupRows];
+        if (e >= 0 && e < p.num_b_groups) c.bgrp = e;
+        else c.nkb = 0;
+    }
+    // an empty group's or a skipped block's tile copies nothing and leaves its output untouched
+    c.src = select_src(tile_src(p, c.m0, c.n0, c.bgrp), c.nkb > 0);
     return c;
 }
 
@@ -804,7 +815,8 @@ __device__ __forceinline__ bool row_scales_pow2(const GemmArgs& p, const TileCtx
             v[u] = make_float4(1.f, 1.f, 1.f, 1.f);
             if (left[u] > 0)
                 v[u] = *reinterpret_cast<const float4*>(is_a ? p.sa + (int64_t)kb * p.lsa + c.m0 + r
-                                                             : p.sb + (int64_t)kb * p.lsb + c.n0 + r);
+                                                             : p.sb + c.bgrp * p.sb_group_stride +
+                                                                   (int64_t)kb * p.lsb + c.n0 + r);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -877,10 +889,11 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p, int
         // (a tile inside the matrix takes the copy of the epilogue without
         // bounds checks: straight-line code lets its loads be in flight together)
         if (c.nkb > 0) {
+            const uint16_t* bias_v = p.bias + c.bgrp * p.bias_group_stride;
             if (c.m0 + kBM <= p.M && c.n0 + kBN <= p.N)
-                epilogue<kEpi, true>(p, acc, c.m0, c.n0, c.out_off, wave, lane);
+                epilogue<kEpi, true>(p, acc, c.m0, c.n0, c.out_off, bias_v, wave, lane);
             else
-                epilogue<kEpi, false>(p, acc, c.m0, c.n0, c.out_off, wave, lane);
+                epilogue<kEpi, false>(p, acc, c.m0, c.n0, c.out_off, bias_v, wave, lane);
         }
         if (!more) break;
         // (after the epilogue: the scale reads overlap its stores)

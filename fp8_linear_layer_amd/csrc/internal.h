@@ -26,6 +26,7 @@ struct Group {
 
 constexpr int kMaxGroupsPerLaunch = 128;
 constexpr int kMaxDeviceGroups = 256;  // groups of the device-sized K-grouped call
+constexpr int kMGroupRows = 256;       // rows per block of the M-grouped layout (the GEMM's tile height)
 
 struct GemmArgs {
     const uint8_t* a;      // [M][lda] fp8
@@ -57,6 +58,15 @@ struct GemmArgs {
     // group, in elements) and clamped to the sum_kb blocks of the operands.
     const int64_t* group_k_dev;
     int64_t sum_kb;
+    // M-grouped (mixture-of-experts forward/data gradient): when set, the
+    // 256-row block i of A belongs to expert m_block_group[i] (device memory;
+    // a value outside [0, num_b_groups) skips the block, its output rows are
+    // not written), whose B operand, B scales and bias sit at these strides.
+    const int32_t* m_block_group;
+    int32_t num_b_groups;
+    int64_t b_group_stride;     // bytes
+    int64_t sb_group_stride;    // floats
+    int64_t bias_group_stride;  // elements
 };
 
 struct LaunchInfo {

@@ -295,6 +295,36 @@ te_status_t te_fp8_kgrouped_wgrad_device_sizes(const void* a, const float* a_sca
                                                int64_t M, int64_t N, int64_t sum_k, const int64_t* group_k_device,
                                                int32_t G, float* out, te_accum_t accum, hipStream_t stream);
 
+/*
+ * M-grouped forward GEMM for mixture-of-experts layers (also the data
+ * gradient, with each expert's W^T as w and no epilogue): the tokens are
+ * sorted by expert into blocks of 256 rows (each expert's rows padded to a
+ * multiple of 256), and block i uses expert e = m_block_group[i]:
+ *   y[m][n] = epi( sum_k x[m][k] w[e][n][k] (+ bias[e][n]) ),  m in block i
+ * with the epilogues of te_fp8_gemm_fwd.  A block whose entry is outside
+ * [0, G) (e.g. -1 for padding) is skipped: its rows of y (and preact) are not
+ * written.  The expert of each block is read from device memory when the
+ * kernel runs (no host synchronisation).  The pages' grouped GEMMs are the
+ * K-grouped weight gradient; this is its forward/data-gradient counterpart
+ * over the same per-expert token layout.
+ *
+ *  x, x_scales     [sum_m][K] fp8, [K/128][te_scale_ld(sum_m)]
+ *  w, w_scales     [G][N][K] fp8, [G][K/128][te_scale_ld(N)] (each expert's
+ *                  operand and scales as te_fp8_gemm_fwd takes them)
+ *  sum_m           >= 256, a multiple of 256;  N >= 1;  K as te_fp8_gemm_fwd
+ *  G               1 .. 1024
+ *  m_block_group   DEVICE array of sum_m/256 int32 (4-byte aligned)
+ *  bias_bf16       [G][N] bf16, required iff TE_EPI_BIAS (then N % 8 == 0)
+ *  y, preact_bf16  as te_fp8_gemm_fwd, [sum_m][ld]
+ */
+te_status_t te_fp8_mgrouped_gemm_fwd(const void* x, const float* x_scales, te_dtype_t x_dtype,
+                                     const void* w, const float* w_scales, te_dtype_t w_dtype,
+                                     int64_t sum_m, int64_t N, int64_t K, int32_t G, const int32_t* m_block_group,
+                                     const void* bias_bf16, uint32_t epilogue,
+                                     void* y, te_dtype_t y_dtype, int64_t ld_y,
+                                     void* preact_bf16, int64_t ld_preact,
+                                     te_accum_t accum, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* te_status_string(te_status_t status);
 

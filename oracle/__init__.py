@@ -192,6 +192,24 @@ def fwd_epilogue(o, d, bias_bits=None, gelu_on: bool = False):
     return y, z, zmag
 
 
+def mgrouped_fwd(qx, sx, fx, qw, sw, fw, m_block_group, bias_bits=None, gelu_on: bool = False, block: int = 256):
+    """The M-grouped forward by definition: every `block`-row slice of x whose expert e =
+    m_block_group[i] is in [0, G) goes through gemm_nt with w[e] and fwd_epilogue with bias[e]
+    (expert weights qw [G, N, K], row-major scales sw [G, N, K/128]).  Returns (y, z, zmag) with
+    NaN in the rows of skipped blocks."""
+    qx = _c(qx, np.uint8); sx = _c(sx, np.float32)
+    G, N, _ = qw.shape
+    M = qx.shape[0]
+    y = np.full((M, N), np.nan); z = np.full((M, N), np.nan); zm = np.full((M, N), np.nan)
+    for i, e in enumerate(np.asarray(m_block_group)):
+        if not 0 <= e < G:
+            continue
+        r = slice(i * block, (i + 1) * block)
+        o, d = gemm_nt(qx[r], sx[r], fx, qw[e], sw[e], fw)
+        y[r], z[r], zm[r] = fwd_epilogue(o, d, None if bias_bits is None else bias_bits[e], gelu_on)
+    return y, z, zm
+
+
 def dgrad_epilogue(o, d, preact_bits=None, bgrad: bool = False):
     """D = o * GELU'(z) (if preact given); db = column sums of D.  Returns (D, Dmag, db, dbmag)."""
     o = _c(o, np.float64); d = _c(d, np.float64)

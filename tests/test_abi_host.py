@@ -150,6 +150,25 @@ def kgrouped_dev(lib, gk=GK, G=4, sum_k=512, M=256, N=256, out=O, accum=1):
                                                   accum, None)
 
 
+MB = 0xA0000  # dummy device address of the per-block experts
+
+
+def mgrouped(lib, mb=MB, G=4, sum_m=512, N=256, K=256, bias=0, epi=0, y=O, ydt=4, ldy=256, pre=0, ldpre=0, accum=2):
+    return lib.te_fp8_mgrouped_gemm_fwd(p(A), p(S), 1, p(B), p(S), 1, sum_m, N, K, G, p(mb), p(bias), epi, p(y), ydt,
+                                        ldy, p(pre), ldpre, accum, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mb=0), INV), (dict(mb=MB + 2), MISAL), (dict(G=0), INV), (dict(G=1025), INV), (dict(sum_m=0), INV),
+    (dict(sum_m=300), INV), (dict(K=100), INV), (dict(epi=8), INV), (dict(epi=4), INV), (dict(epi=1), INV),
+    (dict(bias=BIAS), INV), (dict(epi=1, bias=BIAS, N=250, ldy=252), MISAL), (dict(epi=1, bias=BIAS + 8), MISAL),
+    (dict(y=0), INV), (dict(ydt=1), INV), (dict(ldy=128), INV), (dict(pre=Z, ldpre=256), INV),
+    (dict(epi=6, pre=0), INV), (dict(accum=0), INV),
+])
+def test_mgrouped_rejects(lib, kw, status):
+    assert mgrouped(lib, **kw) == status
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(gk=0), INV), (dict(G=0), INV), (dict(G=257), INV), (dict(sum_k=0), INV), (dict(sum_k=200), INV),
     (dict(M=0), INV), (dict(out=0), INV), (dict(accum=0), INV), (dict(gk=GK + 4), MISAL),

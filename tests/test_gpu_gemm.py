@@ -272,6 +272,86 @@ def test_dgrad_workload_dgelu_bgrad():
     check_f32(host(bg).numpy()[bcols], db, dbm, "bias grad")
 
 
+# ------------------------------------------------------------------ M-grouped
+def mgrouped_case(seed, G, blocks, N, K, pow2=False, fx=E4, wstd=0.05):
+    sum_m = 256 * len(blocks)
+    qx, sx = operand(seed, sum_m, K, fx, pow2=pow2)
+    ws = [operand(seed + 1 + e, N, K, E4, std=wstd, pow2=pow2) for e in range(G)]
+    qw = np.stack([w[0] for w in ws])
+    sw = np.stack([w[1] for w in ws])
+    b = W.normal_bf16(np.random.SeedSequence(seed + 100), (G, N), 0.1)
+    return qx, sx, qw, sw, b
+
+
+def w_dev(qw, sw):
+    """Expert operands and scales in the layout the M-grouped call takes."""
+    return dev(qw), torch.stack([sdev(sw[e]) for e in range(sw.shape[0])]).contiguous()
+
+
+@pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
+@pytest.mark.parametrize("epi,ydt", [(te.TE_EPI_NONE, te.TE_DTYPE_F32),
+                                     (te.TE_EPI_BIAS | te.TE_EPI_GELU, te.TE_DTYPE_F32),
+                                     (te.TE_EPI_BIAS | te.TE_EPI_GELU | te.TE_EPI_AUX_PREACT, te.TE_DTYPE_BF16)])
+def test_mgrouped_fwd(accum, pow2, epi, ydt):
+    """Blocks of 256 token rows, each with its expert (or -1: skipped, rows untouched); N ragged."""
+    blocks = np.array([2, 0, -1, 2, 1], np.int32)
+    G, N, K = 3, 200, 384
+    qx, sx, qw, sw, b = mgrouped_case(70, G, blocks, N, K, pow2)
+    y, z, zmag = oracle.mgrouped_fwd(qx, sx, oracle.E4M3, qw, sw, oracle.E4M3, blocks,
+                                     b if epi & te.TE_EPI_BIAS else None, bool(epi & te.TE_EPI_GELU))
+    tdt = torch.float32 if ydt == te.TE_DTYPE_F32 else torch.bfloat16
+    M = 256 * len(blocks)
+    ybuf = torch.full((M, N + 8), 77.0, dtype=tdt, device="cuda")
+    pre = None
+    if epi & te.TE_EPI_AUX_PREACT:
+        prebuf = torch.full((M, N + 8), 55.0, dtype=torch.bfloat16, device="cuda")
+        pre = prebuf[:, :N]
+    wq, ws = w_dev(qw, sw)
+    te.te_fp8_mgrouped_gemm_fwd(dev(qx), sdev(sx), E4, wq, ws, E4, torch.from_numpy(blocks).cuda(),
+                                bias=bf16_dev(b) if epi & te.TE_EPI_BIAS else None, epilogue=epi,
+                                y=ybuf[:, :N], y_dtype=ydt, preact=pre, accum=accum)
+    torch.cuda.synchronize()
+    yb = host(ybuf)
+    assert torch.all(yb[:, N:] == 77.0), "wrote past N"
+    live = np.repeat(blocks >= 0, 256)
+    assert torch.all(yb[torch.from_numpy(~live)] == 77.0), "a skipped block was written"
+    ymag = zmag * (GELU_LIP if epi & te.TE_EPI_GELU else 1.0)
+    if ydt == te.TE_DTYPE_F32:
+        check_f32(yb[:, :N].numpy()[live], y[live], ymag[live], "mgrouped y")
+    else:
+        check_bf16(bf16_host_f64(yb[:, :N])[live], y[live], ymag[live], "mgrouped y")
+    if pre is not None:
+        pb = host(prebuf)
+        assert torch.all(pb[torch.from_numpy(~live)] == 55.0)
+        check_bf16(bf16_host_f64(pb[:, :N])[live], z[live], zmag[live], "mgrouped preact")
+
+
+def test_mgrouped_dgrad_form_e5m2():
+    """The data gradient of an expert layer: dY (e5m2) blocks times each expert's W^T, no epilogue, bf16."""
+    blocks = np.array([1, 1, 0, 3, -1, 2], np.int32)
+    G, N, K = 4, 512, 640
+    qx, sx, qw, sw, _ = mgrouped_case(80, G, blocks, N, K, fx=te.TE_DTYPE_E5M2)
+    y, _, zmag = oracle.mgrouped_fwd(qx, sx, oracle.E5M2, qw, sw, oracle.E4M3, blocks)
+    wq, ws = w_dev(qw, sw)
+    yg = te.te_fp8_mgrouped_gemm_fwd(dev(qx), sdev(sx), te.TE_DTYPE_E5M2, wq, ws, E4,
+                                     torch.from_numpy(blocks).cuda(), y_dtype=te.TE_DTYPE_BF16, accum=FULL)
+    live = np.repeat(blocks >= 0, 256)
+    check_bf16(bf16_host_f64(yg)[live], y[live], zmag[live], "mgrouped dX")
+
+
+def test_mgrouped_same_expert_equals_dense():
+    """With every block on one expert the call is the dense forward GEMM, bit for bit."""
+    blocks = np.zeros(4, np.int32)
+    qx, sx, qw, sw, b = mgrouped_case(90, 1, blocks, 384, 512)
+    epi = te.TE_EPI_BIAS | te.TE_EPI_GELU
+    wq, ws = w_dev(qw, sw)
+    yg = te.te_fp8_mgrouped_gemm_fwd(dev(qx), sdev(sx), E4, wq, ws, E4, torch.from_numpy(blocks).cuda(),
+                                     bias=bf16_dev(b), epilogue=epi, y_dtype=te.TE_DTYPE_F32, accum=FULL)
+    yd = te.te_fp8_gemm_fwd(dev(qx), sdev(sx), E4, dev(qw[0]), sdev(sw[0]), E4, bias=bf16_dev(b[0]), epilogue=epi,
+                            y_dtype=te.TE_DTYPE_F32, accum=FULL)
+    assert torch.equal(host(yg).view(torch.int32), host(yd).view(torch.int32))
+
+
 # ------------------------------------------------------------------ K-grouped
 @pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
 def test_kgrouped_small(accum, pow2):
