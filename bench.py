@@ -11,7 +11,7 @@ the GEMM kernel's roofline fraction against the FP8 dense matrix-core peak
 (kernel time from HIP events on the launch stream), the oracle's CPU
 throughput on a bounded sample, and per-kernel timings of the other
 workloads (fprop with bias+GELU at 8192 x 14336 x 4096 in both accumulation
-policies, the fused cast + cast-transpose of the activation, dgrad at
+policies and with the quantising store, the fused cast + cast-transpose of the activation, dgrad at
 8192 x 4096 x 14336 and its dGELU+bias-grad form, the e5m2 cast of the
 gradient, the dense weight gradient fed from token-major sources through
 the cast-transpose, the 8-expert K-grouped wgrad with its group sizes on
@@ -130,6 +130,15 @@ def breakdown(te, torch):
                                         accum=acc)
         med, mn = timed(fn, 10)
         out[name] = {"shape": [M, N, K], "ms": round(med, 4), "tflops": round(flop / med / 1e9, 1)}
+    # the same forward storing its per-token e4m3 cast (the next layer's operand) instead of bf16 y
+    qy = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    qys = torch.empty((N // 128, te.scale_ld(M)), dtype=torch.float32, device=dev)
+    med, _ = timed(lambda: te.te_fp8_gemm_fwd_quant(px, psx, E4, pw, psw, E4, bias=b,
+                                                    epilogue=te.TE_EPI_BIAS | te.TE_EPI_GELU, q=qy, q_scales=qys,
+                                                    accum=te.TE_ACCUM_FAST), 10)
+    out["fprop_bias_gelu_quant_e4m3_fast_pow2"] = {"shape": [M, N, K], "ms": round(med, 4),
+                                                   "tflops": round(flop / med / 1e9, 1)}
+    del qy, qys
     cast_bytes = M * K * 2 + M * K + M * (K // 128) * 4
     med, _ = timed(lambda: te.te_cast_fp8_per_token(x, E4, q=qx, scales=sx), 10)
     out["cast_e4m3_8192x4096"] = {"ms": round(med, 4), "gbs": round(cast_bytes / med / 1e6, 1),

@@ -35,7 +35,7 @@ TE_EPI_BGRAD = 16
 # cast flags
 TE_CAST_POW2_SCALE = 1
 
-EXPORTED = ("te_cast_fp8_per_token", "te_cast_fp8_per_token_transpose", "te_fp8_gemm_fwd", "te_fp8_gemm_dgrad", "te_fp8_wgrad_accum",
+EXPORTED = ("te_cast_fp8_per_token", "te_cast_fp8_per_token_transpose", "te_fp8_gemm_fwd", "te_fp8_gemm_fwd_quant", "te_fp8_gemm_dgrad", "te_fp8_wgrad_accum",
             "te_fp8_kgrouped_wgrad", "te_fp8_kgrouped_wgrad_device_sizes", "te_fp8_mgrouped_gemm_fwd",
             "te_status_string", "te_last_error_message", "te_scale_ld")
 
@@ -70,6 +70,8 @@ def load_library():
     lib.te_cast_fp8_per_token_transpose.argtypes = [P, I64, I64, I64, I, U32, P, I64, P, P, I64, P, P]
     lib.te_fp8_gemm_fwd.restype = I
     lib.te_fp8_gemm_fwd.argtypes = [P, P, I, P, P, I, I64, I64, I64, P, U32, P, I, I64, P, I64, I, P]
+    lib.te_fp8_gemm_fwd_quant.restype = I
+    lib.te_fp8_gemm_fwd_quant.argtypes = [P, P, I, P, P, I, I64, I64, I64, P, U32, I, U32, P, I64, P, P, I64, I, P]
     lib.te_fp8_gemm_dgrad.restype = I
     lib.te_fp8_gemm_dgrad.argtypes = [P, P, I, P, P, I, I64, I64, I64, U32, P, I64, P, P, I, I64, I, P]
     lib.te_fp8_wgrad_accum.restype = I
@@ -174,6 +176,26 @@ def te_fp8_gemm_fwd(x, x_scales, x_dtype, w, w_scales, w_dtype, bias=None, epilo
         _ptr(bias), epilogue, _ptr(y), y_dtype, y.stride(0),
         _ptr(preact), preact.stride(0) if preact is not None else 0, accum, _stream(stream)))
     return y
+
+
+def te_fp8_gemm_fwd_quant(x, x_scales, x_dtype, w, w_scales, w_dtype, bias=None, epilogue=TE_EPI_NONE,
+                          q_dtype=TE_DTYPE_E4M3, cast_flags=0, q=None, q_scales=None, preact=None,
+                          accum=TE_ACCUM_FAST, stream=None):
+    """The forward GEMM whose fp32 result is stored as its per-token cast: returns (q, q_scales)."""
+    M, K = x.shape
+    N = w.shape[0]
+    _scales_ok(x_scales, M, K, "x_scales")
+    _scales_ok(w_scales, N, K, "w_scales")
+    if q is None:
+        q = torch.empty((M, N), dtype=torch.uint8, device=x.device)
+    if q_scales is None:
+        q_scales = torch.empty((N // 128, scale_ld(M)), dtype=torch.float32, device=x.device)
+    _scales_ok(q_scales, M, N, "q_scales")
+    _check(load_library().te_fp8_gemm_fwd_quant(
+        _ptr(x), _ptr(x_scales), x_dtype, _ptr(w), _ptr(w_scales), w_dtype, M, N, K,
+        _ptr(bias), epilogue, q_dtype, cast_flags, _ptr(q), q.stride(0), _ptr(q_scales),
+        _ptr(preact), preact.stride(0) if preact is not None else 0, accum, _stream(stream)))
+    return q, q_scales
 
 
 def te_fp8_gemm_dgrad(dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, epilogue=TE_EPI_NONE, preact=None,

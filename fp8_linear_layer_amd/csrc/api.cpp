@@ -473,4 +473,54 @@ te_status_t te_fp8_mgrouped_gemm_fwd(const void* x, const float* x_scales, te_dt
     }
 }
 
+te_status_t te_fp8_gemm_fwd_quant(const void* x, const float* x_scales, te_dtype_t x_dtype,
+                                  const void* w, const float* w_scales, te_dtype_t w_dtype,
+                                  int64_t M, int64_t N, int64_t K,
+                                  const void* bias_bf16, uint32_t epilogue,
+                                  te_dtype_t q_dtype, uint32_t cast_flags, void* q, int64_t ld_q, float* q_scales,
+                                  void* preact_bf16, int64_t ld_preact,
+                                  te_accum_t accum, hipStream_t stream)
+{
+    try {
+        const char* fn = "te_fp8_gemm_fwd_quant";
+        te_status_t st = check_operands(fn, x, x_scales, x_dtype, w, w_scales, w_dtype, M, N, K, accum);
+        if (st != TE_OK) return st;
+        if (N % 128 != 0) return fail(TE_ERR_INVALID_ARGUMENT, "%s: N must be a multiple of 128 (whole 1x128 groups; got %lld)", fn, (long long)N);
+        const uint32_t allowed = TE_EPI_BIAS | TE_EPI_GELU | TE_EPI_AUX_PREACT;
+        if (epilogue & ~allowed) return fail(TE_ERR_INVALID_ARGUMENT, "%s: epilogue flags 0x%x are not forward flags", fn, epilogue);
+        if ((epilogue & TE_EPI_AUX_PREACT) && !(epilogue & TE_EPI_GELU))
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: TE_EPI_AUX_PREACT requires TE_EPI_GELU", fn);
+        if ((epilogue & TE_EPI_BIAS) && !bias_bf16) return fail(TE_ERR_INVALID_ARGUMENT, "%s: TE_EPI_BIAS needs bias_bf16", fn);
+        if (bias_bf16 && !(epilogue & TE_EPI_BIAS)) return fail(TE_ERR_INVALID_ARGUMENT, "%s: bias_bf16 given without TE_EPI_BIAS", fn);
+        if (bias_bf16 && !aligned(bias_bf16, 16)) return fail(TE_ERR_MISALIGNED, "%s: bias must be 16-byte aligned", fn);
+        if (!is_fp8(q_dtype)) return fail(TE_ERR_INVALID_ARGUMENT, "%s: q_dtype must be TE_DTYPE_E4M3 or TE_DTYPE_E5M2 (got %d)", fn, (int)q_dtype);
+        if (cast_flags & ~(uint32_t)TE_CAST_POW2_SCALE) return fail(TE_ERR_INVALID_ARGUMENT, "%s: unknown cast flag bits 0x%x", fn, cast_flags);
+        if (!q || !q_scales) return fail(TE_ERR_INVALID_ARGUMENT, "%s: q and q_scales are required", fn);
+        if (ld_q < N) return fail(TE_ERR_INVALID_ARGUMENT, "%s: ld_q must be >= N", fn);
+        if (!aligned(q, 16) || ld_q % 16 != 0) return fail(TE_ERR_MISALIGNED, "%s: q must be 16-byte aligned with ld_q a multiple of 16", fn);
+        if (!aligned(q_scales, 16)) return fail(TE_ERR_MISALIGNED, "%s: q_scales must be 16-byte aligned", fn);
+        if (epilogue & TE_EPI_AUX_PREACT) {
+            st = check_output(fn, "preact", preact_bf16, TE_DTYPE_BF16, ld_preact, N);
+            if (st != TE_OK) return st;
+        } else if (preact_bf16) {
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: preact given without TE_EPI_AUX_PREACT", fn);
+        }
+        tefp8::GemmArgs g = base_args(x, x_scales, x_dtype, w, w_scales, w_dtype, M, N, K, accum);
+        g.epi = tefp8::Epi::Fwd;
+        g.flags = epilogue;
+        g.bias = static_cast<const uint16_t*>(bias_bf16);
+        g.aux = static_cast<uint16_t*>(preact_bf16);
+        g.ld_aux = ld_preact;
+        g.q_out = static_cast<uint8_t*>(q);
+        g.q_scales = q_scales;
+        g.ld_q = ld_q;
+        g.ld_qs = te_scale_ld(M);
+        g.q_fmt = to_fmt(q_dtype);
+        g.q_pow2 = (cast_flags & TE_CAST_POW2_SCALE) ? 1 : 0;
+        return launch(fn, g, stream, K, x_dtype, w_dtype, accum, epilogue);
+    } catch (...) {
+        return fail(TE_ERR_INTERNAL, "te_fp8_gemm_fwd_quant: internal error");
+    }
+}
+
 }  // extern "C"

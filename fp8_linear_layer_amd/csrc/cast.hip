@@ -35,6 +35,7 @@
 
 #include <algorithm>
 
+#include "fp8_codec.h"
 #include "internal.h"
 
 namespace tefp8 {
@@ -60,59 +61,14 @@ __device__ __forceinline__ float max_with_dpp(float v)
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
-// Eight fp32 values (already scaled) -> eight fp8 codes in two dwords.
-template <int kFmt>
-__device__ __forceinline__ uint2 encode8(const float (&v)[8], float fmax)
-{
-    uint32_t w[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        float a = __builtin_amdgcn_fmed3f(v[4 * h + 0], -fmax, fmax);
-        float b = __builtin_amdgcn_fmed3f(v[4 * h + 1], -fmax, fmax);
-        float c = __builtin_amdgcn_fmed3f(v[4 * h + 2], -fmax, fmax);
-        float d = __builtin_amdgcn_fmed3f(v[4 * h + 3], -fmax, fmax);
-        int p;
-        if (kFmt == FMT_E4M3) {
-            p = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-            p = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, p, true);
-        } else {
-            p = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
-            p = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, p, true);
-        }
-        w[h] = (uint32_t)p;
-    }
-    return make_uint2(w[0], w[1]);
-}
-
 constexpr int kTileRows = 32;   // 4 waves x 8 rows
 constexpr int kTileGroups = 4;  // 128-column groups per tile
-
-template <int kFmt, bool kPow2>
-__device__ __forceinline__ void group_scale(float amax, float& scale, float& mult)
-{
-    // FP8_MAX = 1.75 * 2^kMaxExp for both formats (448 and 57344).
-    constexpr int kMaxExp = kFmt == FMT_E4M3 ? 8 : 15;
-    const float fmax = kFmt == FMT_E4M3 ? 448.0f : 57344.0f;
-    const float amax_c = fmaxf(amax, 0x1p-100f);
-    if (kPow2) {
-        // smallest j with 1.75 * 2^(kMaxExp + j) >= amax_c, from amax_c's bits
-        const uint32_t bits = __builtin_bit_cast(uint32_t, amax_c);
-        const int e = (int)(bits >> 23) - 127;
-        const int j = e - kMaxExp + ((bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
-        scale = __builtin_bit_cast(float, (uint32_t)(j + 127) << 23);
-        mult = __builtin_bit_cast(float, (uint32_t)(127 - j) << 23);
-    } else {
-        scale = amax_c / fmax;  // IEEE-rounded divisions (no fast-math)
-        mult = fmax / amax_c;
-    }
-}
 
 template <int kFmt, bool kPow2>
 __global__ __launch_bounds__(kThreads) void cast_per_token_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t groups_per_row, int64_t tiles_c, int64_t ld_x,
     uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scales, int64_t ld_s)
 {
-    const float fmax = kFmt == FMT_E4M3 ? 448.0f : 57344.0f;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -160,8 +116,8 @@ __global__ __launch_bounds__(kThreads) void cast_per_token_kernel(
             s0[i] = v[i] * mult;
             s1[i] = v[8 + i] * mult;
         }
-        const uint2 c0 = encode8<kFmt>(s0, fmax);
-        const uint2 c1 = encode8<kFmt>(s1, fmax);
+        const uint2 c0 = encode8<kFmt>(s0);
+        const uint2 c1 = encode8<kFmt>(s1);
         const int64_t gc = g0 + t;
         if (row_ok && gc < groups_per_row) {
             *reinterpret_cast<uint4*>(q + row * ld_q + gc * 128 + part * 16) = make_uint4(c0.x, c0.y, c1.x, c1.y);
@@ -202,7 +158,6 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(
     int64_t ld_qt, float* __restrict__ scales_t, int64_t ld_st)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tile[kCT * kCT * 2];
-    const float fmax = kFmt == FMT_E4M3 ? 448.0f : 57344.0f;
     const int t = threadIdx.x;
     const int cc = t & 15;
 
@@ -246,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(
                 group_scale<kFmt, kPow2>(amax, scale, mult);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) f[i] *= mult;
-                const uint2 c = encode8<kFmt>(f, fmax);
+                const uint2 c = encode8<kFmt>(f);
                 *reinterpret_cast<uint2*>(q + (r0 + r) * ld_q + c0 + cc * 8) = c;
                 if (cc == 0) scales[(c0 / kCT) * ld_s + r0 + r] = scale;
             }
@@ -280,8 +235,8 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(
                 s0[i] = f[i] * mult;
                 s1[i] = f[8 + i] * mult;
             }
-            const uint2 e0 = encode8<kFmt>(s0, fmax);
-            const uint2 e1 = encode8<kFmt>(s1, fmax);
+            const uint2 e0 = encode8<kFmt>(s0);
+            const uint2 e1 = encode8<kFmt>(s1);
             if (c0 + col < cols) {
                 *reinterpret_cast<uint4*>(qt + (c0 + col) * ld_qt + r0 + part * 16) = make_uint4(e0.x, e0.y, e1.x, e1.y);
                 if (part == 0) scales_t[(r0 / kCT) * ld_st + c0 + col] = scale;

@@ -58,6 +58,7 @@
 
 #include <algorithm>
 
+#include "fp8_codec.h"
 #include "internal.h"
 #include "te_fp8.h"
 
@@ -259,6 +260,24 @@ __device__ __forceinline__ float dgelu(float z)
     const float one_minus_s = e * s;
     const float z2 = z * z;
     return fmaf(2.0f * kGeluC * z * s * one_minus_s, fmaf(3.0f * kGeluA, z2, 1.0f), s);
+}
+
+// The cast's group scale and encoding with the format and power-of-two flag
+// chosen at run time (the quantising epilogue; uniform branches).
+__device__ __forceinline__ void quant_scale(int fmt, int pow2, float amax, float& scale, float& mult)
+{
+    if (fmt == FMT_E4M3) {
+        if (pow2) group_scale<FMT_E4M3, true>(amax, scale, mult);
+        else group_scale<FMT_E4M3, false>(amax, scale, mult);
+    } else {
+        if (pow2) group_scale<FMT_E5M2, true>(amax, scale, mult);
+        else group_scale<FMT_E5M2, false>(amax, scale, mult);
+    }
+}
+
+__device__ __forceinline__ uint2 quant_encode8(int fmt, const float (&t)[8])
+{
+    return fmt == FMT_E4M3 ? encode8<FMT_E4M3>(t) : encode8<FMT_E5M2>(t);
 }
 
 // The block barrier: this wave's copies have landed and its LDS reads are
@@ -679,6 +698,70 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
     const bool has_gelu = (p.flags & TE_EPI_GELU) != 0;
     const bool has_aux = (p.flags & TE_EPI_AUX_PREACT) != 0;
     uint4 bw[kTN / 2];
+
+    if (p.q_out) {
+        // Quantising store.  A wave's 128 columns are one 1x128 group of each
+        // of its rows (N is a multiple of 128, tile corners of 256), so a
+        // group is wholly inside or outside the matrix, and a row's amax is
+        // the max over the lane's 32 values and the 4 lanes sharing r16.
+        const int64_t ng = n0 + wn * kWN;
+        const bool group_in = kFull || ng < p.N;
+#pragma unroll
+        for (int jp = 0; jp < kTN / 2; ++jp) {
+            bw[jp] = make_uint4(0u, 0u, 0u, 0u);
+            if (has_bias && group_in)
+                bw[jp] = *reinterpret_cast<const uint4*>(bias_v + ng + (2 * jp + (q4 & 1)) * 16 + (q4 >> 1) * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < kTM; ++i) {
+            const int64_t m = m0 + wm * kWM + i * 16 + r16;
+            const bool live = group_in && (kFull || m < p.M);
+            float v[kTN / 2][8];
+#pragma unroll
+            for (int jp = 0; jp < kTN / 2; ++jp) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const auto sw = __builtin_amdgcn_permlane16_swap(
+                        __float_as_uint(acc[i][2 * jp][c]), __float_as_uint(acc[i][2 * jp + 1][c]), false, false);
+                    v[jp][c] = __uint_as_float(sw[0]);
+                    v[jp][4 + c] = __uint_as_float(sw[1]);
+                }
+                const int64_t n = ng + (2 * jp + (q4 & 1)) * 16 + (q4 >> 1) * 8;
+                if (has_bias) {
+                    float b8[8];
+                    unpack_bf16x8(bw[jp], b8);
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) v[jp][r] += b8[r];
+                }
+                if (has_aux && live) store_bf16x8(p.aux + m * p.ld_aux + n, v[jp], true, 8);
+                if (has_gelu) {
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) v[jp][r] = gelu(v[jp][r]);
+                }
+            }
+            float amax = 0.0f;
+#pragma unroll
+            for (int jp = 0; jp < kTN / 2; ++jp)
+#pragma unroll
+                for (int r = 0; r < 8; ++r) amax = fmaxf(amax, fabsf(v[jp][r]));
+            amax = fmaxf(amax, __shfl_xor(amax, 16));
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            float scale, mult;
+            quant_scale(p.q_fmt, p.q_pow2, amax, scale, mult);
+#pragma unroll
+            for (int jp = 0; jp < kTN / 2; ++jp) {
+                float t[8];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) t[r] = v[jp][r] * mult;
+                const uint2 c = quant_encode8(p.q_fmt, t);
+                const int64_t n = ng + (2 * jp + (q4 & 1)) * 16 + (q4 >> 1) * 8;
+                if (live) *reinterpret_cast<uint2*>(p.q_out + m * p.ld_q + n) = c;
+            }
+            if (live && q4 == 0) p.q_scales[(ng / 128) * p.ld_qs + m] = scale;
+        }
+        return;
+    }
+
     if (kFull && has_bias) {
 #pragma unroll
         for (int jp = 0; jp < kTN / 2; ++jp)

@@ -67,6 +67,14 @@ struct GemmArgs {
     int64_t b_group_stride;     // bytes
     int64_t sb_group_stride;    // floats
     int64_t bias_group_stride;  // elements
+    // Quantising forward store: when q_out is set the forward epilogue writes
+    // the per-token cast of its fp32 result (groups of 128 columns) instead
+    // of y: codes [M][ld_q], scales block-major [N/128][ld_qs].
+    uint8_t* q_out;
+    float* q_scales;
+    int64_t ld_q, ld_qs;
+    int q_fmt;
+    int q_pow2;
 };
 
 struct LaunchInfo {

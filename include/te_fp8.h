@@ -211,6 +211,29 @@ te_status_t te_fp8_gemm_fwd(const void* x, const float* x_scales, te_dtype_t x_d
                             te_accum_t accum, hipStream_t stream);
 
 /*
+ * The forward GEMM with a quantising store: the fp32 result of the forward
+ * epilogue (the y of te_fp8_gemm_fwd before any rounding) is written as the
+ * per-token cast the next FP8 Linear layer consumes, with no bf16 round trip
+ * and no separate cast (the DeepGEMM weight-gradient page counts the unfused
+ * casts around its kernel among the end-to-end costs):
+ *   (q, q_scales) = te_cast_fp8_per_token applied to y[M][N] in fp32
+ * i.e. 1x128 groups along N, the same scale and rounding rules, with
+ * q_dtype and cast_flags (0 or TE_CAST_POW2_SCALE) as the cast takes them.
+ * preact (TE_EPI_AUX_PREACT) is stored as in te_fp8_gemm_fwd.
+ *
+ *  x, w, bias, epilogue, preact, accum   as te_fp8_gemm_fwd;  N % 128 == 0
+ *  q         [M][ld_q] bytes, ld_q >= N, ld_q % 16 == 0
+ *  q_scales  [N/128][te_scale_ld(M)] fp32 (block-major); padding untouched
+ */
+te_status_t te_fp8_gemm_fwd_quant(const void* x, const float* x_scales, te_dtype_t x_dtype,
+                                  const void* w, const float* w_scales, te_dtype_t w_dtype,
+                                  int64_t M, int64_t N, int64_t K,
+                                  const void* bias_bf16, uint32_t epilogue,
+                                  te_dtype_t q_dtype, uint32_t cast_flags, void* q, int64_t ld_q, float* q_scales,
+                                  void* preact_bf16, int64_t ld_preact,
+                                  te_accum_t accum, hipStream_t stream);
+
+/*
  * Data-gradient GEMM of a Linear layer with its backward epilogues
  * (dX = dY * W, and for the layer before a GELU, the gradient through it):
  *   acc[m][n] = sum_k dy[m][k] wt[n][k]

@@ -55,6 +55,8 @@ def _load():
     lib.oracle_fp8_encode_array.argtypes = [P, I64, I, P]
     lib.oracle_cast_per_token.restype = I
     lib.oracle_cast_per_token.argtypes = [P, I64, I64, I64, I, I, P, I64, P]
+    lib.oracle_cast_per_token_f32.restype = I
+    lib.oracle_cast_per_token_f32.argtypes = [P, I64, I64, I64, I, I, P, I64, P]
     lib.oracle_gemm_nt.argtypes = [P, P, I, I64, I64, P, P, I, I64, I64, I64, I64, I64, I64, P, P]
     lib.oracle_gemm_nt_entries.argtypes = [P, P, I, I64, I64, P, P, I, I64, I64, I64, I64,
                                            P, P, I64, P, P]
@@ -122,6 +124,21 @@ def cast_per_token(x_bf16_bits, fmt: int, pow2: bool = False):
     q = np.empty((rows, cols), np.uint8)
     s = np.empty((rows, cols // 128), np.float32)
     rc = _load().oracle_cast_per_token(_p(x), rows, cols, cols, fmt, int(bool(pow2)), _p(q), cols, _p(s))
+    if rc != 0:
+        raise ValueError("non-finite input to the per-token cast")
+    return q, s
+
+
+def cast_per_token_f32(x, fmt: int, pow2: bool = False):
+    """The per-token cast of an fp32 [rows, cols] array (the same fp32 operations as
+    cast_per_token, on values that need not be bf16).  Returns (q, s), s row-major."""
+    x = _c(x, np.float32)
+    rows, cols = x.shape
+    if cols % 128:
+        raise ValueError("cols must be a multiple of 128")
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((rows, cols // 128), np.float32)
+    rc = _load().oracle_cast_per_token_f32(_p(x), rows, cols, cols, fmt, int(bool(pow2)), _p(q), cols, _p(s))
     if rc != 0:
         raise ValueError("non-finite input to the per-token cast")
     return q, s

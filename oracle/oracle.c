@@ -137,6 +137,38 @@ static int pow2_exponent(float a, double fmax)
 }
 
 /*
+ * One 128-element group of the per-token cast, from fp32 values: amax,
+ * amax_c = max(amax, 2^-100), the dequantisation scale fl32(amax_c / FP8_MAX)
+ * (or the power of two 2^j, j smallest with FP8_MAX 2^j >= amax_c) and the
+ * codes enc(fl32(v * fl32(FP8_MAX / amax_c))) (or enc(v * 2^-j)).  Returns
+ * the scale; *bad is set for a non-finite input.
+ */
+static float cast_group(const float* v, int fmt, int pow2, uint8_t* q, int* bad)
+{
+    const float fmax = (float)oracle_fp8_max(fmt);
+    float amax = 0.0f;
+    for (int i = 0; i < 128; ++i) {
+        if (!isfinite(v[i])) *bad = 1;
+        if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+    }
+    float amax_c = amax > 0x1p-100f ? amax : 0x1p-100f;
+    float scale, mult;
+    if (pow2) {
+        int j = pow2_exponent(amax_c, (double)fmax);
+        scale = ldexpf(1.0f, j);
+        mult = ldexpf(1.0f, -j);
+    } else {
+        scale = amax_c / fmax;
+        mult = fmax / amax_c;
+    }
+    for (int i = 0; i < 128; ++i) {
+        float prod = v[i] * mult;
+        q[i] = oracle_fp8_encode(prod, fmt);
+    }
+    return scale;
+}
+
+/*
  * Per-token cast: x is bf16 [rows][cols] (row stride ld_x elements), cols a
  * multiple of 128.  Writes q [rows][cols] (row stride ld_q bytes) and
  * s [rows][cols/128].  Returns 0, or -1 for a non-finite input (undefined).
@@ -144,36 +176,32 @@ static int pow2_exponent(float a, double fmax)
 int oracle_cast_per_token(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                           int fmt, int pow2, uint8_t* q, int64_t ld_q, float* s)
 {
-    const float fmax = (float)oracle_fp8_max(fmt);
     const int64_t groups = cols / 128;
     int bad = 0;
 #pragma omp parallel for schedule(static) reduction(| : bad)
     for (int64_t r = 0; r < rows; ++r) {
         for (int64_t g = 0; g < groups; ++g) {
-            const uint16_t* xg = x + r * ld_x + g * 128;
-            float amax = 0.0f;
-            for (int i = 0; i < 128; ++i) {
-                float f = oracle_bf16_to_f32(xg[i]);
-                if (!isfinite(f)) bad = 1;
-                if (fabsf(f) > amax) amax = fabsf(f);
-            }
-            float amax_c = amax > 0x1p-100f ? amax : 0x1p-100f;
-            float scale, mult;
-            if (pow2) {
-                int j = pow2_exponent(amax_c, (double)fmax);
-                scale = ldexpf(1.0f, j);
-                mult = ldexpf(1.0f, -j);
-            } else {
-                scale = amax_c / fmax;
-                mult = fmax / amax_c;
-            }
-            s[r * groups + g] = scale;
-            for (int i = 0; i < 128; ++i) {
-                float prod = oracle_bf16_to_f32(xg[i]) * mult;
-                q[r * ld_q + g * 128 + i] = oracle_fp8_encode(prod, fmt);
-            }
+            float v[128];
+            for (int i = 0; i < 128; ++i) v[i] = oracle_bf16_to_f32(x[r * ld_x + g * 128 + i]);
+            s[r * groups + g] = cast_group(v, fmt, pow2, q + r * ld_q + g * 128, &bad);
         }
     }
+    return bad ? -1 : 0;
+}
+
+/*
+ * The same cast of an fp32 matrix x [rows][cols] (row stride ld_x elements):
+ * the per-token cast of a GEMM epilogue's fp32 result before any rounding.
+ */
+int oracle_cast_per_token_f32(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
+                              int fmt, int pow2, uint8_t* q, int64_t ld_q, float* s)
+{
+    const int64_t groups = cols / 128;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t g = 0; g < groups; ++g)
+            s[r * groups + g] = cast_group(x + r * ld_x + g * 128, fmt, pow2, q + r * ld_q + g * 128, &bad);
     return bad ? -1 : 0;
 }
 

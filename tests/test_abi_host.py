@@ -150,6 +150,25 @@ def kgrouped_dev(lib, gk=GK, G=4, sum_k=512, M=256, N=256, out=O, accum=1):
                                                   accum, None)
 
 
+QS = 0xB0000
+
+
+def fwdq(lib, M=256, N=256, K=256, bias=0, epi=0, qdt=1, cf=0, q=B + 0x100000, ldq=256, qs=QS, pre=0, ldpre=0,
+         accum=2):
+    return lib.te_fp8_gemm_fwd_quant(p(A), p(S), 1, p(B), p(S), 1, M, N, K, p(bias), epi, qdt, cf, p(q), ldq, p(qs),
+                                     p(pre), ldpre, accum, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=200, ldq=208), INV), (dict(N=0), INV), (dict(epi=8), INV), (dict(epi=4), INV), (dict(epi=1), INV),
+    (dict(bias=BIAS), INV), (dict(qdt=3), INV), (dict(cf=2), INV), (dict(q=0), INV), (dict(qs=0), INV),
+    (dict(ldq=128), INV), (dict(q=MIS), MISAL), (dict(ldq=264), MISAL), (dict(qs=QS + 4), MISAL),
+    (dict(pre=Z, ldpre=256), INV), (dict(epi=6), INV), (dict(accum=0), INV), (dict(K=64), INV),
+])
+def test_fwd_quant_rejects(lib, kw, status):
+    assert fwdq(lib, **kw) == status
+
+
 MB = 0xA0000  # dummy device address of the per-block experts
 
 

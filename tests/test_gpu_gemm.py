@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads as W
-from parity import GELU_LIP, bf16_dev, bf16_host_f64, check_bf16, check_f32, dev, host, sdev
+from parity import GELU_LIP, bf16_dev, bf16_host_f64, check_bf16, check_f32, dev, host, scale_ld, sdev, shost
 
 te = pytest.importorskip("fp8_linear_layer_amd")
 pytestmark = pytest.mark.gpu
@@ -165,6 +165,71 @@ def test_fwd_small(accum, pow2, epi, ydt, M, N, K):
         pb = host(prebuf)
         assert torch.all(pb[:, N:] == 55.0)
         check_bf16(bf16_host_f64(pb[:, :N]), z, zmag, "fwd preact")
+
+
+def quant_fwd(qx, sx, qw, sw, b, epi, accum, qdt, cast_pow2, M, N, pre=None):
+    """Run the quantising forward with sentinel-filled outputs; return (q, row-major scales) and
+    check that nothing outside them was written."""
+    qbuf = torch.full((M, N + 16), 0xA5, dtype=torch.uint8, device="cuda")
+    qs = torch.full((N // 128, scale_ld(M)), -3.0, dtype=torch.float32, device="cuda")
+    te.te_fp8_gemm_fwd_quant(dev(qx), sdev(sx), E4, dev(qw), sdev(sw), E4,
+                             bias=bf16_dev(b) if epi & te.TE_EPI_BIAS else None, epilogue=epi, q_dtype=qdt,
+                             cast_flags=te.TE_CAST_POW2_SCALE if cast_pow2 else 0, q=qbuf[:, :N], q_scales=qs,
+                             preact=pre, accum=accum)
+    torch.cuda.synchronize()
+    qh, sh = host(qbuf).numpy(), host(qs).numpy()
+    assert (qh[:, N:] == 0xA5).all(), "wrote past N"
+    assert (sh[:, M:] == -3.0).all(), "wrote into the scale padding"
+    return qh[:, :N], shost(qs, M)
+
+
+@pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
+@pytest.mark.parametrize("epi", FWD_EPIS)
+@pytest.mark.parametrize("qdt,cast_pow2", [(te.TE_DTYPE_E4M3, False), (te.TE_DTYPE_E5M2, False),
+                                           (te.TE_DTYPE_E4M3, True)])
+@pytest.mark.parametrize("M,N,K", [(300, 384, 512), (17, 128, 128)])
+def test_fwd_quant(accum, pow2, epi, qdt, cast_pow2, M, N, K):
+    """The quantised forward equals the per-token cast of the forward's own fp32 result (the oracle's
+    fp32-input cast of the fp32 y the plain forward call returns: the codes are decided in the
+    kernel's fp32), and that fp32 y matches the fp64 oracle."""
+    qx, sx, qw, sw, b, y, z, zmag = fwd_case(M, N, K, epi, te.TE_DTYPE_F32, accum, pow2, seed=M + 5)
+    y32 = te.te_fp8_gemm_fwd(dev(qx), sdev(sx), E4, dev(qw), sdev(sw), E4,
+                             bias=bf16_dev(b) if epi & te.TE_EPI_BIAS else None, epilogue=epi & ~te.TE_EPI_AUX_PREACT,
+                             y_dtype=te.TE_DTYPE_F32, accum=accum)
+    y32h = host(y32).numpy()
+    check_f32(y32h, y, zmag * (GELU_LIP if epi & te.TE_EPI_GELU else 1.0), "fwd y (fp32)")
+    pre = None
+    if epi & te.TE_EPI_AUX_PREACT:
+        prebuf = torch.full((M, N + 8), 55.0, dtype=torch.bfloat16, device="cuda")
+        pre = prebuf[:, :N]
+    q, s = quant_fwd(qx, sx, qw, sw, b, epi, accum, qdt, cast_pow2, M, N, pre)
+    qo, so = oracle.cast_per_token_f32(y32h, OF[qdt], cast_pow2)
+    bad = np.argwhere(q != qo)
+    assert bad.size == 0, f"{len(bad)} code mismatches, first {bad[0]}"
+    assert np.array_equal(s.view(np.uint32), so.view(np.uint32)), "scale mismatch"
+    if pre is not None:
+        pb = host(prebuf)
+        assert torch.all(pb[:, N:] == 55.0)
+        check_bf16(bf16_host_f64(pb[:, :N]), z, zmag, "fwd preact")
+
+
+def test_fwd_quant_workload():
+    """8192 x 14336 x 4096 with bias + GELU, FAST on power-of-two inputs, e4m3 codes for the next
+    layer; rows sampled (the cast is per row)."""
+    sh = W.FPROP.shapes
+    inp = W.fprop_inputs()
+    qx, sx = oracle.cast_per_token(inp["x"], oracle.E4M3, True)
+    qw, sw = oracle.cast_per_token(inp["w"], oracle.E4M3, True)
+    M, N = sh["M"], sh["N"]
+    epi = te.TE_EPI_BIAS | te.TE_EPI_GELU
+    X, SX, Wd, SW, B = dev(qx), sdev(sx), dev(qw), sdev(sw), bf16_dev(inp["b"])
+    y32 = te.te_fp8_gemm_fwd(X, SX, E4, Wd, SW, E4, bias=B, epilogue=epi, y_dtype=te.TE_DTYPE_F32, accum=FAST)
+    q, qs = te.te_fp8_gemm_fwd_quant(X, SX, E4, Wd, SW, E4, bias=B, epilogue=epi, accum=FAST)
+    rows = sample_idx(M, 24, 5)
+    yr = host(y32[torch.from_numpy(rows).cuda()]).numpy()
+    qo, so = oracle.cast_per_token_f32(yr, oracle.E4M3)
+    assert np.array_equal(host(q).numpy()[rows], qo)
+    assert np.array_equal(shost(qs, M)[rows].view(np.uint32), so.view(np.uint32))
 
 
 def test_fwd_tiny_workload():

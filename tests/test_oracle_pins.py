@@ -171,6 +171,34 @@ def test_cast_invariants(fmt):
 
 
 @pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_cast_f32_matches_library_route_and_bf16_cast(fmt, pow2):
+    """The fp32-input cast (of a GEMM epilogue's fp32 result): torch's float8 conversion of the
+    values times FP8_MAX / amax, scales amax / FP8_MAX; on bf16-representable inputs it equals the
+    bf16 cast."""
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal((48, 512)) * 10.0 ** rng.uniform(-3, 3, (48, 1))).astype(np.float32)
+    q, s = oracle.cast_per_token_f32(x, fmt, pow2)
+    t = torch.from_numpy(x).view(48, 4, 128)
+    amax = t.abs().amax(-1, keepdim=True).clamp_min(2.0 ** -100)
+    fmax = torch.tensor(oracle.fp8_max(fmt), dtype=torch.float32)
+    if pow2:
+        sd = torch.from_numpy(s).double().view(48, 4, 1)
+        assert torch.all(torch.log2(sd) == torch.round(torch.log2(sd)))
+        assert torch.all(fmax * sd >= amax.double()) and torch.all(fmax * sd / 2 < amax.double())
+        mult = 1.0 / torch.from_numpy(s).view(48, 4, 1)
+    else:
+        assert torch.equal(torch.from_numpy(s).view(48, 4, 1), amax / fmax)
+        mult = fmax / amax
+    ref = (t * mult).to(FMTS[fmt]).view(torch.uint8).view(48, 512).numpy()
+    assert np.array_equal(q, ref)
+    xb = W.normal_bf16(np.random.SeedSequence(14), (16, 256), 0.4)
+    qa, sa = oracle.cast_per_token(xb, fmt, pow2)
+    qb, sb = oracle.cast_per_token_f32(W.bf16_bits_to_f32(xb), fmt, pow2)
+    assert np.array_equal(qa, qb) and np.array_equal(sa, sb)
+
+
+@pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
 def test_cast_transpose_groups_run_down_the_columns(fmt):
     """The transposed cast groups 128 consecutive rows of one column (the weight gradient's
     contraction over tokens): its scale of (column c, row block rb) is that column segment's
