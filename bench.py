@@ -12,8 +12,8 @@ the GEMM kernel's roofline fraction against the FP8 dense matrix-core peak
 throughput on a bounded sample, and per-kernel timings of the other
 workloads (fprop with bias+GELU at 8192 x 14336 x 4096 in both accumulation
 policies and with the quantising store, the fused cast + cast-transpose of the activation, dgrad at
-8192 x 4096 x 14336 and its dGELU+bias-grad form, the e5m2 cast of the
-gradient, the dense weight gradient fed from token-major sources through
+8192 x 4096 x 14336 and its dGELU+bias-grad form (also storing e5m2 dZ),
+the e5m2 cast of the gradient, the dense weight gradient fed from token-major sources through
 the cast-transpose, the 8-expert K-grouped wgrad with its group sizes on
 the host and on the device, and the 8-expert M-grouped forward).
 """
@@ -180,6 +180,15 @@ def breakdown(te, torch):
     out["dgrad_dz_none_full"] = {"shape": [M, N, K], "ms": round(med0, 4), "tflops": round(f / med0 / 1e9, 1)}
     out["dgrad_dz_dgelu_bgrad_full"] = {"shape": [M, N, K], "ms": round(med1, 4), "tflops": round(f / med1 / 1e9, 1),
                                         "epilogue_overhead": round(med1 / med0 - 1.0, 3)}
+    # the same with dZ stored as its per-token e5m2 cast (the next data-gradient GEMM's operand)
+    qz = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    qzs = torch.empty((N // 128, te.scale_ld(M)), dtype=torch.float32, device=dev)
+    med2, _ = timed(lambda: te.te_fp8_gemm_dgrad_quant(qo, so, E5, q2, s2, E4, epilogue=te.TE_EPI_DGELU | te.TE_EPI_BGRAD,
+                                                       preact=zz, bias_grad=bg, q=qz, q_scales=qzs,
+                                                       accum=te.TE_ACCUM_FULL_FP32), 10)
+    out["dgrad_dz_dgelu_bgrad_quant_e5m2_full"] = {"shape": [M, N, K], "ms": round(med2, 4),
+                                                   "tflops": round(f / med2 / 1e9, 1)}
+    del qz, qzs
     del do, w2t, zz, qo, so, q2, s2, dz, bg
 
     # the dense weight gradient from token-major sources: dY [4096 tokens x 7168] and X [4096 x 2112]

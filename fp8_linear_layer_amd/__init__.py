@@ -35,7 +35,8 @@ TE_EPI_BGRAD = 16
 # cast flags
 TE_CAST_POW2_SCALE = 1
 
-EXPORTED = ("te_cast_fp8_per_token", "te_cast_fp8_per_token_transpose", "te_fp8_gemm_fwd", "te_fp8_gemm_fwd_quant", "te_fp8_gemm_dgrad", "te_fp8_wgrad_accum",
+EXPORTED = ("te_cast_fp8_per_token", "te_cast_fp8_per_token_transpose", "te_fp8_gemm_fwd", "te_fp8_gemm_fwd_quant",
+            "te_fp8_gemm_dgrad_quant", "te_fp8_gemm_dgrad", "te_fp8_wgrad_accum",
             "te_fp8_kgrouped_wgrad", "te_fp8_kgrouped_wgrad_device_sizes", "te_fp8_mgrouped_gemm_fwd",
             "te_status_string", "te_last_error_message", "te_scale_ld")
 
@@ -72,6 +73,8 @@ def load_library():
     lib.te_fp8_gemm_fwd.argtypes = [P, P, I, P, P, I, I64, I64, I64, P, U32, P, I, I64, P, I64, I, P]
     lib.te_fp8_gemm_fwd_quant.restype = I
     lib.te_fp8_gemm_fwd_quant.argtypes = [P, P, I, P, P, I, I64, I64, I64, P, U32, I, U32, P, I64, P, P, I64, I, P]
+    lib.te_fp8_gemm_dgrad_quant.restype = I
+    lib.te_fp8_gemm_dgrad_quant.argtypes = [P, P, I, P, P, I, I64, I64, I64, U32, P, I64, P, I, U32, P, I64, P, I, P]
     lib.te_fp8_gemm_dgrad.restype = I
     lib.te_fp8_gemm_dgrad.argtypes = [P, P, I, P, P, I, I64, I64, I64, U32, P, I64, P, P, I, I64, I, P]
     lib.te_fp8_wgrad_accum.restype = I
@@ -279,3 +282,24 @@ def te_fp8_mgrouped_gemm_fwd(x, x_scales, x_dtype, w, w_scales, w_dtype, m_block
         _ptr(bias), epilogue, _ptr(y), y_dtype, y.stride(0),
         _ptr(preact), preact.stride(0) if preact is not None else 0, accum, _stream(stream)))
     return y
+
+
+def te_fp8_gemm_dgrad_quant(dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, epilogue=TE_EPI_NONE, preact=None,
+                            bias_grad=None, q_dtype=TE_DTYPE_E5M2, cast_flags=0, q=None, q_scales=None,
+                            accum=TE_ACCUM_FULL_FP32, stream=None):
+    """The data-gradient GEMM whose fp32 D (after dGELU) is stored as its per-token cast:
+    returns (q, q_scales); bias_grad is filled as by te_fp8_gemm_dgrad."""
+    M, K = dy.shape
+    N = wt.shape[0]
+    _scales_ok(dy_scales, M, K, "dy_scales")
+    _scales_ok(wt_scales, N, K, "wt_scales")
+    if q is None:
+        q = torch.empty((M, N), dtype=torch.uint8, device=dy.device)
+    if q_scales is None:
+        q_scales = torch.empty((N // 128, scale_ld(M)), dtype=torch.float32, device=dy.device)
+    _scales_ok(q_scales, M, N, "q_scales")
+    _check(load_library().te_fp8_gemm_dgrad_quant(
+        _ptr(dy), _ptr(dy_scales), dy_dtype, _ptr(wt), _ptr(wt_scales), wt_dtype, M, N, K, epilogue,
+        _ptr(preact), preact.stride(0) if preact is not None else 0, _ptr(bias_grad), q_dtype, cast_flags,
+        _ptr(q), q.stride(0), _ptr(q_scales), accum, _stream(stream)))
+    return q, q_scales

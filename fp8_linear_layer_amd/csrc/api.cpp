@@ -523,4 +523,60 @@ te_status_t te_fp8_gemm_fwd_quant(const void* x, const float* x_scales, te_dtype
     }
 }
 
+te_status_t te_fp8_gemm_dgrad_quant(const void* dy, const float* dy_scales, te_dtype_t dy_dtype,
+                                    const void* wt, const float* wt_scales, te_dtype_t wt_dtype,
+                                    int64_t M, int64_t N, int64_t K, uint32_t epilogue,
+                                    const void* preact_bf16, int64_t ld_preact, float* bias_grad,
+                                    te_dtype_t q_dtype, uint32_t cast_flags, void* q, int64_t ld_q, float* q_scales,
+                                    te_accum_t accum, hipStream_t stream)
+{
+    try {
+        const char* fn = "te_fp8_gemm_dgrad_quant";
+        te_status_t st = check_operands(fn, dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, M, N, K, accum);
+        if (st != TE_OK) return st;
+        if (N % 128 != 0) return fail(TE_ERR_INVALID_ARGUMENT, "%s: N must be a multiple of 128 (whole 1x128 groups; got %lld)", fn, (long long)N);
+        const uint32_t allowed = TE_EPI_DGELU | TE_EPI_BGRAD;
+        if (epilogue & ~allowed) return fail(TE_ERR_INVALID_ARGUMENT, "%s: epilogue flags 0x%x are not dgrad flags", fn, epilogue);
+        if (epilogue & TE_EPI_DGELU) {
+            if (!preact_bf16) return fail(TE_ERR_INVALID_ARGUMENT, "%s: TE_EPI_DGELU needs preact_bf16", fn);
+            if (ld_preact < N) return fail(TE_ERR_INVALID_ARGUMENT, "%s: ld_preact (%lld) is below N", fn, (long long)ld_preact);
+            if (!aligned(preact_bf16, 16) || ld_preact % 8 != 0)
+                return fail(TE_ERR_MISALIGNED, "%s: preact must be 16-byte aligned with ld_preact a multiple of 8", fn);
+        } else if (preact_bf16) {
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: preact given without TE_EPI_DGELU", fn);
+        }
+        if (epilogue & TE_EPI_BGRAD) {
+            if (!bias_grad) return fail(TE_ERR_INVALID_ARGUMENT, "%s: TE_EPI_BGRAD needs bias_grad", fn);
+            if (!aligned(bias_grad, 4)) return fail(TE_ERR_MISALIGNED, "%s: bias_grad must be 4-byte aligned", fn);
+        } else if (bias_grad) {
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: bias_grad given without TE_EPI_BGRAD", fn);
+        }
+        if (!is_fp8(q_dtype)) return fail(TE_ERR_INVALID_ARGUMENT, "%s: q_dtype must be TE_DTYPE_E4M3 or TE_DTYPE_E5M2 (got %d)", fn, (int)q_dtype);
+        if (cast_flags & ~(uint32_t)TE_CAST_POW2_SCALE) return fail(TE_ERR_INVALID_ARGUMENT, "%s: unknown cast flag bits 0x%x", fn, cast_flags);
+        if (!q || !q_scales) return fail(TE_ERR_INVALID_ARGUMENT, "%s: q and q_scales are required", fn);
+        if (ld_q < N) return fail(TE_ERR_INVALID_ARGUMENT, "%s: ld_q must be >= N", fn);
+        if (!aligned(q, 16) || ld_q % 16 != 0) return fail(TE_ERR_MISALIGNED, "%s: q must be 16-byte aligned with ld_q a multiple of 16", fn);
+        if (!aligned(q_scales, 16)) return fail(TE_ERR_MISALIGNED, "%s: q_scales must be 16-byte aligned", fn);
+        tefp8::GemmArgs g = base_args(dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, M, N, K, accum);
+        g.epi = tefp8::Epi::Dgrad;
+        g.flags = epilogue;
+        g.preact = static_cast<const uint16_t*>(preact_bf16);
+        g.ld_aux = ld_preact;
+        g.bias_grad = bias_grad;
+        g.q_out = static_cast<uint8_t*>(q);
+        g.q_scales = q_scales;
+        g.ld_q = ld_q;
+        g.ld_qs = te_scale_ld(M);
+        g.q_fmt = to_fmt(q_dtype);
+        g.q_pow2 = (cast_flags & TE_CAST_POW2_SCALE) ? 1 : 0;
+        if (epilogue & TE_EPI_BGRAD) {
+            hipError_t e = tefp8::launch_zero_f32(bias_grad, N, stream);
+            if (e != hipSuccess) return fail(TE_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+        }
+        return launch(fn, g, stream, K, dy_dtype, wt_dtype, accum, epilogue);
+    } catch (...) {
+        return fail(TE_ERR_INTERNAL, "te_fp8_gemm_dgrad_quant: internal error");
+    }
+}
+
 }  // extern "C"

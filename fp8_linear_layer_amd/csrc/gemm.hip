@@ -494,7 +494,7 @@ __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&v)[8],
 // holds eight consecutive columns of its row (group j + (q4 & 1), columns
 // 8 (q4 >> 1) .. +7).  Each bf16 load and store is then a 16-byte run, and
 // four lanes cover 64 contiguous bytes of a row.
-template <int kEpi, bool kFull>
+template <int kEpi, bool kFull, bool kQuant>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM][kTN], int64_t m0, int64_t n0,
                                          int64_t out_off, const uint16_t* bias_v, int wave, int lane)
 {
@@ -589,7 +589,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
 #pragma unroll
         for (int j = 0; j < kTN; ++j) colsum[j][0] = colsum[j][1] = colsum[j][2] = colsum[j][3] = 0.f;
         uint4 zq[kTN / 2][kTM];
-        if (kFull && has_dgelu) {
+        if (kFull && has_dgelu && !kQuant) {
 #pragma unroll
             for (int jp = 0; jp < kTN / 2; ++jp)
 #pragma unroll
@@ -598,6 +598,78 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
                         p.preact + (m0 + wm * kWM + i * 16 + r16) * p.ld_aux + n0 + wn * kWN + (2 * jp + (q4 & 1)) * 16 +
                         (q4 >> 1) * 8);
         }
+        if (kQuant) {
+            // Quantising store of D (after dGELU): as in the forward, the
+            // wave's 128 columns are one 1x128 group of each row; the lane's
+            // 32 values of a row are its 8 column groups x 4 columns.
+            const int64_t ng = n0 + wn * kWN;
+            const bool group_in = kFull || ng < p.N;
+#pragma unroll
+            for (int i = 0; i < kTM; ++i) {
+                const int64_t m = m0 + wm * kWM + i * 16 + r16;
+                const bool live = group_in && (kFull || m < p.M);
+                float v[kTN][4];
+#pragma unroll
+                for (int j = 0; j < kTN; ++j)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) v[j][c] = acc[i][j][c];
+                if (has_dgelu) {
+                    // (this row's four Z runs, loaded together; the whole tile's
+                    // runs do not fit in registers beside the row's values)
+                    uint4 zr[kTN / 2];
+#pragma unroll
+                    for (int jp = 0; jp < kTN / 2; ++jp) {
+                        zr[jp] = make_uint4(0u, 0u, 0u, 0u);
+                        if (live)
+                            zr[jp] = *reinterpret_cast<const uint4*>(
+                                p.preact + m * p.ld_aux + ng + (2 * jp + (q4 & 1)) * 16 + (q4 >> 1) * 8);
+                    }
+#pragma unroll
+                    for (int jp = 0; jp < kTN / 2; ++jp) {
+                        const uint32_t zw[4] = {zr[jp].x, zr[jp].y, zr[jp].z, zr[jp].w};
+                        const auto lo = __builtin_amdgcn_permlane16_swap(zw[0], zw[2], false, false);
+                        const auto hi = __builtin_amdgcn_permlane16_swap(zw[1], zw[3], false, false);
+                        const uint32_t a0 = lo[0], b0 = lo[1], a1 = hi[0], b1 = hi[1];
+                        float* v0 = v[2 * jp];
+                        float* v1 = v[2 * jp + 1];
+                        v0[0] *= dgelu(bf16_to_f32(a0 & 0xFFFF)); v0[1] *= dgelu(bf16_to_f32(a0 >> 16));
+                        v0[2] *= dgelu(bf16_to_f32(a1 & 0xFFFF)); v0[3] *= dgelu(bf16_to_f32(a1 >> 16));
+                        v1[0] *= dgelu(bf16_to_f32(b0 & 0xFFFF)); v1[1] *= dgelu(bf16_to_f32(b0 >> 16));
+                        v1[2] *= dgelu(bf16_to_f32(b1 & 0xFFFF)); v1[3] *= dgelu(bf16_to_f32(b1 >> 16));
+                    }
+                }
+                float amax = 0.0f;
+#pragma unroll
+                for (int j = 0; j < kTN; ++j)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        if (has_bgrad) colsum[j][c] += v[j][c];
+                        amax = fmaxf(amax, fabsf(v[j][c]));
+                    }
+                amax = fmaxf(amax, __shfl_xor(amax, 16));
+                amax = fmaxf(amax, __shfl_xor(amax, 32));
+                float scale, mult;
+                quant_scale(p.q_fmt, p.q_pow2, amax, scale, mult);
+#pragma unroll
+                for (int jp = 0; jp < kTN / 2; ++jp) {
+                    float t[8];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        t[c] = v[2 * jp][c] * mult;
+                        t[4 + c] = v[2 * jp + 1][c] * mult;
+                    }
+                    const uint2 e = quant_encode8(p.q_fmt, t);
+                    if (live) {
+                        uint8_t* o = p.q_out + m * p.ld_q + ng + q4 * 4;
+                        *reinterpret_cast<uint32_t*>(o + (2 * jp) * 16) = e.x;
+                        *reinterpret_cast<uint32_t*>(o + (2 * jp + 1) * 16) = e.y;
+                    }
+                }
+                if (live && q4 == 0) p.q_scales[(ng / 128) * p.ld_qs + m] = scale;
+                // (one row at a time: keeps the next rows' Z loads and values out of this row's registers)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else
 #pragma unroll
         for (int jp = 0; jp < kTN / 2; ++jp) {
             const int j0 = 2 * jp, j1 = 2 * jp + 1;
@@ -699,7 +771,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
     const bool has_aux = (p.flags & TE_EPI_AUX_PREACT) != 0;
     uint4 bw[kTN / 2];
 
-    if (p.q_out) {
+    if (kQuant) {
         // Quantising store.  A wave's 128 columns are one 1x128 group of each
         // of its rows (N is a multiple of 128, tile corners of 256), so a
         // group is wholly inside or outside the matrix, and a row's amax is
@@ -914,7 +986,7 @@ __device__ __forceinline__ bool row_scales_pow2(const GemmArgs& p, const TileCtx
 // size).  While a tile's epilogue runs, the first stage of the workgroup's
 // next tile is already being copied in; the next tile's FAST test follows the
 // epilogue.
-template <int kFmtA, int kFmtB, bool kFast, int kEpi>
+template <int kFmtA, int kFmtB, bool kFast, int kEpi, bool kQuant>
 __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p, int64_t total_tiles)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageBytes + kWaves * 4];
@@ -974,9 +1046,9 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p, int
         if (c.nkb > 0) {
             const uint16_t* bias_v = p.bias + c.bgrp * p.bias_group_stride;
             if (c.m0 + kBM <= p.M && c.n0 + kBN <= p.N)
-                epilogue<kEpi, true>(p, acc, c.m0, c.n0, c.out_off, bias_v, wave, lane);
+                epilogue<kEpi, true, kQuant>(p, acc, c.m0, c.n0, c.out_off, bias_v, wave, lane);
             else
-                epilogue<kEpi, false>(p, acc, c.m0, c.n0, c.out_off, bias_v, wave, lane);
+                epilogue<kEpi, false, kQuant>(p, acc, c.m0, c.n0, c.out_off, bias_v, wave, lane);
         }
         if (!more) break;
         // (after the epilogue: the scale reads overlap its stores)
@@ -995,10 +1067,18 @@ __global__ void zero_f32_kernel(float* p, int64_t n)
 template <int kFmtA, int kFmtB, bool kFast>
 hipError_t launch_epi(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s)
 {
+    // (the quantising store is its own kernel: its registers stay out of the plain epilogues)
+    const bool qz = a.q_out != nullptr;
     switch (a.epi) {
-    case Epi::Wgrad: gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Wgrad><<<grid, kThreads, 0, s>>>(a, tiles); break;
-    case Epi::Fwd: gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Fwd><<<grid, kThreads, 0, s>>>(a, tiles); break;
-    case Epi::Dgrad: gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Dgrad><<<grid, kThreads, 0, s>>>(a, tiles); break;
+    case Epi::Wgrad: gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Wgrad, false><<<grid, kThreads, 0, s>>>(a, tiles); break;
+    case Epi::Fwd:
+        if (qz) gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Fwd, true><<<grid, kThreads, 0, s>>>(a, tiles);
+        else gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Fwd, false><<<grid, kThreads, 0, s>>>(a, tiles);
+        break;
+    case Epi::Dgrad:
+        if (qz) gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Dgrad, true><<<grid, kThreads, 0, s>>>(a, tiles);
+        else gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Dgrad, false><<<grid, kThreads, 0, s>>>(a, tiles);
+        break;
     }
     return hipGetLastError();
 }

@@ -259,6 +259,23 @@ te_status_t te_fp8_gemm_dgrad(const void* dy, const float* dy_scales, te_dtype_t
                               te_accum_t accum, hipStream_t stream);
 
 /*
+ * The data-gradient GEMM with a quantising store: D (after dGELU) is written
+ * as its per-token cast along N, e.g. the e5m2 dZ the next data-gradient
+ * GEMM consumes, instead of dx; the bias gradient is formed from the fp32 D
+ * as in te_fp8_gemm_dgrad.
+ *   (q, q_scales) = te_cast_fp8_per_token applied to D[M][N] in fp32
+ *
+ *  dy, wt, epilogue, preact, bias_grad, accum   as te_fp8_gemm_dgrad;  N % 128 == 0
+ *  q_dtype, cast_flags, q, ld_q, q_scales        as te_fp8_gemm_fwd_quant
+ */
+te_status_t te_fp8_gemm_dgrad_quant(const void* dy, const float* dy_scales, te_dtype_t dy_dtype,
+                                    const void* wt, const float* wt_scales, te_dtype_t wt_dtype,
+                                    int64_t M, int64_t N, int64_t K, uint32_t epilogue,
+                                    const void* preact_bf16, int64_t ld_preact, float* bias_grad,
+                                    te_dtype_t q_dtype, uint32_t cast_flags, void* q, int64_t ld_q, float* q_scales,
+                                    te_accum_t accum, hipStream_t stream);
+
+/*
  * Weight-gradient GEMM that accumulates: out[m][n] += sum_k a[m][k] b[n][k].
  * The product is formed in fp32 from zero and added to out once (one fp32
  * rounding of the sum), as the gradient of a weight accumulates over

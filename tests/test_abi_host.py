@@ -169,6 +169,22 @@ def test_fwd_quant_rejects(lib, kw, status):
     assert fwdq(lib, **kw) == status
 
 
+def dgq(lib, M=256, N=256, K=256, epi=0, pre=0, ldpre=0, bg=0, qdt=2, cf=0, q=B + 0x100000, ldq=256, qs=QS,
+        accum=1):
+    return lib.te_fp8_gemm_dgrad_quant(p(A), p(S), 2, p(B), p(S), 1, M, N, K, epi, p(pre), ldpre, p(bg), qdt, cf,
+                                       p(q), ldq, p(qs), accum, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=200, ldq=208), INV), (dict(epi=1), INV), (dict(epi=8), INV), (dict(epi=16), INV), (dict(pre=Z), INV),
+    (dict(bg=O), INV), (dict(epi=8, pre=Z, ldpre=128), INV), (dict(epi=8, pre=Z + 8, ldpre=256), MISAL),
+    (dict(epi=16, bg=O + 2), MISAL), (dict(qdt=3), INV), (dict(cf=2), INV), (dict(q=0), INV), (dict(qs=0), INV),
+    (dict(ldq=128), INV), (dict(q=MIS), MISAL), (dict(ldq=264), MISAL), (dict(qs=QS + 4), MISAL), (dict(accum=3), INV),
+])
+def test_dgrad_quant_rejects(lib, kw, status):
+    assert dgq(lib, **kw) == status
+
+
 MB = 0xA0000  # dummy device address of the per-block experts
 
 

@@ -302,6 +302,49 @@ def test_dgrad_small(accum, pow2, epi, dxdt, M, N, K):
         check_f32(g[:N], db, dbm, "bias grad")
 
 
+DGRAD_EPIS = [te.TE_EPI_NONE, te.TE_EPI_DGELU, te.TE_EPI_DGELU | te.TE_EPI_BGRAD]
+
+
+@pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
+@pytest.mark.parametrize("epi", DGRAD_EPIS)
+@pytest.mark.parametrize("qdt,cast_pow2", [(te.TE_DTYPE_E5M2, False), (te.TE_DTYPE_E4M3, False),
+                                           (te.TE_DTYPE_E5M2, True)])
+@pytest.mark.parametrize("M,N,K", [(300, 384, 512), (40, 128, 256)])
+def test_dgrad_quant(accum, pow2, epi, qdt, cast_pow2, M, N, K):
+    """The quantised dgrad equals the per-token cast of the dgrad's own fp32 D (the oracle's
+    fp32-input cast of the fp32 dx the plain call returns), that fp32 D and the bias gradient match
+    the fp64 oracle, and nothing outside q, its scales and the bias gradient is written."""
+    qa, sa = operand(M + 31, M, K, E5, 1e-3, pow2)
+    qb, sb = operand(N + 32, N, K, E4, 0.02, pow2)
+    zb = W.normal_bf16(np.random.SeedSequence(M + 33), (M, N), 1.28)
+    o, d = oracle.gemm_nt(qa, sa, oracle.E5M2, qb, sb, oracle.E4M3)
+    has_dg, has_bg = bool(epi & te.TE_EPI_DGELU), bool(epi & te.TE_EPI_BGRAD)
+    D, Dm, db, dbm = oracle.dgrad_epilogue(o, d, zb if has_dg else None, has_bg)
+    A, SA, B, SB = dev(qa), sdev(sa), dev(qb), sdev(sb)
+    Z = bf16_dev(zb) if has_dg else None
+    d32 = te.te_fp8_gemm_dgrad(A, SA, E5, B, SB, E4, epilogue=epi & ~te.TE_EPI_BGRAD, preact=Z,
+                               dx_dtype=te.TE_DTYPE_F32, accum=accum)
+    d32h = host(d32).numpy()
+    check_f32(d32h, D, Dm, "dgrad D (fp32)")
+    qbuf = torch.full((M, N + 16), 0xA5, dtype=torch.uint8, device="cuda")
+    qs = torch.full((N // 128, scale_ld(M)), -3.0, dtype=torch.float32, device="cuda")
+    bg = torch.full((N + 4,), 3.0, dtype=torch.float32, device="cuda") if has_bg else None
+    te.te_fp8_gemm_dgrad_quant(A, SA, E5, B, SB, E4, epilogue=epi, preact=Z, bias_grad=bg[:N] if has_bg else None,
+                               q_dtype=qdt, cast_flags=te.TE_CAST_POW2_SCALE if cast_pow2 else 0, q=qbuf[:, :N],
+                               q_scales=qs, accum=accum)
+    torch.cuda.synchronize()
+    qh, sh = host(qbuf).numpy(), host(qs).numpy()
+    assert (qh[:, N:] == 0xA5).all() and (sh[:, M:] == -3.0).all()
+    qo, so = oracle.cast_per_token_f32(d32h, OF[qdt], cast_pow2)
+    bad = np.argwhere(qh[:, :N] != qo)
+    assert bad.size == 0, f"{len(bad)} code mismatches, first {bad[0]}"
+    assert np.array_equal(shost(qs, M).view(np.uint32), so.view(np.uint32)), "scale mismatch"
+    if has_bg:
+        g = host(bg).numpy()
+        assert np.all(g[N:] == 3.0)
+        check_f32(g[:N], db, dbm, "bias grad")
+
+
 @pytest.mark.parametrize("accum", [FULL, FAST])
 def test_dgrad_workload_dx(accum):
     """dX[8192x4096] = dY[8192x14336] (e5m2) W^T (e4m3), bf16 out."""
