@@ -73,6 +73,20 @@ def test_wgrad_small(accum, pow2, da, db, M, N, K):
     check_f32(b[:M, :N], want, mag, "wgrad")
 
 
+@pytest.mark.parametrize("accum,pow2", [(FULL, False), (FAST, True)], ids=["full", "fast-pow2"])
+def test_wgrad_max_k(accum, pow2):
+    """The largest contraction the ABI accepts, K = 2^22 (32768 scale blocks in one tile's loop)."""
+    M, N, K = 3, 4, 1 << 22
+    qa, sa = operand(101, M, K, E4, pow2=pow2)
+    qb, sb = operand(102, N, K, E4, pow2=pow2)
+    out0 = W.normal_f32(np.random.SeedSequence(103), (M, N))
+    o, d = oracle.gemm_nt(qa, sa, oracle.E4M3, qb, sb, oracle.E4M3)
+    want, mag = oracle.wgrad(o, d, out0)
+    out = dev(out0)
+    te.te_fp8_wgrad_accum(dev(qa), sdev(sa), E4, dev(qb), sdev(sb), E4, out, accum)
+    check_f32(host(out).numpy(), want, mag, "wgrad K=2^22")
+
+
 def test_wgrad_pages_ones_example():
     """out1 = ref.clone(); out1 += x y^T makes out1/ref ~ 2; zero-initialised out gives ~ref."""
     m, n, k = 512, 1024, 4096
