@@ -12,7 +12,8 @@ the GEMM kernel's roofline fraction against the FP8 dense matrix-core peak
 throughput on a bounded sample, and per-kernel timings of the other
 workloads (fprop with bias+GELU at 8192 x 14336 x 4096 in both accumulation
 policies and with the quantising store, the fused cast + cast-transpose of the activation, dgrad at
-8192 x 4096 x 14336 and its dGELU+bias-grad form (also storing e5m2 dZ),
+8192 x 4096 x 14336 and its dGELU+bias-grad form (also with the
+deterministic bias gradient, and storing e5m2 dZ),
 the e5m2 cast of the gradient, the dense weight gradient fed from token-major sources through
 the cast-transpose, the 8-expert K-grouped wgrad with its group sizes on
 the host and on the device, and the 8-expert M-grouped forward).
@@ -180,6 +181,14 @@ def breakdown(te, torch):
     out["dgrad_dz_none_full"] = {"shape": [M, N, K], "ms": round(med0, 4), "tflops": round(f / med0 / 1e9, 1)}
     out["dgrad_dz_dgelu_bgrad_full"] = {"shape": [M, N, K], "ms": round(med1, 4), "tflops": round(f / med1 / 1e9, 1),
                                         "epilogue_overhead": round(med1 / med0 - 1.0, 3)}
+    # the same with the bias gradient summed in a fixed order through a workspace (no atomics)
+    ws = torch.empty((te.load_library().te_fp8_dgrad_bgrad_workspace_bytes(M, N),), dtype=torch.uint8, device=dev)
+    med3, _ = timed(lambda: te.te_fp8_gemm_dgrad_deterministic(qo, so, E5, q2, s2, E4, bg,
+                                                               epilogue=te.TE_EPI_DGELU | te.TE_EPI_BGRAD, preact=zz,
+                                                               workspace=ws, dx=dz, accum=te.TE_ACCUM_FULL_FP32), 10)
+    out["dgrad_dz_dgelu_bgrad_deterministic_full"] = {"shape": [M, N, K], "ms": round(med3, 4),
+                                                      "tflops": round(f / med3 / 1e9, 1)}
+    del ws
     # the same with dZ stored as its per-token e5m2 cast (the next data-gradient GEMM's operand)
     qz = torch.empty((M, N), dtype=torch.uint8, device=dev)
     qzs = torch.empty((N // 128, te.scale_ld(M)), dtype=torch.float32, device=dev)

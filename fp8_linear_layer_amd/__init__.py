@@ -36,7 +36,7 @@ TE_EPI_BGRAD = 16
 TE_CAST_POW2_SCALE = 1
 
 EXPORTED = ("te_cast_fp8_per_token", "te_cast_fp8_per_token_transpose", "te_fp8_gemm_fwd", "te_fp8_gemm_fwd_quant",
-            "te_fp8_gemm_dgrad_quant", "te_fp8_gemm_dgrad", "te_fp8_wgrad_accum",
+            "te_fp8_gemm_dgrad_quant", "te_fp8_gemm_dgrad_deterministic", "te_fp8_dgrad_bgrad_workspace_bytes", "te_fp8_gemm_dgrad", "te_fp8_wgrad_accum",
             "te_fp8_kgrouped_wgrad", "te_fp8_kgrouped_wgrad_device_sizes", "te_fp8_mgrouped_gemm_fwd",
             "te_status_string", "te_last_error_message", "te_scale_ld")
 
@@ -75,6 +75,11 @@ def load_library():
     lib.te_fp8_gemm_fwd_quant.argtypes = [P, P, I, P, P, I, I64, I64, I64, P, U32, I, U32, P, I64, P, P, I64, I, P]
     lib.te_fp8_gemm_dgrad_quant.restype = I
     lib.te_fp8_gemm_dgrad_quant.argtypes = [P, P, I, P, P, I, I64, I64, I64, U32, P, I64, P, I, U32, P, I64, P, I, P]
+    lib.te_fp8_dgrad_bgrad_workspace_bytes.restype = I64
+    lib.te_fp8_dgrad_bgrad_workspace_bytes.argtypes = [I64, I64]
+    lib.te_fp8_gemm_dgrad_deterministic.restype = I
+    lib.te_fp8_gemm_dgrad_deterministic.argtypes = [P, P, I, P, P, I, I64, I64, I64, U32, P, I64, P, P, I64, P, I,
+                                                    I64, I, P]
     lib.te_fp8_gemm_dgrad.restype = I
     lib.te_fp8_gemm_dgrad.argtypes = [P, P, I, P, P, I, I64, I64, I64, U32, P, I64, P, P, I, I64, I, P]
     lib.te_fp8_wgrad_accum.restype = I
@@ -303,3 +308,25 @@ def te_fp8_gemm_dgrad_quant(dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, ep
         _ptr(preact), preact.stride(0) if preact is not None else 0, _ptr(bias_grad), q_dtype, cast_flags,
         _ptr(q), q.stride(0), _ptr(q_scales), accum, _stream(stream)))
     return q, q_scales
+
+
+def te_fp8_gemm_dgrad_deterministic(dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, bias_grad,
+                                    epilogue=TE_EPI_BGRAD, preact=None, workspace=None, dx=None,
+                                    dx_dtype=TE_DTYPE_BF16, accum=TE_ACCUM_FULL_FP32, stream=None):
+    """te_fp8_gemm_dgrad with the bias gradient summed in a fixed order through a workspace
+    (allocated here when not given); returns dx."""
+    M, K = dy.shape
+    N = wt.shape[0]
+    _scales_ok(dy_scales, M, K, "dy_scales")
+    _scales_ok(wt_scales, N, K, "wt_scales")
+    lib = load_library()
+    need = int(lib.te_fp8_dgrad_bgrad_workspace_bytes(M, N))
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dy.device)
+    if dx is None:
+        dx = torch.empty((M, N), dtype=torch.bfloat16 if dx_dtype == TE_DTYPE_BF16 else torch.float32, device=dy.device)
+    _check(lib.te_fp8_gemm_dgrad_deterministic(
+        _ptr(dy), _ptr(dy_scales), dy_dtype, _ptr(wt), _ptr(wt_scales), wt_dtype, M, N, K, epilogue,
+        _ptr(preact), preact.stride(0) if preact is not None else 0, _ptr(bias_grad), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(dx), dx_dtype, dx.stride(0), accum, _stream(stream)))
+    return dx

@@ -89,6 +89,7 @@ constexpr int kOpPerWave = (kBM / 8) / kWaves;    // 1 KiB copies of A (and of B
 constexpr int kBarrierGroup = kTN - 2;            // the block's barrier precedes this column group
 static_assert(kTM == 4 && kTN == 8 && kWaves * 64 == kBM + kBN, "layout assumed below");
 static_assert(kMGroupRows == kBM, "an M-grouped block is one tile row");
+static_assert(kBgradRowsPerTile == kWavesM, "one bias-gradient workspace row per wave along M");
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
@@ -755,7 +756,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
                     colsum[j][r] = t;
                 }
                 const int64_t n = n0 + wn * kWN + j * 16 + q4 * 4;
-                if (r16 == 0) {
+                if (r16 == 0 && p.bgrad_ws) {
+                    // deterministic: this wave's row of partial sums (the row is padded to a
+                    // multiple of 4 columns, so the 16-byte store never passes it)
+                    if (kFull || n < p.N)
+                        *reinterpret_cast<float4*>(p.bgrad_ws + ((m0 / kBM) * kWavesM + wm) * p.bgrad_ws_ld + n) =
+                            make_float4(colsum[j][0], colsum[j][1], colsum[j][2], colsum[j][3]);
+                } else if (r16 == 0) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         if (kFull || n + r < p.N) unsafeAtomicAdd(p.bias_grad + n + r, colsum[j][r]);
@@ -1064,6 +1071,18 @@ __global__ void zero_f32_kernel(float* p, int64_t n)
     if (i < n) p[i] = 0.0f;
 }
 
+// The second pass of the deterministic bias gradient: one thread per column
+// sums the workspace rows in order (coalesced across the threads of a row).
+__global__ void bgrad_reduce_kernel(const float* __restrict__ ws, int64_t rows, int64_t ld, int64_t N,
+                                    float* __restrict__ bias_grad)
+{
+    const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= N) return;
+    float s = 0.0f;
+    for (int64_t r = 0; r < rows; ++r) s += ws[r * ld + n];
+    bias_grad[n] = s;
+}
+
 template <int kFmtA, int kFmtB, bool kFast>
 hipError_t launch_epi(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s)
 {
@@ -1123,6 +1142,14 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream, LaunchInfo* info)
     if (a.fmt_a == FMT_E5M2 && a.fmt_b == FMT_E4M3) return launch_policy<FMT_E5M2, FMT_E4M3>(a, grid, tiles, stream);
     if (a.fmt_a == FMT_E4M3 && a.fmt_b == FMT_E5M2) return launch_policy<FMT_E4M3, FMT_E5M2>(a, grid, tiles, stream);
     return launch_policy<FMT_E5M2, FMT_E5M2>(a, grid, tiles, stream);
+}
+
+hipError_t launch_bgrad_reduce(const float* ws, int64_t rows, int64_t ld, int64_t N, float* bias_grad,
+                               hipStream_t stream)
+{
+    if (N <= 0) return hipSuccess;
+    bgrad_reduce_kernel<<<(unsigned)((N + 255) / 256), 256, 0, stream>>>(ws, rows, ld, N, bias_grad);
+    return hipGetLastError();
 }
 
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream)

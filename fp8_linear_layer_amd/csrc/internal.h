@@ -75,6 +75,11 @@ struct GemmArgs {
     int64_t ld_q, ld_qs;
     int q_fmt;
     int q_pow2;
+    // Deterministic bias gradient: when set, each wave stores its column sums
+    // to row (tile_m * 4 + wave_m) of this [P][bgrad_ws_ld] workspace instead
+    // of adding them atomically; a second kernel sums the rows in order.
+    float* bgrad_ws;
+    int64_t bgrad_ws_ld;
 };
 
 struct LaunchInfo {
@@ -85,6 +90,10 @@ struct LaunchInfo {
 int device_cus();  // compute units of the current device
 hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream, LaunchInfo* info);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
+// bias_grad[n] = sum over p = 0 .. rows-1, in order, of ws[p * ld + n]
+hipError_t launch_bgrad_reduce(const float* ws, int64_t rows, int64_t ld, int64_t N, float* bias_grad,
+                               hipStream_t stream);
+constexpr int kBgradRowsPerTile = 4;  // waves along M per 256-row tile
 hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
                        bool pow2, uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s, hipStream_t stream,
                        LaunchInfo* info);

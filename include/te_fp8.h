@@ -259,6 +259,34 @@ te_status_t te_fp8_gemm_dgrad(const void* dy, const float* dy_scales, te_dtype_t
                               te_accum_t accum, hipStream_t stream);
 
 /*
+ * Bytes of workspace te_fp8_gemm_dgrad_deterministic needs for an M x N
+ * output: one row of N fp32 column sums (padded to a multiple of 4) per 64
+ * output rows, i.e. ceil(M/256) * 4 * roundup(N, 4) * 4.  0 for M or N < 1.
+ */
+int64_t te_fp8_dgrad_bgrad_workspace_bytes(int64_t M, int64_t N);
+
+/*
+ * te_fp8_gemm_dgrad with a run-to-run deterministic bias gradient: instead of
+ * fp32 atomics, every 64-row slice of D stores its column sums to a row of the
+ * caller's workspace, and a second kernel sums those rows in a fixed order
+ * (bias_grad is overwritten).  The epilogue must include TE_EPI_BGRAD.  The
+ * pages place the bias gradient's reduction in the library (BGRADB among the
+ * cuBLASLt-style epilogues); this is its atomic-free form.
+ *
+ *  workspace        device memory, 16-byte aligned, at least
+ *                   te_fp8_dgrad_bgrad_workspace_bytes(M, N) bytes
+ *                   (contents on entry irrelevant; clobbered)
+ *  everything else  as te_fp8_gemm_dgrad
+ */
+te_status_t te_fp8_gemm_dgrad_deterministic(const void* dy, const float* dy_scales, te_dtype_t dy_dtype,
+                                            const void* wt, const float* wt_scales, te_dtype_t wt_dtype,
+                                            int64_t M, int64_t N, int64_t K, uint32_t epilogue,
+                                            const void* preact_bf16, int64_t ld_preact,
+                                            float* bias_grad, void* workspace, int64_t workspace_bytes,
+                                            void* dx, te_dtype_t dx_dtype, int64_t ld_dx,
+                                            te_accum_t accum, hipStream_t stream);
+
+/*
  * The data-gradient GEMM with a quantising store: D (after dGELU) is written
  * as its per-token cast along N, e.g. the e5m2 dZ the next data-gradient
  * GEMM consumes, instead of dx; the bias gradient is formed from the fp32 D

@@ -185,6 +185,29 @@ def test_dgrad_quant_rejects(lib, kw, status):
     assert dgq(lib, **kw) == status
 
 
+WS = 0xC0000
+
+
+@pytest.mark.parametrize("M,N,want", [(0, 5, 0), (5, 0, 0), (1, 1, 4 * 4 * 4), (256, 14336, 4 * 14336 * 4),
+                                      (257, 14337, 8 * 14340 * 4), (8192, 14336, 128 * 14336 * 4)])
+def test_dgrad_bgrad_workspace_bytes(lib, M, N, want):
+    assert lib.te_fp8_dgrad_bgrad_workspace_bytes(M, N) == want
+
+
+def dgd(lib, M=256, N=256, K=256, epi=16, pre=0, ldpre=0, bg=O, ws=WS, wsb=1 << 20, dx=Z, ldx=256, accum=1):
+    return lib.te_fp8_gemm_dgrad_deterministic(p(A), p(S), 2, p(B), p(S), 1, M, N, K, epi, p(pre), ldpre, p(bg), p(ws),
+                                               wsb, p(dx), 3, ldx, accum, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(epi=0), INV), (dict(epi=8, pre=Z + 0x1000, ldpre=256), INV), (dict(ws=0), INV), (dict(ws=WS + 8), MISAL),
+    (dict(wsb=4 * 256 * 4 - 1), INV), (dict(bg=0), INV), (dict(bg=O + 2), MISAL), (dict(pre=Z + 0x1000), INV),
+    (dict(epi=24, pre=0), INV), (dict(dx=0), INV), (dict(ldx=128), INV), (dict(K=100), INV), (dict(accum=0), INV),
+])
+def test_dgrad_deterministic_rejects(lib, kw, status):
+    assert dgd(lib, **kw) == status
+
+
 MB = 0xA0000  # dummy device address of the per-block experts
 
 

@@ -359,6 +359,41 @@ def test_dgrad_quant(accum, pow2, epi, qdt, cast_pow2, M, N, K):
         check_f32(g[:N], db, dbm, "bias grad")
 
 
+@pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
+@pytest.mark.parametrize("epi", [te.TE_EPI_BGRAD, te.TE_EPI_DGELU | te.TE_EPI_BGRAD])
+@pytest.mark.parametrize("M,N,K", [(300, 264, 512), (600, 37, 128)])
+def test_dgrad_deterministic_bias_grad(accum, pow2, epi, M, N, K):
+    """The atomic-free bias gradient: within tolerance of the oracle, bit-identical from run to run,
+    and the dx it writes is the plain call's dx bit for bit."""
+    qa, sa = operand(M + 41, M, K, E5, 1e-3, pow2)
+    qb, sb = operand(N + 42, N, K, E4, 0.02, pow2)
+    zb = W.normal_bf16(np.random.SeedSequence(M + 43), (M, N), 1.28)
+    o, d = oracle.gemm_nt(qa, sa, oracle.E5M2, qb, sb, oracle.E4M3)
+    has_dg = bool(epi & te.TE_EPI_DGELU)
+    _, _, db, dbm = oracle.dgrad_epilogue(o, d, zb if has_dg else None, True)
+    A, SA, B, SB = dev(qa), sdev(sa), dev(qb), sdev(sb)
+    zpad = np.zeros((M, N + 8 - N % 8), np.uint16)
+    zpad[:, :N] = zb
+    Z = bf16_dev(zpad)[:, :N] if has_dg else None
+    ld = N + 4 - N % 4
+    runs = []
+    for _ in range(3):
+        bg = torch.full((N,), 7.0, dtype=torch.float32, device="cuda")
+        ws = torch.full((te.load_library().te_fp8_dgrad_bgrad_workspace_bytes(M, N) // 4,), float("nan"),
+                        dtype=torch.float32, device="cuda")
+        dx = torch.empty((M, ld), dtype=torch.float32, device="cuda")[:, :N]
+        te.te_fp8_gemm_dgrad_deterministic(A, SA, E5, B, SB, E4, bg, epilogue=epi, preact=Z, workspace=ws, dx=dx,
+                                           dx_dtype=te.TE_DTYPE_F32, accum=accum)
+        runs.append((host(bg).numpy(), host(dx).numpy()))
+    for g, _ in runs[1:]:
+        assert np.array_equal(g.view(np.uint32), runs[0][0].view(np.uint32)), "bias grad not deterministic"
+    check_f32(runs[0][0], db, dbm, "deterministic bias grad")
+    ref = torch.empty((M, ld), dtype=torch.float32, device="cuda")[:, :N]
+    te.te_fp8_gemm_dgrad(A, SA, E5, B, SB, E4, epilogue=epi & ~te.TE_EPI_BGRAD, preact=Z, dx=ref,
+                         dx_dtype=te.TE_DTYPE_F32, accum=accum)
+    assert np.array_equal(runs[0][1].view(np.uint32), host(ref).numpy().view(np.uint32))
+
+
 @pytest.mark.parametrize("accum", [FULL, FAST])
 def test_dgrad_workload_dx(accum):
     """dX[8192x4096] = dY[8192x14336] (e5m2) W^T (e4m3), bf16 out."""
