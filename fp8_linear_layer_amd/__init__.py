@@ -35,7 +35,7 @@ TE_EPI_BGRAD = 16
 # cast flags
 TE_CAST_POW2_SCALE = 1
 
-EXPORTED = ("te_cast_fp8_per_token", "te_cast_fp8_per_token_transpose", "te_fp8_gemm_fwd", "te_fp8_gemm_fwd_quant",
+EXPORTED = ("te_cast_fp8_per_token", "te_cast_fp8_per_token_batch", "te_cast_fp8_per_token_transpose", "te_fp8_gemm_fwd", "te_fp8_gemm_fwd_quant",
             "te_fp8_gemm_dgrad_quant", "te_fp8_gemm_dgrad_deterministic", "te_fp8_dgrad_bgrad_workspace_bytes", "te_fp8_gemm_dgrad", "te_fp8_wgrad_accum",
             "te_fp8_kgrouped_wgrad", "te_fp8_kgrouped_wgrad_device_sizes", "te_fp8_mgrouped_gemm_fwd",
             "te_status_string", "te_last_error_message", "te_scale_ld")
@@ -67,6 +67,8 @@ def load_library():
     lib.te_scale_ld.argtypes = [I64]
     lib.te_cast_fp8_per_token.restype = I
     lib.te_cast_fp8_per_token.argtypes = [P, I64, I64, I64, I, U32, P, I64, P, P]
+    lib.te_cast_fp8_per_token_batch.restype = I
+    lib.te_cast_fp8_per_token_batch.argtypes = [P, I32, I, U32, P]
     lib.te_cast_fp8_per_token_transpose.restype = I
     lib.te_cast_fp8_per_token_transpose.argtypes = [P, I64, I64, I64, I, U32, P, I64, P, P, I64, P, P]
     lib.te_fp8_gemm_fwd.restype = I
@@ -142,6 +144,38 @@ def te_cast_fp8_per_token(x, out_dtype=TE_DTYPE_E4M3, flags=0, q=None, scales=No
     _check(load_library().te_cast_fp8_per_token(_ptr(x), rows, cols, x.stride(0), out_dtype, flags,
                                                 _ptr(q), q.stride(0), _ptr(scales), _stream(stream)))
     return q, scales
+
+
+class _CastOperand(ctypes.Structure):
+    _fields_ = [("x_bf16", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("ld_x", ctypes.c_int64), ("q", ctypes.c_void_p), ("ld_q", ctypes.c_int64),
+                ("scales", ctypes.c_void_p)]
+
+
+_CAST_ARRAYS = {}  # one reusable operand array per batch size (calls on one thread at a time)
+
+
+def te_cast_fp8_per_token_batch(xs, out_dtype=TE_DTYPE_E4M3, flags=0, qs=None, scales=None, stream=None):
+    """The per-token cast of every bf16 matrix in xs in one launch; returns [(q, scales), ...]."""
+    n = len(xs)
+    arr = _CAST_ARRAYS.get(n)
+    if arr is None:
+        arr = _CAST_ARRAYS[n] = (_CastOperand * n)()
+    out = []
+    for i, x in enumerate(xs):
+        assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+        rows, cols = x.shape
+        q = qs[i] if qs is not None and qs[i] is not None else \
+            torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+        sc = scales[i] if scales is not None and scales[i] is not None else \
+            torch.empty((cols // 128, scale_ld(rows)), dtype=torch.float32, device=x.device)
+        _scales_ok(sc, rows, cols, "scales")
+        o = arr[i]
+        o.x_bf16, o.rows, o.cols, o.ld_x = x.data_ptr(), rows, cols, x.stride(0)
+        o.q, o.ld_q, o.scales = q.data_ptr(), q.stride(0), sc.data_ptr()
+        out.append((q, sc))
+    _check(load_library().te_cast_fp8_per_token_batch(arr, n, out_dtype, flags, _stream(stream)))
+    return out
 
 
 def te_cast_fp8_per_token_transpose(x, out_dtype=TE_DTYPE_E4M3, flags=0, rowwise=True, q=None, scales=None,

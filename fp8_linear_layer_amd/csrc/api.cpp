@@ -154,6 +154,59 @@ const char* te_last_error_message(void) { return g_last_error.c_str(); }
 
 int64_t te_scale_ld(int64_t rows) { return rows > 0 ? (rows + 3) / 4 * 4 : 0; }
 
+namespace {
+// The checks of one cast operand (shared by the single and batched casts).
+te_status_t check_cast_operand(const char* fn, const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                               const void* q, int64_t ld_q, const float* scales)
+{
+    if (!x_bf16 || !q || !scales) return fail(TE_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
+    if (rows < 1 || rows >= kMaxDim) return fail(TE_ERR_INVALID_ARGUMENT, "%s: rows must be in [1, 2^31) (got %lld)", fn, (long long)rows);
+    if (cols < 128 || cols % 128 != 0 || cols >= kMaxDim)
+        return fail(TE_ERR_INVALID_ARGUMENT, "%s: cols must be a positive multiple of 128 (got %lld)", fn, (long long)cols);
+    if (ld_x < cols || ld_q < cols) return fail(TE_ERR_INVALID_ARGUMENT, "%s: ld_x and ld_q must be >= cols", fn);
+    if (!aligned(x_bf16, 16) || ld_x % 8 != 0) return fail(TE_ERR_MISALIGNED, "%s: x must be 16-byte aligned with ld_x a multiple of 8", fn);
+    if (!aligned(q, 16) || ld_q % 16 != 0) return fail(TE_ERR_MISALIGNED, "%s: q must be 16-byte aligned with ld_q a multiple of 16", fn);
+    if (!aligned(scales, 16)) return fail(TE_ERR_MISALIGNED, "%s: scales must be 16-byte aligned", fn);
+    return TE_OK;
+}
+}  // namespace
+
+te_status_t te_cast_fp8_per_token_batch(const te_cast_operand_t* ops, int32_t n, te_dtype_t out_dtype,
+                                        uint32_t flags, hipStream_t stream)
+{
+    try {
+        const char* fn = "te_cast_fp8_per_token_batch";
+        if (!ops) return fail(TE_ERR_INVALID_ARGUMENT, "%s: ops is null", fn);
+        if (n < 1 || n > tefp8::kMaxCastBatch)
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: n must be in [1, %d] (got %d)", fn, tefp8::kMaxCastBatch, (int)n);
+        if (!is_fp8(out_dtype)) return fail(TE_ERR_INVALID_ARGUMENT, "%s: out_dtype must be TE_DTYPE_E4M3 or TE_DTYPE_E5M2 (got %d)", fn, (int)out_dtype);
+        if (flags & ~(uint32_t)TE_CAST_POW2_SCALE) return fail(TE_ERR_INVALID_ARGUMENT, "%s: unknown flag bits 0x%x", fn, flags);
+        tefp8::CastOperand co[tefp8::kMaxCastBatch] = {};
+        for (int32_t i = 0; i < n; ++i) {
+            const te_cast_operand_t& o = ops[i];
+            te_status_t st = check_cast_operand(fn, o.x_bf16, o.rows, o.cols, o.ld_x, o.q, o.ld_q, o.scales);
+            if (st != TE_OK) return fail(st, "%s (operand %d)", te_last_error_message(), (int)i);
+            co[i].x = static_cast<const uint16_t*>(o.x_bf16);
+            co[i].rows = o.rows;
+            co[i].cols = o.cols;
+            co[i].ld_x = o.ld_x;
+            co[i].q = static_cast<uint8_t*>(o.q);
+            co[i].ld_q = o.ld_q;
+            co[i].scales = o.scales;
+            co[i].ld_s = te_scale_ld(o.rows);
+        }
+        tefp8::LaunchInfo info{};
+        hipError_t e = tefp8::launch_cast_batch(co, n, to_fmt(out_dtype), (flags & TE_CAST_POW2_SCALE) != 0, stream, &info);
+        if (log_enabled())
+            std::fprintf(stderr, "[te_fp8] %s n=%d out=%s pow2=%d threads=%d grid=%lld\n", fn, (int)n,
+                         dtype_name(out_dtype), (flags & TE_CAST_POW2_SCALE) ? 1 : 0, info.threads, (long long)info.grid);
+        if (e != hipSuccess) return fail(TE_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+        return ok();
+    } catch (...) {
+        return fail(TE_ERR_INTERNAL, "te_cast_fp8_per_token_batch: internal error");
+    }
+}
+
 te_status_t te_cast_fp8_per_token(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                                   te_dtype_t out_dtype, uint32_t flags, void* q, int64_t ld_q,
                                   float* scales, hipStream_t stream)

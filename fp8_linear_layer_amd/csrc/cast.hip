@@ -64,30 +64,28 @@ __device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(
 constexpr int kTileRows = 32;   // 4 waves x 8 rows
 constexpr int kTileGroups = 4;  // 128-column groups per tile
 
+// One 32-row x 512-column tile of one operand.
 template <int kFmt, bool kPow2>
-__global__ __launch_bounds__(kThreads) void cast_per_token_kernel(
-    const uint16_t* __restrict__ x, int64_t rows, int64_t groups_per_row, int64_t tiles_c, int64_t ld_x,
-    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scales, int64_t ld_s)
+__device__ __forceinline__ void cast_tile(const CastOperand& o, int64_t tile)
 {
-
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int part = lane & (kLanesPerGroup - 1);
-    const int64_t tile_r = blockIdx.x / tiles_c;
-    const int64_t tile_c = blockIdx.x - tile_r * tiles_c;
+    const int64_t tile_r = tile / o.tiles_c;
+    const int64_t tile_c = tile - tile_r * o.tiles_c;
     const int64_t row_raw = tile_r * kTileRows + wave * 8 + (lane >> 3);
     // Rows and groups past the end repeat the last valid one (the 8 lanes of
     // a group stay together, so the DPP exchange is unaffected) and store
     // nothing.
-    const bool row_ok = row_raw < rows;
-    const int64_t row = row_ok ? row_raw : rows - 1;
+    const bool row_ok = row_raw < o.rows;
+    const int64_t row = row_ok ? row_raw : o.rows - 1;
     const int64_t g0 = tile_c * kTileGroups;
 
     u32x4 u[kTileGroups][2];
 #pragma unroll
     for (int t = 0; t < kTileGroups; ++t) {
-        const int64_t gc = min(g0 + t, groups_per_row - 1);
-        const u32x4* src = reinterpret_cast<const u32x4*>(x + row * ld_x + gc * 128 + part * 16);
+        const int64_t gc = min(g0 + t, o.gpr - 1);
+        const u32x4* src = reinterpret_cast<const u32x4*>(o.x + row * o.ld_x + gc * 128 + part * 16);
         u[t][0] = __builtin_nontemporal_load(src);
         u[t][1] = __builtin_nontemporal_load(src + 1);
     }
@@ -119,11 +117,25 @@ __global__ __launch_bounds__(kThreads) void cast_per_token_kernel(
         const uint2 c0 = encode8<kFmt>(s0);
         const uint2 c1 = encode8<kFmt>(s1);
         const int64_t gc = g0 + t;
-        if (row_ok && gc < groups_per_row) {
-            *reinterpret_cast<uint4*>(q + row * ld_q + gc * 128 + part * 16) = make_uint4(c0.x, c0.y, c1.x, c1.y);
-            if (part == 0) scales[gc * ld_s + row] = scale;  // block-major: [cols/128][ld_s]
+        if (row_ok && gc < o.gpr) {
+            *reinterpret_cast<uint4*>(o.q + row * o.ld_q + gc * 128 + part * 16) = make_uint4(c0.x, c0.y, c1.x, c1.y);
+            if (part == 0) o.scales[gc * o.ld_s + row] = scale;  // block-major: [cols/128][ld_s]
         }
     }
+}
+
+// One launch over the tiles of up to kMaxCastBatch operands: workgroup w
+// casts tile w - tile_begin of the last operand whose tiles begin at or
+// before w.
+template <int kFmt, bool kPow2>
+__global__ __launch_bounds__(kThreads) void cast_per_token_kernel(const CastBatch b)
+{
+    const int64_t w = blockIdx.x;
+    int k = 0;
+    for (int i = 1; i < b.n; ++i)
+        if (w >= b.op[i].tile_begin) k = i;
+    const CastOperand* ops = b.op;
+    cast_tile<kFmt, kPow2>(ops[k], w - ops[k].tile_begin);
 }
 
 // ------------------------------------------------------------ cast-transpose
@@ -250,25 +262,47 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(
 
 }  // namespace
 
-hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
-                       bool pow2, uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s, hipStream_t stream,
-                       LaunchInfo* info)
+hipError_t launch_cast_batch(const CastOperand* ops, int n, int fmt, bool pow2, hipStream_t stream, LaunchInfo* info)
 {
-    const int64_t gpr = cols / 128;
-    const int64_t tiles_c = (gpr + kTileGroups - 1) / kTileGroups;
-    const int64_t blocks = ((rows + kTileRows - 1) / kTileRows) * tiles_c;
+    if (n < 1 || n > kMaxCastBatch) return hipErrorInvalidValue;
+    CastBatch b{};
+    b.n = n;
+    int64_t blocks = 0;
+    for (int i = 0; i < n; ++i) {
+        b.op[i] = ops[i];
+        b.op[i].gpr = ops[i].cols / 128;
+        b.op[i].tiles_c = (b.op[i].gpr + kTileGroups - 1) / kTileGroups;
+        b.op[i].tile_begin = blocks;
+        blocks += ((ops[i].rows + kTileRows - 1) / kTileRows) * b.op[i].tiles_c;
+    }
     if (info) { info->tile_m = kTileRows; info->tile_n = 128 * kTileGroups; info->threads = kThreads; info->grid = blocks; }
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (blocks <= 0) return hipSuccess;
     dim3 grid((unsigned)blocks), block(kThreads);
     if (fmt == FMT_E4M3) {
-        if (pow2) cast_per_token_kernel<FMT_E4M3, true><<<grid, block, 0, stream>>>(x, rows, gpr, tiles_c, ld_x, q, ld_q, scales, ld_s);
-        else cast_per_token_kernel<FMT_E4M3, false><<<grid, block, 0, stream>>>(x, rows, gpr, tiles_c, ld_x, q, ld_q, scales, ld_s);
+        if (pow2) cast_per_token_kernel<FMT_E4M3, true><<<grid, block, 0, stream>>>(b);
+        else cast_per_token_kernel<FMT_E4M3, false><<<grid, block, 0, stream>>>(b);
     } else {
-        if (pow2) cast_per_token_kernel<FMT_E5M2, true><<<grid, block, 0, stream>>>(x, rows, gpr, tiles_c, ld_x, q, ld_q, scales, ld_s);
-        else cast_per_token_kernel<FMT_E5M2, false><<<grid, block, 0, stream>>>(x, rows, gpr, tiles_c, ld_x, q, ld_q, scales, ld_s);
+        if (pow2) cast_per_token_kernel<FMT_E5M2, true><<<grid, block, 0, stream>>>(b);
+        else cast_per_token_kernel<FMT_E5M2, false><<<grid, block, 0, stream>>>(b);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
+                       bool pow2, uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s, hipStream_t stream,
+                       LaunchInfo* info)
+{
+    CastOperand o{};
+    o.x = x;
+    o.rows = rows;
+    o.cols = cols;
+    o.ld_x = ld_x;
+    o.q = q;
+    o.ld_q = ld_q;
+    o.scales = scales;
+    o.ld_s = ld_s;
+    return launch_cast_batch(&o, 1, fmt, pow2, stream, info);
 }
 
 hipError_t launch_cast_transpose(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int fmt, bool pow2,

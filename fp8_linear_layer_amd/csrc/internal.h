@@ -97,6 +97,23 @@ constexpr int kBgradRowsPerTile = 4;  // waves along M per 256-row tile
 hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
                        bool pow2, uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s, hipStream_t stream,
                        LaunchInfo* info);
+// One operand of a batched per-token cast (gpr, tiles_c and tile_begin are
+// filled in by launch_cast_batch).
+struct CastOperand {
+    const uint16_t* x;
+    int64_t rows, cols, ld_x;
+    uint8_t* q;
+    int64_t ld_q;
+    float* scales;
+    int64_t ld_s;
+    int64_t gpr, tiles_c, tile_begin;
+};
+constexpr int kMaxCastBatch = 8;
+struct CastBatch {
+    int n;
+    CastOperand op[kMaxCastBatch];
+};
+hipError_t launch_cast_batch(const CastOperand* ops, int n, int fmt, bool pow2, hipStream_t stream, LaunchInfo* info);
 // Row-wise cast (q may be null) and cast of the transpose in one pass; rows a
 // multiple of 128, cols a multiple of 128 with the row-wise cast, else of 8.
 hipError_t launch_cast_transpose(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int fmt, bool pow2,

@@ -154,6 +154,28 @@ te_status_t te_cast_fp8_per_token(const void* x_bf16, int64_t rows, int64_t cols
                                   te_dtype_t out_dtype, uint32_t flags, void* q, int64_t ld_q,
                                   float* scales, hipStream_t stream);
 
+/* One operand of te_cast_fp8_per_token_batch (fields as te_cast_fp8_per_token's). */
+typedef struct {
+    const void* x_bf16;
+    int64_t rows, cols, ld_x;
+    void* q;
+    int64_t ld_q;
+    float* scales;
+} te_cast_operand_t;
+
+/*
+ * Several per-token casts with one format and flags in one launch, e.g. the
+ * two operands of a weight gradient: each operand's result is exactly that
+ * of te_cast_fp8_per_token on it.  One launch lets a small operand's loads
+ * overlap a large one's instead of paying its own start-up and latency.
+ *
+ *  ops    HOST array of n operands (read during the call), each valid for
+ *         te_cast_fp8_per_token; outputs must not overlap
+ *  n      1 .. 8
+ */
+te_status_t te_cast_fp8_per_token_batch(const te_cast_operand_t* ops, int32_t n, te_dtype_t out_dtype,
+                                        uint32_t flags, hipStream_t stream);
+
 /*
  * Fused per-token cast and cast-transpose: one read of a bf16 matrix X
  * [rows][cols] produces the operand cast of X (as te_cast_fp8_per_token) and

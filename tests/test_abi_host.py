@@ -250,6 +250,35 @@ def test_cast_rejects(lib, kw, status):
     assert cast(lib, **kw) == status
 
 
+class CastOp(ctypes.Structure):
+    _fields_ = [("x_bf16", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("ld_x", ctypes.c_int64), ("q", ctypes.c_void_p), ("ld_q", ctypes.c_int64),
+                ("scales", ctypes.c_void_p)]
+
+
+def cast_batch(lib, ops, n=None, dt=1, flags=0):
+    arr = (CastOp * max(1, len(ops)))(*[CastOp(*o) for o in ops])
+    return lib.te_cast_fp8_per_token_batch(ctypes.cast(arr, ctypes.c_void_p), len(ops) if n is None else n, dt, flags,
+                                           None)
+
+
+GOOD = (A, 4, 256, 256, B, 256, S)
+
+
+@pytest.mark.parametrize("ops,n,dt,flags,status", [
+    ([GOOD], 0, 1, 0, INV), ([GOOD] * 9, None, 1, 0, INV), ([GOOD], None, 3, 0, INV), ([GOOD], None, 1, 2, INV),
+    ([GOOD, (A, 4, 100, 256, B, 256, S)], None, 1, 0, INV), ([GOOD, (0, 4, 256, 256, B, 256, S)], None, 1, 0, INV),
+    ([(A, 0, 256, 256, B, 256, S)], None, 1, 0, INV), ([GOOD, (MIS, 4, 256, 256, B, 256, S)], None, 1, 0, MISAL),
+    ([(A, 4, 256, 256, B, 264, S)], None, 1, 0, MISAL), ([(A, 4, 256, 256, B, 256, S + 4)], None, 1, 0, MISAL),
+])
+def test_cast_batch_rejects(lib, ops, n, dt, flags, status):
+    assert cast_batch(lib, ops, n, dt, flags) == status
+
+
+def test_cast_batch_null_ops(lib):
+    assert lib.te_cast_fp8_per_token_batch(None, 1, 1, 0, None) == INV
+
+
 QT = 0x70000
 ST = 0x80000
 

@@ -178,3 +178,41 @@ def test_cast_transpose_ragged_columns(dt, rows, cols, ldx, ldqt):
 def test_cast_transpose_workload_sizes(name, shape, std, dt):
     bits = W.normal_bf16(np.random.SeedSequence(zlib.crc32(name.encode())), shape, std)
     assert_same_t(bits, dt, False, rowwise=shape[1] % 128 == 0)
+
+
+@pytest.mark.parametrize("dt", [te.TE_DTYPE_E4M3, te.TE_DTYPE_E5M2])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_cast_batch_matches_the_oracle_per_operand(dt, pow2):
+    """One launch over operands of different shapes and strides: each result bit-identical to the
+    oracle's cast of that operand; nothing written outside any of them."""
+    shapes = [(37, 384, 392, 400), (300, 128, None, None), (1, 1024, 1152, 1040), (513, 640, None, 656)]
+    xs, bufs, ss, bits_all = [], [], [], []
+    for i, (rows, cols, ldx, ldq) in enumerate(shapes):
+        ldx, ldq = ldx or cols, ldq or cols
+        bits = W.normal_bf16(np.random.SeedSequence(500 + i), (rows, cols), 0.3 + i)
+        xb = np.zeros((rows, ldx), np.uint16)
+        xb[:, :cols] = bits
+        xs.append(bf16_dev(xb)[:, :cols])
+        bufs.append(torch.full((rows, ldq), 0xA5, dtype=torch.uint8, device="cuda"))
+        ss.append(torch.full((cols // 128, scale_ld(rows)), -7.0, dtype=torch.float32, device="cuda"))
+        bits_all.append(bits)
+    te.te_cast_fp8_per_token_batch(xs, dt, te.TE_CAST_POW2_SCALE if pow2 else 0,
+                                   qs=[b[:, :x.shape[1]] for b, x in zip(bufs, xs)], scales=ss)
+    torch.cuda.synchronize()
+    for (rows, cols, _, _), bits, qb, sb in zip(shapes, bits_all, bufs, ss):
+        qh, sh = host(qb).numpy(), host(sb).numpy()
+        assert (qh[:, cols:] == 0xA5).all() and (sh[:, rows:] == -7.0).all()
+        qo, so = oracle.cast_per_token(bits, FMT[dt], pow2)
+        assert np.array_equal(qh[:, :cols], qo)
+        assert np.array_equal(shost(sb, rows).view(np.uint32), so.view(np.uint32))
+
+
+def test_cast_batch_wgrad_operands():
+    """The dense weight gradient's two operands (7168 x 4096 and 2112 x 4096) in one launch."""
+    a = W.normal_bf16(np.random.SeedSequence(601), (7168, 4096))
+    b = W.normal_bf16(np.random.SeedSequence(602), (2112, 4096))
+    (qa, sa), (qb, sb) = te.te_cast_fp8_per_token_batch([bf16_dev(a), bf16_dev(b)], te.TE_DTYPE_E4M3)
+    for bits, q, s in ((a, qa, sa), (b, qb, sb)):
+        qo, so = oracle.cast_per_token(bits, oracle.E4M3)
+        assert np.array_equal(host(q).numpy(), qo)
+        assert np.array_equal(shost(s, bits.shape[0]).view(np.uint32), so.view(np.uint32))
