@@ -373,13 +373,9 @@ def main():
     # The kernel's own duration: back-to-back launches between one event pair
     # on the launch stream (an event pair around a single launch also counts
     # the dispatch gap in front of it).
-    kst, ken = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    kst.record(stream)
-    for _ in range(args.kernel_reps):
-        te.te_fp8_wgrad_accum(qa, sa, E4, qb, sb, E4, out, te.TE_ACCUM_FULL_FP32)
-    ken.record(stream)
-    torch.cuda.synchronize()
-    gemm_ms = kst.elapsed_time(ken) / args.kernel_reps
+    # (median of 5 rounds of kernel_reps back-to-back launches, one event pair each)
+    gemm_ms, _ = timed(lambda: te.te_fp8_wgrad_accum(qa, sa, E4, qb, sb, E4, out, te.TE_ACCUM_FULL_FP32),
+                       args.kernel_reps, warm=0, rounds=5)
     flop = 2.0 * M * N * K
     value = flop / (ms_step * 1e-3) / 1e12
     achieved = flop / (gemm_ms * 1e-3) / 1e12
