@@ -2,11 +2,22 @@
  * te_fp8.h - C ABI of the MI355X (gfx950) scaled-FP8 Linear-layer GEMM library.
  *
  * Five operations make up the FP8 hot path of a transformer Linear layer in
- * training: the per-token fp8 cast that produces the operands (also fused
- * with the transposed cast the weight gradient needs), the forward
+ * training: the per-token fp8 cast that produces the operands, the forward
  * GEMM with its bias/GELU epilogue, the data-gradient GEMM with its dGELU and
  * bias-gradient epilogue, the weight-gradient GEMM that accumulates into an
- * fp32 buffer, and its K-grouped (mixture-of-experts) variant.
+ * fp32 buffer, and its K-grouped (mixture-of-experts) variant:
+ *   te_cast_fp8_per_token, te_fp8_gemm_fwd, te_fp8_gemm_dgrad,
+ *   te_fp8_wgrad_accum, te_fp8_kgrouped_wgrad.
+ * Around them:
+ *   te_cast_fp8_per_token_batch       several casts in one launch
+ *   te_cast_fp8_per_token_transpose   the cast and the cast of the transpose
+ *                                     (the weight gradient's operand) from one read
+ *   te_fp8_gemm_fwd_quant,            the forward / data-gradient result stored
+ *   te_fp8_gemm_dgrad_quant           as the next GEMM's fp8 operand
+ *   te_fp8_gemm_dgrad_deterministic   the bias gradient without atomics
+ *                                     (te_fp8_dgrad_bgrad_workspace_bytes)
+ *   te_fp8_kgrouped_wgrad_device_sizes  expert sizes in device memory
+ *   te_fp8_mgrouped_gemm_fwd          the experts' forward / data gradient
  *
  * Conventions shared by every entry point
  * ---------------------------------------
