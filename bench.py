@@ -10,7 +10,8 @@ Printed: one JSON line with the whole-step throughput (2 M N K flop per step),
 the GEMM kernel's roofline fraction against the FP8 dense matrix-core peak
 (kernel time from HIP events on the launch stream), the oracle's CPU
 throughput on a bounded sample, and per-kernel timings of the other
-workloads (fprop with bias+GELU at 8192 x 14336 x 4096 in both accumulation
+workloads (the tiny 256 x 256 x 512 fprop and wgrad calls, fprop with
+bias+GELU at 8192 x 14336 x 4096 in both accumulation
 policies and with the quantising store, the fused cast + cast-transpose of the activation, dgrad at
 8192 x 4096 x 14336 and its dGELU+bias-grad form (also with the
 deterministic bias gradient, and storing e5m2 dZ),
@@ -109,6 +110,21 @@ def breakdown(te, torch):
         return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
 
     E4, E5 = te.TE_DTYPE_E4M3, te.TE_DTYPE_E5M2
+    # tiny fprop 256 x 256 x 512 with bias + GELU, fp32 out, and the wgrad out += call on the same
+    # operands: latency-bound (one workgroup), reported in microseconds
+    xt, wt_, bt = randn((256, 512), 1.0, 21), randn((256, 512), 1.0, 22), randn((256,), 0.1, 23)
+    qxt, sxt = te.te_cast_fp8_per_token(xt, E4)
+    qwt, swt = te.te_cast_fp8_per_token(wt_, E4)
+    yt = torch.empty((256, 256), dtype=torch.float32, device=dev)
+    ot = torch.zeros((256, 256), dtype=torch.float32, device=dev)
+    med, _ = timed(lambda: te.te_fp8_gemm_fwd(qxt, sxt, E4, qwt, swt, E4, bias=bt,
+                                              epilogue=te.TE_EPI_BIAS | te.TE_EPI_GELU, y=yt,
+                                              y_dtype=te.TE_DTYPE_F32, accum=te.TE_ACCUM_FULL_FP32), 50)
+    out["tiny_fprop_bias_gelu_256x256x512"] = {"us": round(med * 1e3, 2)}
+    med, _ = timed(lambda: te.te_fp8_wgrad_accum(qxt, sxt, E4, qwt, swt, E4, ot, te.TE_ACCUM_FULL_FP32), 50)
+    out["tiny_wgrad_256x256x512"] = {"us": round(med * 1e3, 2)}
+    del xt, wt_, bt, qxt, sxt, qwt, swt, yt, ot
+
     # fprop 8192 x 14336 x 4096, bias + GELU (+ saved pre-activation), bf16 out
     M, N, K = 8192, 14336, 4096
     x, w, b = randn((M, K), 1.0, 1), randn((N, K), 0.02, 2), randn((N,), 0.1, 3)
