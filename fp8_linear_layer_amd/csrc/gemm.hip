@@ -497,7 +497,8 @@ __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&v)[8],
 // four lanes cover 64 contiguous bytes of a row.
 template <int kEpi, bool kFull, bool kQuant>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM][kTN], int64_t m0, int64_t n0,
-                                         int64_t out_off, const uint16_t* bias_v, int wave, int lane)
+                                         int64_t out_off, const uint16_t* bias_v, float* bgrad_v, int wave,
+                                         int lane)
 {
     const int wm = wave / kWavesN, wn = wave % kWavesN;
     // (the lane index is re-derived here so that its address arithmetic is not
@@ -765,7 +766,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
                 } else if (r16 == 0) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (kFull || n + r < p.N) unsafeAtomicAdd(p.bias_grad + n + r, colsum[j][r]);
+                        if (kFull || n + r < p.N) unsafeAtomicAdd(bgrad_v + n + r, colsum[j][r]);
                 }
             }
         }
@@ -1051,11 +1052,13 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p, int
         // (a tile inside the matrix takes the copy of the epilogue without
         // bounds checks: straight-line code lets its loads be in flight together)
         if (c.nkb > 0) {
+            // an expert's bias and bias gradient (M-grouped; offset 0 otherwise)
             const uint16_t* bias_v = p.bias + c.bgrp * p.bias_group_stride;
+            float* bgrad_v = p.bias_grad + c.bgrp * p.bias_group_stride;
             if (c.m0 + kBM <= p.M && c.n0 + kBN <= p.N)
-                epilogue<kEpi, true, kQuant>(p, acc, c.m0, c.n0, c.out_off, bias_v, wave, lane);
+                epilogue<kEpi, true, kQuant>(p, acc, c.m0, c.n0, c.out_off, bias_v, bgrad_v, wave, lane);
             else
-                epilogue<kEpi, false, kQuant>(p, acc, c.m0, c.n0, c.out_off, bias_v, wave, lane);
+                epilogue<kEpi, false, kQuant>(p, acc, c.m0, c.n0, c.out_off, bias_v, bgrad_v, wave, lane);
         }
         if (!more) break;
         // (after the epilogue: the scale reads overlap its stores)

@@ -17,7 +17,9 @@
  *   te_fp8_gemm_dgrad_deterministic   the bias gradient without atomics
  *                                     (te_fp8_dgrad_bgrad_workspace_bytes)
  *   te_fp8_kgrouped_wgrad_device_sizes  expert sizes in device memory
- *   te_fp8_mgrouped_gemm_fwd          the experts' forward / data gradient
+ *   te_fp8_mgrouped_gemm_fwd          the experts' forward (and plain data gradient)
+ *   te_fp8_mgrouped_gemm_dgrad        the experts' data gradient with dGELU and
+ *                                     per-expert bias gradients
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -425,6 +427,28 @@ te_status_t te_fp8_mgrouped_gemm_fwd(const void* x, const float* x_scales, te_dt
                                      void* y, te_dtype_t y_dtype, int64_t ld_y,
                                      void* preact_bf16, int64_t ld_preact,
                                      te_accum_t accum, hipStream_t stream);
+
+/*
+ * M-grouped data gradient with the backward epilogues of te_fp8_gemm_dgrad,
+ * per expert: block i of 256 token rows uses expert e = m_block_group[i]'s
+ * W^T, and
+ *   D = dy * wt[e]^T, D *= GELU'(preact) (TE_EPI_DGELU, preact [sum_m][ld]),
+ *   bias_grad[e][n] = sum of D[m][n] over the rows m of expert e's blocks
+ *                     (TE_EPI_BGRAD; fp32 atomics; all G rows overwritten,
+ *                     an expert with no block gets zeros),
+ *   dx = D.  Blocks outside [0, G) are skipped (their dx rows not written).
+ *
+ *  dy, dy_scales   [sum_m][K] fp8, [K/128][te_scale_ld(sum_m)]
+ *  wt, wt_scales   [G][N][K] fp8, [G][K/128][te_scale_ld(N)]
+ *  bias_grad       [G][N] fp32, required iff TE_EPI_BGRAD
+ *  everything else as te_fp8_mgrouped_gemm_fwd / te_fp8_gemm_dgrad
+ */
+te_status_t te_fp8_mgrouped_gemm_dgrad(const void* dy, const float* dy_scales, te_dtype_t dy_dtype,
+                                       const void* wt, const float* wt_scales, te_dtype_t wt_dtype,
+                                       int64_t sum_m, int64_t N, int64_t K, int32_t G, const int32_t* m_block_group,
+                                       uint32_t epilogue, const void* preact_bf16, int64_t ld_preact,
+                                       float* bias_grad, void* dx, te_dtype_t dx_dtype, int64_t ld_dx,
+                                       te_accum_t accum, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* te_status_string(te_status_t status);

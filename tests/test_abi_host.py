@@ -216,6 +216,22 @@ def mgrouped(lib, mb=MB, G=4, sum_m=512, N=256, K=256, bias=0, epi=0, y=O, ydt=4
                                         ldy, p(pre), ldpre, accum, None)
 
 
+def mgrouped_dg(lib, mb=MB, G=4, sum_m=512, N=256, K=256, epi=16, pre=0, ldpre=0, bg=O, dx=Z, dxdt=3, ldx=256,
+                accum=1):
+    return lib.te_fp8_mgrouped_gemm_dgrad(p(A), p(S), 2, p(B), p(S), 1, sum_m, N, K, G, p(mb), epi, p(pre), ldpre,
+                                          p(bg), p(dx), dxdt, ldx, accum, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mb=0), INV), (dict(mb=MB + 2), MISAL), (dict(G=0), INV), (dict(G=1025), INV), (dict(sum_m=300), INV),
+    (dict(epi=1), INV), (dict(epi=8), INV), (dict(epi=24, pre=Z + 0x10000, ldpre=128), INV),
+    (dict(epi=24, pre=Z + 0x10008, ldpre=256), MISAL), (dict(bg=0), INV), (dict(epi=0), INV),
+    (dict(bg=O + 2), MISAL), (dict(dx=0), INV), (dict(ldx=128), INV), (dict(accum=0), INV),
+])
+def test_mgrouped_dgrad_rejects(lib, kw, status):
+    assert mgrouped_dg(lib, **kw) == status
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(mb=0), INV), (dict(mb=MB + 2), MISAL), (dict(G=0), INV), (dict(G=1025), INV), (dict(sum_m=0), INV),
     (dict(sum_m=300), INV), (dict(K=100), INV), (dict(epi=8), INV), (dict(epi=4), INV), (dict(epi=1), INV),

@@ -496,6 +496,54 @@ def test_mgrouped_dgrad_form_e5m2():
     check_bf16(bf16_host_f64(yg)[live], y[live], zmag[live], "mgrouped dX")
 
 
+@pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
+@pytest.mark.parametrize("epi,dxdt", [(te.TE_EPI_DGELU | te.TE_EPI_BGRAD, te.TE_DTYPE_F32),
+                                      (te.TE_EPI_BGRAD, te.TE_DTYPE_BF16), (te.TE_EPI_DGELU, te.TE_DTYPE_BF16)])
+def test_mgrouped_dgrad(accum, pow2, epi, dxdt):
+    """Per-expert data gradient through GELU' with per-expert bias gradients: each live block is
+    the dense dgrad epilogue with its expert's W^T; bias_grad[e] sums expert e's blocks (an expert
+    with no block gets zeros); skipped blocks are not written."""
+    blocks = np.array([1, 0, -1, 1, 2], np.int32)
+    G, N, K = 4, 200, 384
+    M = 256 * len(blocks)
+    qa, sa = operand(110, M, K, E5, 1e-3, pow2)
+    ws = [operand(111 + e, N, K, E4, 0.02, pow2) for e in range(G)]
+    qw, sw = np.stack([w[0] for w in ws]), np.stack([w[1] for w in ws])
+    zb = W.normal_bf16(np.random.SeedSequence(120), (M, N), 1.28)
+    has_dg, has_bg = bool(epi & te.TE_EPI_DGELU), bool(epi & te.TE_EPI_BGRAD)
+    D = np.full((M, N), np.nan); Dm = np.full((M, N), np.nan)
+    db = np.zeros((G, N)); dbm = np.zeros((G, N))
+    for i, e in enumerate(blocks):
+        if e < 0:
+            continue
+        r = slice(256 * i, 256 * (i + 1))
+        o, d = oracle.gemm_nt(qa[r], sa[r], oracle.E5M2, qw[e], sw[e], oracle.E4M3)
+        D[r], Dm[r], dbi, dbmi = oracle.dgrad_epilogue(o, d, zb[r] if has_dg else None, True)
+        db[e] += dbi
+        dbm[e] += dbmi
+    tdt = torch.float32 if dxdt == te.TE_DTYPE_F32 else torch.bfloat16
+    dxbuf = torch.full((M, N + 8), 9.0, dtype=tdt, device="cuda")
+    bg = torch.full((G * N,), 3.0, dtype=torch.float32, device="cuda") if has_bg else None
+    zpad = np.zeros((M, N + 8), np.uint16)
+    zpad[:, :N] = zb
+    wq, wsd = w_dev(qw, sw)
+    te.te_fp8_mgrouped_gemm_dgrad(dev(qa), sdev(sa), E5, wq, wsd, E4, torch.from_numpy(blocks).cuda(), epilogue=epi,
+                                  preact=bf16_dev(zpad)[:, :N] if has_dg else None, bias_grad=bg, dx=dxbuf[:, :N],
+                                  dx_dtype=dxdt, accum=accum)
+    torch.cuda.synchronize()
+    xb = host(dxbuf)
+    live = np.repeat(blocks >= 0, 256)
+    assert torch.all(xb[:, N:] == 9.0) and torch.all(xb[torch.from_numpy(~live)] == 9.0)
+    if dxdt == te.TE_DTYPE_F32:
+        check_f32(xb[:, :N].numpy()[live], D[live], Dm[live], "mgrouped dgrad D")
+    else:
+        check_bf16(bf16_host_f64(xb[:, :N])[live], D[live], Dm[live], "mgrouped dgrad D")
+    if has_bg:
+        g = host(bg).numpy().reshape(G, N)
+        assert (g[3] == 0).all(), "an expert without blocks must get a zero bias gradient"
+        check_f32(g[:3], db[:3], dbm[:3], "per-expert bias grad")
+
+
 def test_mgrouped_same_expert_equals_dense():
     """With every block on one expert the call is the dense forward GEMM, bit for bit."""
     blocks = np.zeros(4, np.int32)
