@@ -42,6 +42,13 @@
  *  - GELU is the tanh form, 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
  *  - In the backward pass dGELU is applied before the bias gradient.
  *
+ *  - The library's other entry points reduce to these definitions, composed
+ *    in the Python side of this package: the cast of X and of X^T (fused
+ *    cast-transpose), the cast of an epilogue's fp32 result (quantising
+ *    stores; oracle_cast_per_token_f32 below), and each 256-row block of an
+ *    M-grouped GEMM through the dense forward or dgrad with its expert's
+ *    operand.
+ *
  * parity unpinned: the GELU form (the pages give none; the tanh form is fixed
  * here and pinned against a library implementation of that same form), and
  * the fast-accumulation policy's own precision (the pages state it is
