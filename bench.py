@@ -219,6 +219,18 @@ def breakdown(te, torch):
     del qz, qzs
     del do, w2t, zz, qo, so, q2, s2, dz, bg
 
+    # the dense weight gradient on power-of-two-scaled operands with the FAST policy (scales applied
+    # inside the matrix-core instruction, no vector promotion) next to FULL on the same operands
+    T, M, N = 4096, 7168, 2112
+    pa, psa = te.te_cast_fp8_per_token(randn((M, T), 1.0, 16), E4, te.TE_CAST_POW2_SCALE)
+    pb, psb = te.te_cast_fp8_per_token(randn((N, T), 1.0, 17), E4, te.TE_CAST_POW2_SCALE)
+    o = torch.zeros((M, N), dtype=torch.float32, device=dev)
+    for name, acc in (("wgrad_pow2_full_7168x2112x4096", te.TE_ACCUM_FULL_FP32),
+                      ("wgrad_pow2_fast_7168x2112x4096", te.TE_ACCUM_FAST)):
+        med, _ = timed(lambda: te.te_fp8_wgrad_accum(pa, psa, E4, pb, psb, E4, o, acc), 10)
+        out[name] = {"ms": round(med, 4), "tflops": round(2.0 * M * N * T / med / 1e9, 1)}
+    del pa, psa, pb, psb, o
+
     # the dense weight gradient from token-major sources: dY [4096 tokens x 7168] and X [4096 x 2112]
     # are cast-transposed (1x128 groups along tokens) and fed to out += A B^T
     T, M, N = 4096, 7168, 2112
