@@ -36,7 +36,8 @@ TE_EPI_BGRAD = 16
 TE_CAST_POW2_SCALE = 1
 
 EXPORTED = ("te_cast_fp8_per_token", "te_cast_fp8_per_token_batch", "te_cast_fp8_per_token_transpose", "te_fp8_gemm_fwd", "te_fp8_gemm_fwd_quant",
-            "te_fp8_gemm_dgrad_quant", "te_fp8_gemm_dgrad_deterministic", "te_fp8_dgrad_bgrad_workspace_bytes", "te_fp8_gemm_dgrad", "te_fp8_wgrad_accum",
+            "te_fp8_gemm_dgrad_quant", "te_fp8_gemm_dgrad_deterministic", "te_fp8_dgrad_bgrad_workspace_bytes",
+            "te_fp8_wgrad_accum_bgrad", "te_fp8_gemm_dgrad", "te_fp8_wgrad_accum",
             "te_fp8_kgrouped_wgrad", "te_fp8_kgrouped_wgrad_device_sizes", "te_fp8_mgrouped_gemm_fwd",
             "te_fp8_mgrouped_gemm_dgrad",
             "te_status_string", "te_last_error_message", "te_scale_ld")
@@ -87,6 +88,8 @@ def load_library():
     lib.te_fp8_gemm_dgrad.argtypes = [P, P, I, P, P, I, I64, I64, I64, U32, P, I64, P, P, I, I64, I, P]
     lib.te_fp8_wgrad_accum.restype = I
     lib.te_fp8_wgrad_accum.argtypes = [P, P, I, P, P, I, I64, I64, I64, P, I64, I, P]
+    lib.te_fp8_wgrad_accum_bgrad.restype = I
+    lib.te_fp8_wgrad_accum_bgrad.argtypes = [P, P, I, P, P, I, I64, I64, I64, P, I64, P, I, P]
     lib.te_fp8_kgrouped_wgrad.restype = I
     lib.te_fp8_kgrouped_wgrad.argtypes = [P, P, I, P, P, I, I64, I64, P, I32, P, I, P]
     lib.te_fp8_kgrouped_wgrad_device_sizes.restype = I
@@ -394,3 +397,17 @@ def te_fp8_mgrouped_gemm_dgrad(dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype,
         epilogue, _ptr(preact), preact.stride(0) if preact is not None else 0, _ptr(bias_grad), _ptr(dx), dx_dtype,
         dx.stride(0), accum, _stream(stream)))
     return dx
+
+
+def te_fp8_wgrad_accum_bgrad(a, a_scales, a_dtype, b, b_scales, b_dtype, out, bias_grad,
+                             accum=TE_ACCUM_FULL_FP32, stream=None):
+    """out += A B^T and bias_grad[m] = sum_k A[m, k] (dequantised); returns out."""
+    M, K = a.shape
+    N = b.shape[0]
+    _scales_ok(a_scales, M, K, "a_scales")
+    _scales_ok(b_scales, N, K, "b_scales")
+    assert bias_grad.dtype == torch.float32 and bias_grad.numel() >= M
+    _check(load_library().te_fp8_wgrad_accum_bgrad(
+        _ptr(a), _ptr(a_scales), a_dtype, _ptr(b), _ptr(b_scales), b_dtype, M, N, K, _ptr(out), out.stride(0),
+        _ptr(bias_grad), accum, _stream(stream)))
+    return out

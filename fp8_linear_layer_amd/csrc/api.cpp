@@ -393,6 +393,35 @@ te_status_t te_fp8_wgrad_accum(const void* a, const float* a_scales, te_dtype_t 
     }
 }
 
+te_status_t te_fp8_wgrad_accum_bgrad(const void* a, const float* a_scales, te_dtype_t a_dtype,
+                                     const void* b, const float* b_scales, te_dtype_t b_dtype,
+                                     int64_t M, int64_t N, int64_t K,
+                                     float* out, int64_t ld_out, float* bias_grad,
+                                     te_accum_t accum, hipStream_t stream)
+{
+    try {
+        const char* fn = "te_fp8_wgrad_accum_bgrad";
+        te_status_t st = check_operands(fn, a, a_scales, a_dtype, b, b_scales, b_dtype, M, N, K, accum);
+        if (st != TE_OK) return st;
+        st = check_output(fn, "out", out, TE_DTYPE_F32, ld_out, N);
+        if (st != TE_OK) return st;
+        if (!bias_grad) return fail(TE_ERR_INVALID_ARGUMENT, "%s: bias_grad is null", fn);
+        if (!aligned(bias_grad, 4)) return fail(TE_ERR_MISALIGNED, "%s: bias_grad must be 4-byte aligned", fn);
+        tefp8::GemmArgs g = base_args(a, a_scales, a_dtype, b, b_scales, b_dtype, M, N, K, accum);
+        g.epi = tefp8::Epi::Wgrad;
+        g.out = out;
+        g.ld_out = ld_out;
+        st = launch(fn, g, stream, K, a_dtype, b_dtype, accum, 0);
+        if (st != TE_OK) return st;
+        hipError_t e = tefp8::launch_row_sum(static_cast<const uint8_t*>(a), M, K, K, to_fmt(a_dtype), a_scales,
+                                             te_scale_ld(M), bias_grad, stream);
+        if (e != hipSuccess) return fail(TE_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+        return ok();
+    } catch (...) {
+        return fail(TE_ERR_INTERNAL, "te_fp8_wgrad_accum_bgrad: internal error");
+    }
+}
+
 te_status_t te_fp8_kgrouped_wgrad(const void* a, const float* a_scales, te_dtype_t a_dtype,
                                   const void* b, const float* b_scales, te_dtype_t b_dtype,
                                   int64_t M, int64_t N, const int64_t* group_k, int32_t G,

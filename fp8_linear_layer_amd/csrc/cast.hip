@@ -260,6 +260,46 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(
     }
 }
 
+// ------------------------------------------------------------ operand row sums
+// bias_grad[r] = sum_k dec(q[r][k]) * s(r, k/128): one wave per row, lane l
+// decodes 16 consecutive codes of each 1 KiB chunk (8 lanes per 128-element
+// scale block), multiplies its partial sum by that block's scale, and the
+// wave sums its lanes at the end.
+// The fp8 code in byte kB of w as fp32 (exact).
+template <int kFmt, int kB>
+__device__ __forceinline__ float dec_byte(uint32_t w)
+{
+    if (kFmt == FMT_E4M3) return __builtin_amdgcn_cvt_f32_fp8((int)w, kB);
+    return __builtin_amdgcn_cvt_f32_bf8((int)w, kB);
+}
+
+template <int kFmt>
+__global__ __launch_bounds__(kThreads) void row_sum_kernel(const uint8_t* __restrict__ q, int64_t rows, int64_t cols,
+                                                          int64_t ld_q, const float* __restrict__ scales,
+                                                          int64_t ld_s, float* __restrict__ out)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (r >= rows) return;   // whole waves only: r is uniform in a wave
+    float acc = 0.0f;
+    for (int64_t c0 = 0; c0 < cols; c0 += 1024) {
+        const int64_t c = c0 + lane * 16;
+        if (c < cols) {
+            const uint4 w = *reinterpret_cast<const uint4*>(q + r * ld_q + c);
+            const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+            float part = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                part += (dec_byte<kFmt, 0>(d[i]) + dec_byte<kFmt, 1>(d[i])) +
+                        (dec_byte<kFmt, 2>(d[i]) + dec_byte<kFmt, 3>(d[i]));
+            acc = fmaf(part, scales[(c / 128) * ld_s + r], acc);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) out[r] = acc;
+}
+
 }  // namespace
 
 hipError_t launch_cast_batch(const CastOperand* ops, int n, int fmt, bool pow2, hipStream_t stream, LaunchInfo* info)
@@ -286,6 +326,19 @@ hipError_t launch_cast_batch(const CastOperand* ops, int n, int fmt, bool pow2, 
         if (pow2) cast_per_token_kernel<FMT_E5M2, true><<<grid, block, 0, stream>>>(b);
         else cast_per_token_kernel<FMT_E5M2, false><<<grid, block, 0, stream>>>(b);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_row_sum(const uint8_t* q, int64_t rows, int64_t cols, int64_t ld_q, int fmt, const float* scales,
+                          int64_t ld_s, float* out, hipStream_t stream)
+{
+    const int64_t blocks = (rows + kThreads / 64 - 1) / (kThreads / 64);
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (fmt == FMT_E4M3)
+        row_sum_kernel<FMT_E4M3><<<(unsigned)blocks, kThreads, 0, stream>>>(q, rows, cols, ld_q, scales, ld_s, out);
+    else
+        row_sum_kernel<FMT_E5M2><<<(unsigned)blocks, kThreads, 0, stream>>>(q, rows, cols, ld_q, scales, ld_s, out);
     return hipGetLastError();
 }
 

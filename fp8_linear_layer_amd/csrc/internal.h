@@ -113,6 +113,9 @@ struct CastBatch {
     int n;
     CastOperand op[kMaxCastBatch];
 };
+// out[r] = sum over k of the dequantised fp8 operand row r (block-major scales)
+hipError_t launch_row_sum(const uint8_t* q, int64_t rows, int64_t cols, int64_t ld_q, int fmt, const float* scales,
+                          int64_t ld_s, float* out, hipStream_t stream);
 hipError_t launch_cast_batch(const CastOperand* ops, int n, int fmt, bool pow2, hipStream_t stream, LaunchInfo* info);
 // Row-wise cast (q may be null) and cast of the transpose in one pass; rows a
 // multiple of 128, cols a multiple of 128 with the row-wise cast, else of 8.

@@ -16,6 +16,7 @@
  *   te_fp8_gemm_dgrad_quant           as the next GEMM's fp8 operand
  *   te_fp8_gemm_dgrad_deterministic   the bias gradient without atomics
  *                                     (te_fp8_dgrad_bgrad_workspace_bytes)
+ *   te_fp8_wgrad_accum_bgrad          the bias gradient beside the weight gradient
  *   te_fp8_kgrouped_wgrad_device_sizes  expert sizes in device memory
  *   te_fp8_mgrouped_gemm_fwd          the experts' forward (and plain data gradient)
  *   te_fp8_mgrouped_gemm_dgrad        the experts' data gradient with dGELU and
@@ -353,6 +354,27 @@ te_status_t te_fp8_wgrad_accum(const void* a, const float* a_scales, te_dtype_t 
                                int64_t M, int64_t N, int64_t K,
                                float* out, int64_t ld_out,
                                te_accum_t accum, hipStream_t stream);
+
+/*
+ * The weight gradient with the bias gradient taken from its own operand: the
+ * reduction over tokens that gives the bias gradient is the row sum of
+ * A = dY^T, so the call adds
+ *   bias_grad[m] = sum_k a[m][k]     (dequantised fp8 A, fp32; overwritten)
+ * to te_fp8_wgrad_accum's out += A * B^T.  The pages place the bias
+ * gradient's reduction in the GEMM library next to the weight-gradient GEMM
+ * (the BGRADB epilogue among the cuBLASLt-style ones); here it is a second,
+ * HBM-bound kernel over A's codes and scales (K + K/32 bytes per row).  It
+ * sums the fp8 operand, so it differs from the sum of the bf16 gradient by
+ * the cast's rounding (half an fp8 ulp per element at most).
+ *
+ *  bias_grad  [M] fp32, 4-byte aligned
+ *  everything else as te_fp8_wgrad_accum
+ */
+te_status_t te_fp8_wgrad_accum_bgrad(const void* a, const float* a_scales, te_dtype_t a_dtype,
+                                     const void* b, const float* b_scales, te_dtype_t b_dtype,
+                                     int64_t M, int64_t N, int64_t K,
+                                     float* out, int64_t ld_out, float* bias_grad,
+                                     te_accum_t accum, hipStream_t stream);
 
 /*
  * K-grouped weight gradient for mixture-of-experts layers: expert g owns the

@@ -156,6 +156,16 @@ def cast_per_token_transpose(x_bf16_bits, fmt: int, pow2: bool = False):
     return q, s, qt, st
 
 
+def operand_row_sums(q, s, fmt: int):
+    """sum_k dec(q[r, k]) * s[r, k/128] per row, in fp64 (the bias gradient as the row sums of the
+    fp8 operand dY^T); also the |.|-magnitude of each sum.  Scales row-major [rows][K/128]."""
+    q = _c(q, np.uint8)
+    s = _c(s, np.float32).astype(np.float64)
+    rows, K = q.shape
+    dec = decode(q, fmt).reshape(rows, K // 128, 128)
+    return (dec.sum(-1) * s).sum(-1), (np.abs(dec).sum(-1) * s).sum(-1)
+
+
 # ------------------------------------------------------------------ GEMM
 def gemm_nt(qa, sa, fa, qb, sb, fb, k0: int = 0, K: int | None = None):
     """o[m,n] = sum_kb sA sB sum_k dec(qa[m,k]) dec(qb[n,k]); d = same with |terms|."""

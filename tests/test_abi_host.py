@@ -208,6 +208,14 @@ def test_dgrad_deterministic_rejects(lib, kw, status):
     assert dgd(lib, **kw) == status
 
 
+def test_wgrad_bgrad_rejects(lib):
+    f = lib.te_fp8_wgrad_accum_bgrad
+    assert f(p(A), p(S), 1, p(B), p(S), 1, 256, 256, 256, p(O), 256, None, 1, None) == INV
+    assert f(p(A), p(S), 1, p(B), p(S), 1, 256, 256, 256, p(O), 256, p(Z + 2), 1, None) == MISAL
+    assert f(p(A), p(S), 1, p(B), p(S), 1, 256, 256, 100, p(O), 256, p(Z), 1, None) == INV
+    assert f(p(A), p(S), 1, p(B), p(S), 1, 256, 256, 256, p(O), 100, p(Z), 1, None) == INV
+
+
 MB = 0xA0000  # dummy device address of the per-block experts
 
 

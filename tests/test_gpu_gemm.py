@@ -87,6 +87,29 @@ def test_wgrad_max_k(accum, pow2):
     check_f32(host(out).numpy(), want, mag, "wgrad K=2^22")
 
 
+@pytest.mark.parametrize("da", [E4, E5])
+@pytest.mark.parametrize("M,N,K", [(300, 200, 384), (7, 16, 1024), (513, 64, 128)])
+def test_wgrad_with_bias_grad(da, M, N, K):
+    """out += A B^T exactly as the plain call, plus bias_grad[m] = the dequantised row sums of A."""
+    qa, sa = operand(M + K + 7, M, K, da)
+    qb, sb = operand(N + K + 8, N, K, E4)
+    out0 = W.normal_f32(np.random.SeedSequence(M + 9), (M, N))
+    A, SA, B, SB = dev(qa), sdev(sa), dev(qb), sdev(sb)
+    ld = N + 4 - N % 4
+    out = torch.empty((M, ld), dtype=torch.float32, device="cuda")[:, :N]
+    out.copy_(dev(out0))
+    ref = torch.empty((M, ld), dtype=torch.float32, device="cuda")[:, :N]
+    ref.copy_(dev(out0))
+    bg = torch.full((M + 3,), 5.0, dtype=torch.float32, device="cuda")
+    te.te_fp8_wgrad_accum_bgrad(A, SA, da, B, SB, E4, out, bg[:M], FULL)
+    te.te_fp8_wgrad_accum(A, SA, da, B, SB, E4, ref, FULL)
+    assert torch.equal(host(out).view(torch.int32), host(ref).view(torch.int32))
+    g = host(bg).numpy()
+    assert np.all(g[M:] == 5.0)
+    want, mag = oracle.operand_row_sums(qa, sa, OF[da])
+    check_f32(g[:M], want, mag, "bias grad from A")
+
+
 def test_wgrad_pages_ones_example():
     """out1 = ref.clone(); out1 += x y^T makes out1/ref ~ 2; zero-initialised out gives ~ref."""
     m, n, k = 512, 1024, 4096

@@ -224,6 +224,25 @@ def test_cast_transpose_groups_run_down_the_columns(fmt):
     assert np.all(np.abs(top[nz]) == float(fmax)) and (qt[7, 128:] == 0).all()
 
 
+def test_operand_row_sums_ones_example_and_brute_force():
+    """The pages' all-ones operand: every code is 448 with scale fl32(1/448), so each row sums to
+    K * 448 * fl32(1/448); and a brute-force double loop on random codes."""
+    q, s = oracle.cast_per_token(bits(np.ones((3, 512))), oracle.E4M3)
+    r, mag = oracle.operand_row_sums(q, s, oracle.E4M3)
+    want = 512 * 448.0 * float(np.float32(1.0 / 448.0))
+    assert np.all(r == want) and np.all(mag == want)
+    rng = np.random.default_rng(5)
+    q = rng.integers(0, 256, (4, 256), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0                           # no NaN codes
+    s = rng.uniform(0.5, 2.0, (4, 2)).astype(np.float32)
+    r, _ = oracle.operand_row_sums(q, s, oracle.E4M3)
+    for i in range(4):
+        acc = 0.0
+        for k in range(256):
+            acc += float(oracle.decode(q[i:i + 1, k:k + 1], oracle.E4M3)[0, 0]) * float(s[i, k // 128])
+        assert abs(acc - r[i]) <= 1e-12 * max(1.0, abs(acc))
+
+
 def test_cast_rejects_non_finite():
     xb = bits(np.ones((1, 128)))
     xb[0, 5] = 0x7F80  # +inf
