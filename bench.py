@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=7168, help="rows of the oracle's CPU sample")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="minimum CPU time of the oracle sample")
     ap.add_argument("--cold-steps", type=int, default=30, help="steps timed after a cache flush each")
+    ap.add_argument("--case", default=None, help="run one named workload alone (see GROUPS) and print its time")
+    ap.add_argument("--reps", type=int, default=20, help="launches of --case")
+    ap.add_argument("--breakdown-rounds", type=int, default=20)
     ap.add_argument("--ref-copy", action="store_true",
                     help="first run three plain 1 GiB device copies (reference for HBM byte counters)")
     return ap.parse_args()
@@ -99,193 +102,312 @@ def timed(fn, reps, warm=3, rounds=3):
     return float(np.median(times)), float(np.min(times))
 
 
-def breakdown(te, torch):
-    """Kernel times of the other workloads (inputs generated on the GPU, seeded)."""
-    dev = "cuda"
-    g = torch.Generator(device=dev)
-    out = {}
+def timed_interleaved(fns, reps, rounds, warm=3):
+    """The kernel times of several launches measured in turn: each round times `reps` back-to-back
+    launches of every fn (one event pair each), in the same order, so a drifting clock affects them
+    alike.  Returns name -> list of per-launch times (ms), one per round."""
+    import torch
+    for fn in fns.values():
+        for _ in range(warm):
+            fn()
+    stream = torch.cuda.current_stream()
+    out = {k: [] for k in fns}
+    for _ in range(rounds):
+        evs = []
+        for k, fn in fns.items():
+            st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            st.record(stream)
+            for _ in range(reps):
+                fn()
+            en.record(stream)
+            evs.append((k, st, en))
+        evs[-1][2].synchronize()
+        for k, st, en in evs:
+            out[k].append(st.elapsed_time(en) / reps)
+    return out
 
-    def randn(shape, std, seed):
-        g.manual_seed(seed)
-        return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
 
-    E4, E5 = te.TE_DTYPE_E4M3, te.TE_DTYPE_E5M2
-    # tiny fprop 256 x 256 x 512 with bias + GELU, fp32 out, and the wgrad out += call on the same
-    # operands: latency-bound (one workgroup), reported in microseconds
-    xt, wt_, bt = randn((256, 512), 1.0, 21), randn((256, 512), 1.0, 22), randn((256,), 0.1, 23)
+class Case:
+    """One timed launch: fn, its flop (GEMMs) or algorithmic bytes (HBM-bound kernels)."""
+
+    def __init__(self, fn, flop=None, nbytes=None, note=None):
+        self.fn, self.flop, self.nbytes, self.note = fn, flop, nbytes, note
+
+
+def _randn(torch, g, shape, std, seed):
+    g.manual_seed(seed)
+    return (torch.randn(shape, generator=g, device="cuda", dtype=torch.float32) * std).to(torch.bfloat16)
+
+
+def group_tiny(te, torch, g):
+    """256 x 256 x 512: bias + GELU fprop (fp32 out) and the wgrad += call on the same operands."""
+    E4 = te.TE_DTYPE_E4M3
+    xt, wt_, bt = _randn(torch, g, (256, 512), 1.0, 21), _randn(torch, g, (256, 512), 1.0, 22), \
+        _randn(torch, g, (256,), 0.1, 23)
     qxt, sxt = te.te_cast_fp8_per_token(xt, E4)
     qwt, swt = te.te_cast_fp8_per_token(wt_, E4)
-    yt = torch.empty((256, 256), dtype=torch.float32, device=dev)
-    ot = torch.zeros((256, 256), dtype=torch.float32, device=dev)
-    med, _ = timed(lambda: te.te_fp8_gemm_fwd(qxt, sxt, E4, qwt, swt, E4, bias=bt,
-                                              epilogue=te.TE_EPI_BIAS | te.TE_EPI_GELU, y=yt,
-                                              y_dtype=te.TE_DTYPE_F32, accum=te.TE_ACCUM_FULL_FP32), 50)
-    out["tiny_fprop_bias_gelu_256x256x512"] = {"us": round(med * 1e3, 2)}
-    med, _ = timed(lambda: te.te_fp8_wgrad_accum(qxt, sxt, E4, qwt, swt, E4, ot, te.TE_ACCUM_FULL_FP32), 50)
-    out["tiny_wgrad_256x256x512"] = {"us": round(med * 1e3, 2)}
-    del xt, wt_, bt, qxt, sxt, qwt, swt, yt, ot
+    yt = torch.empty((256, 256), dtype=torch.float32, device="cuda")
+    ot = torch.zeros((256, 256), dtype=torch.float32, device="cuda")
+    f = 2.0 * 256 * 256 * 512
+    return {
+        "tiny_fprop_bias_gelu_256x256x512": Case(
+            lambda: te.te_fp8_gemm_fwd(qxt, sxt, E4, qwt, swt, E4, bias=bt, epilogue=te.TE_EPI_BIAS | te.TE_EPI_GELU,
+                                       y=yt, y_dtype=te.TE_DTYPE_F32, accum=te.TE_ACCUM_FULL_FP32), f),
+        "tiny_wgrad_256x256x512": Case(
+            lambda: te.te_fp8_wgrad_accum(qxt, sxt, E4, qwt, swt, E4, ot, te.TE_ACCUM_FULL_FP32), f),
+    }, []
 
-    # fprop 8192 x 14336 x 4096, bias + GELU (+ saved pre-activation), bf16 out
+
+def group_dense_wgrad(te, torch, g):
+    """7168 x 2112 x 4096 weight gradient: FULL on IEEE-scaled operands (the headline kernel), FULL and
+    FAST on power-of-two-scaled operands, the batched cast of both operands, and the step from
+    token-major sources through the cast-transpose."""
+    E4 = te.TE_DTYPE_E4M3
+    T, M, N = 4096, 7168, 2112
+    a, b = _randn(torch, g, (M, T), 1.0, 16), _randn(torch, g, (N, T), 1.0, 17)
+    qa, sa = te.te_cast_fp8_per_token(a, E4)
+    qb, sb = te.te_cast_fp8_per_token(b, E4)
+    pa, psa = te.te_cast_fp8_per_token(a, E4, te.TE_CAST_POW2_SCALE)
+    pb, psb = te.te_cast_fp8_per_token(b, E4, te.TE_CAST_POW2_SCALE)
+    o = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    dyt, xt = _randn(torch, g, (T, M), 1.0, 11), _randn(torch, g, (T, N), 1.0, 12)
+    qa2 = torch.empty((M, T), dtype=torch.uint8, device="cuda")
+    sa2 = torch.empty((T // 128, te.scale_ld(M)), dtype=torch.float32, device="cuda")
+    qb2 = torch.empty((N, T), dtype=torch.uint8, device="cuda")
+    sb2 = torch.empty((T // 128, te.scale_ld(N)), dtype=torch.float32, device="cuda")
+
+    def token_major():
+        te.te_cast_fp8_per_token_transpose(dyt, E4, rowwise=False, qt=qa2, scales_t=sa2)
+        te.te_cast_fp8_per_token_transpose(xt, E4, rowwise=False, qt=qb2, scales_t=sb2)
+        te.te_fp8_wgrad_accum(qa2, sa2, E4, qb2, sb2, E4, o, te.TE_ACCUM_FULL_FP32)
+
+    f = 2.0 * M * N * T
+    cast_bytes = (M + N) * T * 3 + (M + N) * (T // 128) * 4
+    return {
+        "wgrad_full_7168x2112x4096": Case(lambda: te.te_fp8_wgrad_accum(qa, sa, E4, qb, sb, E4, o,
+                                                                        te.TE_ACCUM_FULL_FP32), f),
+        "wgrad_pow2_full_7168x2112x4096": Case(lambda: te.te_fp8_wgrad_accum(pa, psa, E4, pb, psb, E4, o,
+                                                                             te.TE_ACCUM_FULL_FP32), f),
+        "wgrad_pow2_fast_7168x2112x4096": Case(lambda: te.te_fp8_wgrad_accum(pa, psa, E4, pb, psb, E4, o,
+                                                                             te.TE_ACCUM_FAST), f),
+        "cast_batch_e4m3_7168x4096_2112x4096": Case(
+            lambda: te.te_cast_fp8_per_token_batch([a, b], E4, qs=[qa, qb], scales=[sa, sb]), nbytes=cast_bytes),
+        "wgrad_from_token_major_7168x2112x4096": Case(
+            token_major, f, note="cast-transpose dY and X (tokens x features, bf16) + out += A B^T"),
+    }, [("wgrad_pow2_full_7168x2112x4096", "wgrad_pow2_fast_7168x2112x4096")]
+
+
+def group_fprop(te, torch, g):
+    """8192 x 14336 x 4096 forward, bf16 out: NONE vs bias+GELU (+aux) in both policies, FAST on IEEE
+    scales (every tile falls back to FULL) and on power-of-two scales, the quantising store, and the
+    casts of the activation."""
+    E4 = te.TE_DTYPE_E4M3
     M, N, K = 8192, 14336, 4096
-    x, w, b = randn((M, K), 1.0, 1), randn((N, K), 0.02, 2), randn((N,), 0.1, 3)
+    x, w, b = _randn(torch, g, (M, K), 1.0, 1), _randn(torch, g, (N, K), 0.02, 2), _randn(torch, g, (N,), 0.1, 3)
     qx, sx = te.te_cast_fp8_per_token(x, E4)
     qw, sw = te.te_cast_fp8_per_token(w, E4)
     px, psx = te.te_cast_fp8_per_token(x, E4, te.TE_CAST_POW2_SCALE)
     pw, psw = te.te_cast_fp8_per_token(w, E4, te.TE_CAST_POW2_SCALE)
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    z = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    flop = 2.0 * M * N * K
-    cases = {
-        "fprop_none_full": (qx, sx, qw, sw, te.TE_EPI_NONE, te.TE_ACCUM_FULL_FP32),
-        "fprop_bias_gelu_full": (qx, sx, qw, sw, te.TE_EPI_BIAS | te.TE_EPI_GELU, te.TE_ACCUM_FULL_FP32),
-        "fprop_none_fast": (qx, sx, qw, sw, te.TE_EPI_NONE, te.TE_ACCUM_FAST),
-        "fprop_none_fast_pow2": (px, psx, pw, psw, te.TE_EPI_NONE, te.TE_ACCUM_FAST),
-        "fprop_bias_gelu_fast_pow2": (px, psx, pw, psw, te.TE_EPI_BIAS | te.TE_EPI_GELU, te.TE_ACCUM_FAST),
-        "fprop_bias_gelu_aux_fast_pow2": (px, psx, pw, psw, te.TE_EPI_BIAS | te.TE_EPI_GELU | te.TE_EPI_AUX_PREACT,
-                                          te.TE_ACCUM_FAST),
-    }
-    for name, (a, sa, bb, sb, epi, acc) in cases.items():
-        fn = lambda: te.te_fp8_gemm_fwd(a, sa, E4, bb, sb, E4, bias=b if epi & te.TE_EPI_BIAS else None,
-                                        epilogue=epi, y=y, preact=z if epi & te.TE_EPI_AUX_PREACT else None,
-                                        accum=acc)
-        med, mn = timed(fn, 10)
-        out[name] = {"shape": [M, N, K], "ms": round(med, 4), "tflops": round(flop / med / 1e9, 1)}
-    # the same forward storing its per-token e4m3 cast (the next layer's operand) instead of bf16 y
-    qy = torch.empty((M, N), dtype=torch.uint8, device=dev)
-    qys = torch.empty((N // 128, te.scale_ld(M)), dtype=torch.float32, device=dev)
-    med, _ = timed(lambda: te.te_fp8_gemm_fwd_quant(px, psx, E4, pw, psw, E4, bias=b,
-                                                    epilogue=te.TE_EPI_BIAS | te.TE_EPI_GELU, q=qy, q_scales=qys,
-                                                    accum=te.TE_ACCUM_FAST), 10)
-    out["fprop_bias_gelu_quant_e4m3_fast_pow2"] = {"shape": [M, N, K], "ms": round(med, 4),
-                                                   "tflops": round(flop / med / 1e9, 1)}
-    del qy, qys
-    cast_bytes = M * K * 2 + M * K + M * (K // 128) * 4
-    med, _ = timed(lambda: te.te_cast_fp8_per_token(x, E4, q=qx, scales=sx), 10)
-    out["cast_e4m3_8192x4096"] = {"ms": round(med, 4), "gbs": round(cast_bytes / med / 1e6, 1),
-                                  "frac_hbm": round(cast_bytes / med / 1e6 / HBM_PEAK_GBS, 3)}
-    # fused cast + cast-transpose of the same activation (fprop operand and wgrad operand from one read)
-    ct_bytes = M * K * 2 + 2 * M * K + 2 * M * (K // 128) * 4
-    qxt, sxt = torch.empty((K, M), dtype=torch.uint8, device=dev), torch.empty((M // 128, te.scale_ld(K)),
-                                                                                dtype=torch.float32, device=dev)
-    med, _ = timed(lambda: te.te_cast_fp8_per_token_transpose(x, E4, q=qx, scales=sx, qt=qxt, scales_t=sxt), 10)
-    out["cast_and_transpose_e4m3_8192x4096"] = {"ms": round(med, 4), "gbs": round(ct_bytes / med / 1e6, 1),
-                                                "frac_hbm": round(ct_bytes / med / 1e6 / HBM_PEAK_GBS, 3)}
-    del qxt, sxt
-    del x, w, qw, sw, px, psx, pw, psw, y
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    z = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    qy = torch.empty((M, N), dtype=torch.uint8, device="cuda")
+    qys = torch.empty((N // 128, te.scale_ld(M)), dtype=torch.float32, device="cuda")
+    BG, BGA = te.TE_EPI_BIAS | te.TE_EPI_GELU, te.TE_EPI_BIAS | te.TE_EPI_GELU | te.TE_EPI_AUX_PREACT
+    FULL, FAST = te.TE_ACCUM_FULL_FP32, te.TE_ACCUM_FAST
+    f = 2.0 * M * N * K
 
-    # dgrad: dX [8192 x 4096] = dY [8192 x 14336] (e5m2) W^T (e4m3)
+    def fw(a, sa, bb, sb, epi, acc):
+        return lambda: te.te_fp8_gemm_fwd(a, sa, E4, bb, sb, E4, bias=b if epi & te.TE_EPI_BIAS else None,
+                                          epilogue=epi, y=y, preact=z if epi & te.TE_EPI_AUX_PREACT else None,
+                                          accum=acc)
+
+    qxt = torch.empty((K, M), dtype=torch.uint8, device="cuda")
+    sxt = torch.empty((M // 128, te.scale_ld(K)), dtype=torch.float32, device="cuda")
+    cast_bytes = M * K * 3 + M * (K // 128) * 4
+    ct_bytes = M * K * 2 + 2 * M * K + 2 * M * (K // 128) * 4
+    cases = {
+        "fprop_none_full": Case(fw(qx, sx, qw, sw, te.TE_EPI_NONE, FULL), f),
+        "fprop_bias_gelu_full": Case(fw(qx, sx, qw, sw, BG, FULL), f),
+        "fprop_none_fast": Case(fw(qx, sx, qw, sw, te.TE_EPI_NONE, FAST), f,
+                                note="IEEE scales: every tile takes the FULL update"),
+        "fprop_none_fast_pow2": Case(fw(px, psx, pw, psw, te.TE_EPI_NONE, FAST), f),
+        "fprop_bias_gelu_fast_pow2": Case(fw(px, psx, pw, psw, BG, FAST), f),
+        "fprop_bias_gelu_aux_fast_pow2": Case(fw(px, psx, pw, psw, BGA, FAST), f),
+        "fprop_bias_gelu_quant_e4m3_fast_pow2": Case(
+            lambda: te.te_fp8_gemm_fwd_quant(px, psx, E4, pw, psw, E4, bias=b, epilogue=BG, q=qy, q_scales=qys,
+                                             accum=FAST), f),
+        "cast_e4m3_8192x4096": Case(lambda: te.te_cast_fp8_per_token(x, E4, q=qx, scales=sx), nbytes=cast_bytes),
+        "cast_and_transpose_e4m3_8192x4096": Case(
+            lambda: te.te_cast_fp8_per_token_transpose(x, E4, q=qx, scales=sx, qt=qxt, scales_t=sxt), nbytes=ct_bytes),
+    }
+    pairs = [("fprop_none_full", "fprop_bias_gelu_full"), ("fprop_none_full", "fprop_none_fast"),
+             ("fprop_none_fast_pow2", "fprop_bias_gelu_fast_pow2"),
+             ("fprop_none_fast_pow2", "fprop_bias_gelu_aux_fast_pow2"),
+             ("fprop_bias_gelu_fast_pow2", "fprop_bias_gelu_quant_e4m3_fast_pow2")]
+    return cases, pairs
+
+
+def group_dgrad(te, torch, g):
+    """dX [8192 x 4096] = dY [8192 x 14336] (e5m2) W^T (e4m3); the gradient at the pre-activation shape
+    [8192 x 14336] (contraction 4096) plain, with dGELU + bias-grad (atomic, deterministic, quantising
+    to e5m2); the e5m2 cast of the gradient."""
+    E4, E5 = te.TE_DTYPE_E4M3, te.TE_DTYPE_E5M2
+    FULL, FAST = te.TE_ACCUM_FULL_FP32, te.TE_ACCUM_FAST
     M, N, K = 8192, 4096, 14336
-    dy, wt = randn((M, K), 1e-3, 4), randn((N, K), 0.02, 5)
+    dy, wt = _randn(torch, g, (M, K), 1e-3, 4), _randn(torch, g, (N, K), 0.02, 5)
     qd, sd = te.te_cast_fp8_per_token(dy, E5)
     qt, st = te.te_cast_fp8_per_token(wt, E4)
-    dx = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    med, _ = timed(lambda: te.te_fp8_gemm_dgrad(qd, sd, E5, qt, st, E4, dx=dx, accum=te.TE_ACCUM_FULL_FP32), 10)
-    out["dgrad_dx_full"] = {"shape": [M, N, K], "ms": round(med, 4), "tflops": round(2.0 * M * N * K / med / 1e9, 1)}
-    cast_bytes = M * K * 2 + M * K + M * (K // 128) * 4
-    med, _ = timed(lambda: te.te_cast_fp8_per_token(dy, E5, q=qd, scales=sd), 10)
-    out["cast_e5m2_8192x14336"] = {"ms": round(med, 4), "gbs": round(cast_bytes / med / 1e6, 1),
-                                   "frac_hbm": round(cast_bytes / med / 1e6 / HBM_PEAK_GBS, 3)}
-    del dy, wt, qd, sd, qt, st, dx
-    # dgrad with dGELU + bias-grad at the pre-activation shape [8192 x 14336], contraction 4096
-    M, N, K = 8192, 14336, 4096
-    do, w2t, zz = randn((M, K), 1e-3, 6), randn((N, K), 0.02, 7), randn((M, N), 1.28, 8)
+    dx = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    f = 2.0 * M * N * K
+    cast_bytes = M * K * 3 + M * (K // 128) * 4
+    M2, N2, K2 = 8192, 14336, 4096
+    do, w2t, zz = _randn(torch, g, (M2, K2), 1e-3, 6), _randn(torch, g, (N2, K2), 0.02, 7), \
+        _randn(torch, g, (M2, N2), 1.28, 8)
     qo, so = te.te_cast_fp8_per_token(do, E5)
     q2, s2 = te.te_cast_fp8_per_token(w2t, E4)
-    dz = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    bg = torch.empty((N,), dtype=torch.float32, device=dev)
-    med0, _ = timed(lambda: te.te_fp8_gemm_dgrad(qo, so, E5, q2, s2, E4, dx=dz, accum=te.TE_ACCUM_FULL_FP32), 10)
-    med1, _ = timed(lambda: te.te_fp8_gemm_dgrad(qo, so, E5, q2, s2, E4, epilogue=te.TE_EPI_DGELU | te.TE_EPI_BGRAD,
-                                                 preact=zz, bias_grad=bg, dx=dz, accum=te.TE_ACCUM_FULL_FP32), 10)
-    f = 2.0 * M * N * K
-    out["dgrad_dz_none_full"] = {"shape": [M, N, K], "ms": round(med0, 4), "tflops": round(f / med0 / 1e9, 1)}
-    out["dgrad_dz_dgelu_bgrad_full"] = {"shape": [M, N, K], "ms": round(med1, 4), "tflops": round(f / med1 / 1e9, 1),
-                                        "epilogue_overhead": round(med1 / med0 - 1.0, 3)}
-    # the same with the bias gradient summed in a fixed order through a workspace (no atomics)
-    ws = torch.empty((te.load_library().te_fp8_dgrad_bgrad_workspace_bytes(M, N),), dtype=torch.uint8, device=dev)
-    med3, _ = timed(lambda: te.te_fp8_gemm_dgrad_deterministic(qo, so, E5, q2, s2, E4, bg,
-                                                               epilogue=te.TE_EPI_DGELU | te.TE_EPI_BGRAD, preact=zz,
-                                                               workspace=ws, dx=dz, accum=te.TE_ACCUM_FULL_FP32), 10)
-    out["dgrad_dz_dgelu_bgrad_deterministic_full"] = {"shape": [M, N, K], "ms": round(med3, 4),
-                                                      "tflops": round(f / med3 / 1e9, 1)}
-    del ws
-    # the same with dZ stored as its per-token e5m2 cast (the next data-gradient GEMM's operand)
-    qz = torch.empty((M, N), dtype=torch.uint8, device=dev)
-    qzs = torch.empty((N // 128, te.scale_ld(M)), dtype=torch.float32, device=dev)
-    med2, _ = timed(lambda: te.te_fp8_gemm_dgrad_quant(qo, so, E5, q2, s2, E4, epilogue=te.TE_EPI_DGELU | te.TE_EPI_BGRAD,
-                                                       preact=zz, bias_grad=bg, q=qz, q_scales=qzs,
-                                                       accum=te.TE_ACCUM_FULL_FP32), 10)
-    out["dgrad_dz_dgelu_bgrad_quant_e5m2_full"] = {"shape": [M, N, K], "ms": round(med2, 4),
-                                                   "tflops": round(f / med2 / 1e9, 1)}
-    del qz, qzs
-    del do, w2t, zz, qo, so, q2, s2, dz, bg
+    dz = torch.empty((M2, N2), dtype=torch.bfloat16, device="cuda")
+    bg = torch.empty((N2,), dtype=torch.float32, device="cuda")
+    ws = torch.empty((te.load_library().te_fp8_dgrad_bgrad_workspace_bytes(M2, N2),), dtype=torch.uint8,
+                     device="cuda")
+    qz = torch.empty((M2, N2), dtype=torch.uint8, device="cuda")
+    qzs = torch.empty((N2 // 128, te.scale_ld(M2)), dtype=torch.float32, device="cuda")
+    f2 = 2.0 * M2 * N2 * K2
+    DB = te.TE_EPI_DGELU | te.TE_EPI_BGRAD
+    cases = {
+        "dgrad_dx_full": Case(lambda: te.te_fp8_gemm_dgrad(qd, sd, E5, qt, st, E4, dx=dx, accum=FULL), f),
+        "dgrad_dx_fast": Case(lambda: te.te_fp8_gemm_dgrad(qd, sd, E5, qt, st, E4, dx=dx, accum=FAST), f,
+                              note="IEEE scales: every tile takes the FULL update"),
+        "cast_e5m2_8192x14336": Case(lambda: te.te_cast_fp8_per_token(dy, E5, q=qd, scales=sd), nbytes=cast_bytes),
+        "dgrad_dz_none_full": Case(lambda: te.te_fp8_gemm_dgrad(qo, so, E5, q2, s2, E4, dx=dz, accum=FULL), f2),
+        "dgrad_dz_dgelu_bgrad_full": Case(
+            lambda: te.te_fp8_gemm_dgrad(qo, so, E5, q2, s2, E4, epilogue=DB, preact=zz, bias_grad=bg, dx=dz,
+                                         accum=FULL), f2),
+        "dgrad_dz_dgelu_bgrad_deterministic_full": Case(
+            lambda: te.te_fp8_gemm_dgrad_deterministic(qo, so, E5, q2, s2, E4, bg, epilogue=DB, preact=zz,
+                                                       workspace=ws, dx=dz, accum=FULL), f2),
+        "dgrad_dz_dgelu_bgrad_quant_e5m2_full": Case(
+            lambda: te.te_fp8_gemm_dgrad_quant(qo, so, E5, q2, s2, E4, epilogue=DB, preact=zz, bias_grad=bg, q=qz,
+                                               q_scales=qzs, accum=FULL), f2),
+    }
+    pairs = [("dgrad_dz_none_full", "dgrad_dz_dgelu_bgrad_full"),
+             ("dgrad_dz_none_full", "dgrad_dz_dgelu_bgrad_deterministic_full"),
+             ("dgrad_dz_dgelu_bgrad_full", "dgrad_dz_dgelu_bgrad_quant_e5m2_full")]
+    return cases, pairs
 
-    # the dense weight gradient on power-of-two-scaled operands with the FAST policy (scales applied
-    # inside the matrix-core instruction, no vector promotion) next to FULL on the same operands
-    T, M, N = 4096, 7168, 2112
-    pa, psa = te.te_cast_fp8_per_token(randn((M, T), 1.0, 16), E4, te.TE_CAST_POW2_SCALE)
-    pb, psb = te.te_cast_fp8_per_token(randn((N, T), 1.0, 17), E4, te.TE_CAST_POW2_SCALE)
-    o = torch.zeros((M, N), dtype=torch.float32, device=dev)
-    for name, acc in (("wgrad_pow2_full_7168x2112x4096", te.TE_ACCUM_FULL_FP32),
-                      ("wgrad_pow2_fast_7168x2112x4096", te.TE_ACCUM_FAST)):
-        med, _ = timed(lambda: te.te_fp8_wgrad_accum(pa, psa, E4, pb, psb, E4, o, acc), 10)
-        out[name] = {"ms": round(med, 4), "tflops": round(2.0 * M * N * T / med / 1e9, 1)}
-    del pa, psa, pb, psb, o
 
-    # the dense weight gradient from token-major sources: dY [4096 tokens x 7168] and X [4096 x 2112]
-    # are cast-transposed (1x128 groups along tokens) and fed to out += A B^T
-    T, M, N = 4096, 7168, 2112
-    dyt, xt = randn((T, M), 1.0, 11), randn((T, N), 1.0, 12)
-    qa = torch.empty((M, T), dtype=torch.uint8, device=dev)
-    sa = torch.empty((T // 128, te.scale_ld(M)), dtype=torch.float32, device=dev)
-    qb = torch.empty((N, T), dtype=torch.uint8, device=dev)
-    sb = torch.empty((T // 128, te.scale_ld(N)), dtype=torch.float32, device=dev)
-    o = torch.zeros((M, N), dtype=torch.float32, device=dev)
-
-    def wgrad_token_major():
-        te.te_cast_fp8_per_token_transpose(dyt, E4, rowwise=False, qt=qa, scales_t=sa)
-        te.te_cast_fp8_per_token_transpose(xt, E4, rowwise=False, qt=qb, scales_t=sb)
-        te.te_fp8_wgrad_accum(qa, sa, E4, qb, sb, E4, o, te.TE_ACCUM_FULL_FP32)
-
-    med, _ = timed(wgrad_token_major, 10)
-    out["wgrad_from_token_major_7168x2112x4096"] = {
-        "ms": round(med, 4), "tflops": round(2.0 * M * N * T / med / 1e9, 1),
-        "step": "cast-transpose dY and X (tokens x features, bf16) + out += A B^T"}
-    del dyt, xt, qa, sa, qb, sb, o
-
-    # K-grouped wgrad: 8 experts, 2048 x 7168, per-expert K multinomial in blocks of 128 summing to 32768
+def group_kgrouped(te, torch, g):
+    """8 experts, 2048 x 7168, per-expert K multinomial in blocks of 128 summing to 32768, FULL; the
+    group sizes on the host and on the device."""
     import workloads as W
+    E4 = te.TE_DTYPE_E4M3
     G, M, N, S = 8, 2048, 7168, 32768
     gk = W.moe_group_k(np.random.SeedSequence(5).spawn(4)[2], G, S).tolist()
-    a, bm = randn((M, S), 1.0, 9), randn((N, S), 1.0, 10)
+    a, bm = _randn(torch, g, (M, S), 1.0, 9), _randn(torch, g, (N, S), 1.0, 10)
     qa, sa = te.te_cast_fp8_per_token(a, E4)
     qb, sb = te.te_cast_fp8_per_token(bm, E4)
-    o = torch.zeros((G, M, N), dtype=torch.float32, device=dev)
-    med, _ = timed(lambda: te.te_fp8_kgrouped_wgrad(qa, sa, E4, qb, sb, E4, gk, o, te.TE_ACCUM_FULL_FP32), 10)
+    del a, bm
+    o = torch.zeros((G, M, N), dtype=torch.float32, device="cuda")
+    gk_dev = torch.tensor(gk, dtype=torch.int64, device="cuda")
     f = 2.0 * M * N * S
-    out["kgrouped_wgrad_full"] = {"group_k": gk, "ms": round(med, 4), "tflops": round(f / med / 1e9, 1)}
-    gk_dev = torch.tensor(gk, dtype=torch.int64, device=dev)
-    med, _ = timed(lambda: te.te_fp8_kgrouped_wgrad_device_sizes(qa, sa, E4, qb, sb, E4, gk_dev, o,
-                                                                 te.TE_ACCUM_FULL_FP32), 10)
-    out["kgrouped_wgrad_device_sizes_full"] = {"ms": round(med, 4), "tflops": round(f / med / 1e9, 1)}
-    del qa, sa, qb, sb, o, a, bm
+    return {
+        "kgrouped_wgrad_full": Case(lambda: te.te_fp8_kgrouped_wgrad(qa, sa, E4, qb, sb, E4, gk, o,
+                                                                     te.TE_ACCUM_FULL_FP32), f, note=str(gk)),
+        "kgrouped_wgrad_device_sizes_full": Case(
+            lambda: te.te_fp8_kgrouped_wgrad_device_sizes(qa, sa, E4, qb, sb, E4, gk_dev, o, te.TE_ACCUM_FULL_FP32), f),
+    }, []
 
-    # M-grouped expert forward: 8 experts x 1024 tokens (4 blocks of 256 rows each), N = 4096, K = 7168,
-    # bias + GELU, bf16 out
+
+def group_mgrouped(te, torch, g):
+    """M-grouped expert forward: 8 experts x 1024 tokens (4 blocks of 256 rows each), N = 4096,
+    K = 7168, bias + GELU, bf16 out."""
+    E4 = te.TE_DTYPE_E4M3
     G, T, N, K = 8, 8192, 4096, 7168
-    xg, wg, bg = randn((T, K), 1.0, 13), randn((G * N, K), 0.02, 14), randn((G, N), 0.1, 15)
+    xg, wg, bgs = _randn(torch, g, (T, K), 1.0, 13), _randn(torch, g, (G * N, K), 0.02, 14), \
+        _randn(torch, g, (G, N), 0.1, 15)
     qx, sx = te.te_cast_fp8_per_token(xg, E4)
     qw, sw = te.te_cast_fp8_per_token(wg, E4)
     qw = qw.view(G, N, K)
     # per-expert scale arrays in the [G][K/128][scale_ld(N)] layout (N is a multiple of 4)
     sw = sw.view(K // 128, G, N).permute(1, 0, 2).contiguous()
-    blocks = torch.arange(T // 256, device=dev, dtype=torch.int32) // ((T // 256) // G)
-    yg = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
-    med, _ = timed(lambda: te.te_fp8_mgrouped_gemm_fwd(qx, sx, E4, qw, sw, E4, blocks, bias=bg,
-                                                       epilogue=te.TE_EPI_BIAS | te.TE_EPI_GELU, y=yg,
-                                                       accum=te.TE_ACCUM_FULL_FP32), 10)
-    out["mgrouped_fwd_bias_gelu_full_8x1024x4096x7168"] = {"ms": round(med, 4),
-                                                           "tflops": round(2.0 * T * N * K / med / 1e9, 1)}
+    blocks = torch.arange(T // 256, device="cuda", dtype=torch.int32) // ((T // 256) // G)
+    yg = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    return {
+        "mgrouped_fwd_bias_gelu_full_8x1024x4096x7168": Case(
+            lambda: te.te_fp8_mgrouped_gemm_fwd(qx, sx, E4, qw, sw, E4, blocks, bias=bgs,
+                                                epilogue=te.TE_EPI_BIAS | te.TE_EPI_GELU, y=yg,
+                                                accum=te.TE_ACCUM_FULL_FP32), 2.0 * T * N * K),
+    }, []
+
+
+GROUPS = [group_tiny, group_dense_wgrad, group_fprop, group_dgrad, group_kgrouped, group_mgrouped]
+
+
+def _summ(case, times):
+    t = np.asarray(times)
+    med = float(np.median(t))
+    rec = {"ms": round(med, 5), "p10_ms": round(float(np.percentile(t, 10)), 5),
+           "p90_ms": round(float(np.percentile(t, 90)), 5), "rounds": int(t.size)}
+    if case.flop:
+        rec["tflops"] = round(case.flop / med / 1e9, 1)
+        rec["frac_fp8_peak"] = round(case.flop / med / 1e9 / MFMA_FP8_PEAK_TFLOPS, 4)
+    if case.nbytes:
+        rec["gbs"] = round(case.nbytes / med / 1e6, 1)
+        rec["frac_hbm"] = round(case.nbytes / med / 1e6 / HBM_PEAK_GBS, 4)
+    if case.note:
+        rec["note"] = case.note
+    return rec
+
+
+def breakdown(te, torch, rounds=20, reps=10):
+    """Every other workload's kernel time.  Within a group the cases are timed interleaved (each round
+    times every case once, `reps` back-to-back launches each), after a common warm-up; the median and
+    the 10th/90th percentiles over the rounds are reported, and each epilogue's overhead is the median
+    over rounds of its time divided by its base case's time in the same round."""
+    g = torch.Generator(device="cuda")
+    out = {}
+    for grp in GROUPS:
+        cases, pairs = grp(te, torch, g)
+        # settle the clocks on this group's first case before the measured rounds
+        first = next(iter(cases.values())).fn
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.3:
+            for _ in range(10):
+                first()
+            torch.cuda.synchronize()
+        n = reps if not grp.__name__.endswith("tiny") else 50
+        times = timed_interleaved({k: c.fn for k, c in cases.items()}, n, rounds)
+        for k, c in cases.items():
+            out[k] = _summ(c, times[k])
+            if k.startswith("tiny"):
+                out[k]["us"] = round(out[k]["ms"] * 1e3, 2)
+        for base, epi in pairs:
+            r = np.asarray(times[epi]) / np.asarray(times[base])
+            out[epi].setdefault("overhead_vs", {})[base] = {
+                "median": round(float(np.median(r)) - 1.0, 4),
+                "p10": round(float(np.percentile(r, 10)) - 1.0, 4),
+                "p90": round(float(np.percentile(r, 90)) - 1.0, 4)}
+        del cases
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     return out
+
+
+def run_case(te, torch, name, reps, warm):
+    """One case alone, `warm` + `reps` launches (the command the committed rocprofv3 summaries run)."""
+    g = torch.Generator(device="cuda")
+    for grp in GROUPS:
+        cases, _ = grp(te, torch, g)
+        if name in cases:
+            c = cases[name]
+            for _ in range(warm):
+                c.fn()
+            torch.cuda.synchronize()
+            times = timed_interleaved({name: c.fn}, 1, reps, warm=0)
+            rec = {"case": name, **_summ(c, times[name])}
+            print(json.dumps(rec), flush=True)
+            return
+        del cases
+    raise SystemExit(f"unknown case {name!r}")
 
 
 def cpu_baseline(rows: int, min_seconds: float):
@@ -312,9 +434,31 @@ def cpu_baseline(rows: int, min_seconds: float):
             break
     flop = 2.0 * rows * N * K * runs
     return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"{rows} of 7168 output rows (all 2112 columns, K=4096) incl. the cast of those rows and of B, "
                       f"{runs} run(s) in {dt:.1f} s"}
+
+
+def ref_copy(torch):
+    """Three plain 1 GiB device copies: the reference reading of the HBM byte counters."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def main():
@@ -329,6 +473,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     te.load_library()
     torch.cuda.set_device(0)
+    if args.case:
+        if args.ref_copy:
+            ref_copy(torch)
+        run_case(te, torch, args.case, args.reps, args.warmup)
+        return
     M, N, K = 7168, 2112, 4096
     inp = W.dense_wgrad_inputs()
     a = torch.from_numpy(inp["a"]).cuda().view(torch.bfloat16)
@@ -355,12 +504,7 @@ def main():
         te.te_cast_fp8_per_token_batch([a, b], E4, qs=[qa, qb], scales=[sa, sb])
 
     if args.ref_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        ref_copy(torch)
     # (the garbage collector is paused over the warm-up and timed steps, as
     # timeit does: a collection pass mid-loop leaves the GPU idle for ms)
     gc.collect()
@@ -433,7 +577,7 @@ def main():
                      "casts_ms": round(cast_ms, 5)},
     }
     if not args.no_breakdown:
-        rec["breakdown"] = breakdown(te, torch)
+        rec["breakdown"] = breakdown(te, torch, rounds=args.breakdown_rounds)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args.cpu_rows, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

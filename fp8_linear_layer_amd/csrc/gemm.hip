@@ -58,6 +58,10 @@
 
 #include <algorithm>
 
+#ifndef TE_GEMM_PART
+#define TE_GEMM_PART -1
+#endif
+
 #include "fp8_codec.h"
 #include "internal.h"
 #include "te_fp8.h"
@@ -1068,6 +1072,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p, int
     }
 }
 
+#if TE_GEMM_PART < 0 || TE_GEMM_PART == 4
 __global__ void zero_f32_kernel(float* p, int64_t n)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1085,6 +1090,8 @@ __global__ void bgrad_reduce_kernel(const float* __restrict__ ws, int64_t rows, 
     for (int64_t r = 0; r < rows; ++r) s += ws[r * ld + n];
     bias_grad[n] = s;
 }
+
+#endif
 
 template <int kFmtA, int kFmtB, bool kFast>
 hipError_t launch_epi(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s)
@@ -1114,6 +1121,39 @@ hipError_t launch_policy(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_
 
 }  // namespace
 
+// One translation unit per operand-format pair (TE_GEMM_PART 0-3) and one for
+// the host side (4), so the kernel instantiations compile in parallel; without
+// TE_GEMM_PART everything is in one unit.
+hipError_t launch_pair_e4_e4(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s);
+hipError_t launch_pair_e5_e4(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s);
+hipError_t launch_pair_e4_e5(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s);
+hipError_t launch_pair_e5_e5(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s);
+#if TE_GEMM_PART < 0 || TE_GEMM_PART == 0
+hipError_t launch_pair_e4_e4(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s)
+{
+    return launch_policy<FMT_E4M3, FMT_E4M3>(a, grid, tiles, s);
+}
+#endif
+#if TE_GEMM_PART < 0 || TE_GEMM_PART == 1
+hipError_t launch_pair_e5_e4(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s)
+{
+    return launch_policy<FMT_E5M2, FMT_E4M3>(a, grid, tiles, s);
+}
+#endif
+#if TE_GEMM_PART < 0 || TE_GEMM_PART == 2
+hipError_t launch_pair_e4_e5(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s)
+{
+    return launch_policy<FMT_E4M3, FMT_E5M2>(a, grid, tiles, s);
+}
+#endif
+#if TE_GEMM_PART < 0 || TE_GEMM_PART == 3
+hipError_t launch_pair_e5_e5(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s)
+{
+    return launch_policy<FMT_E5M2, FMT_E5M2>(a, grid, tiles, s);
+}
+#endif
+
+#if TE_GEMM_PART < 0 || TE_GEMM_PART == 4
 // Compute units of the current device (cached per device).
 int device_cus()
 {
@@ -1141,10 +1181,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream, LaunchInfo* info)
     }
     if (blocks <= 0) return hipSuccess;
     const dim3 grid((unsigned)blocks);
-    if (a.fmt_a == FMT_E4M3 && a.fmt_b == FMT_E4M3) return launch_policy<FMT_E4M3, FMT_E4M3>(a, grid, tiles, stream);
-    if (a.fmt_a == FMT_E5M2 && a.fmt_b == FMT_E4M3) return launch_policy<FMT_E5M2, FMT_E4M3>(a, grid, tiles, stream);
-    if (a.fmt_a == FMT_E4M3 && a.fmt_b == FMT_E5M2) return launch_policy<FMT_E4M3, FMT_E5M2>(a, grid, tiles, stream);
-    return launch_policy<FMT_E5M2, FMT_E5M2>(a, grid, tiles, stream);
+    if (a.fmt_a == FMT_E4M3 && a.fmt_b == FMT_E4M3) return launch_pair_e4_e4(a, grid, tiles, stream);
+    if (a.fmt_a == FMT_E5M2 && a.fmt_b == FMT_E4M3) return launch_pair_e5_e4(a, grid, tiles, stream);
+    if (a.fmt_a == FMT_E4M3 && a.fmt_b == FMT_E5M2) return launch_pair_e4_e5(a, grid, tiles, stream);
+    return launch_pair_e5_e5(a, grid, tiles, stream);
 }
 
 hipError_t launch_bgrad_reduce(const float* ws, int64_t rows, int64_t ld, int64_t N, float* bias_grad,
@@ -1162,5 +1202,6 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream)
     zero_f32_kernel<<<(unsigned)blocks, 256, 0, stream>>>(p, n);
     return hipGetLastError();
 }
+#endif
 
 }  // namespace tefp8

@@ -35,10 +35,12 @@
  *            bias vector always has length N, the output-feature count.
  *  Scales.   Operands are fp8 with one fp32 dequantisation scale per row and
  *            per 128 consecutive contraction elements ("1x128" groups): the
- *            value of element (r, k) is dec(q[r][k]) * s(r, k/128).  Scales
- *            are stored contraction-block-major, like the transposed,
- *            16-byte-aligned scale layout of the DeepGEMM weight-gradient
- *            kernels: s(r, kb) = scales[kb * te_scale_ld(rows) + r], i.e. an
+ *            value of element (r, k) is dec(q[r][k]) * s(r, k/128).  The
+ *            pages fix one fp32 scale per row and 128-element block but not
+ *            where it sits in memory; this library's own choice (not a
+ *            statement of the pages) stores them contraction-block-major,
+ *            so that a tile's row scales of one block are a single 16-byte
+ *            aligned run: s(r, kb) = scales[kb * te_scale_ld(rows) + r], i.e. an
  *            array [K/128][te_scale_ld(rows)] whose row kb holds the scales of
  *            all rows for block kb (entries r >= rows are padding, never
  *            used).  K must be a multiple of 128 and at most 2^22 (for the
@@ -398,8 +400,9 @@ te_status_t te_fp8_kgrouped_wgrad(const void* a, const float* a_scales, te_dtype
 /*
  * The same K-grouped weight gradient with the group sizes in device memory,
  * e.g. the per-expert token counts a router produced on the GPU: nothing is
- * read back to the host and the call does not synchronise (the pages' grouped
- * kernel takes its per-group layout on the device, not from the host).
+ * read back to the host and the call does not synchronise.  The pages name
+ * the grouped weight-gradient kernel but not where its group sizes live;
+ * reading them on the device is this library's own design choice.
  *
  *  a, a_scales   [M][sum_k] fp8, [sum_k/128][te_scale_ld(M)]
  *  b, b_scales   [N][sum_k] fp8, [sum_k/128][te_scale_ld(N)]

@@ -237,6 +237,28 @@ def mgrouped_fwd(qx, sx, fx, qw, sw, fw, m_block_group, bias_bits=None, gelu_on:
     return y, z, zm
 
 
+def mgrouped_dgrad(qa, sa, fa, qw, sw, fw, m_block_group, preact_bits=None, block: int = 256):
+    """The M-grouped data gradient by definition: every `block`-row slice of the gradient qa whose
+    expert e = m_block_group[i] is in [0, G) goes through gemm_nt with the expert's transposed
+    weight qw[e] and dgrad_epilogue (GELU' of its pre-activation rows, if given); expert e's bias
+    gradient is the sum of its blocks' column sums, zero for an expert with no block.  Returns
+    (D, Dmag, db [G, N], dbmag [G, N]) with NaN in the rows of skipped blocks."""
+    qa = _c(qa, np.uint8); sa = _c(sa, np.float32)
+    G, N, _ = qw.shape
+    M = qa.shape[0]
+    D = np.full((M, N), np.nan); Dm = np.full((M, N), np.nan)
+    db = np.zeros((G, N)); dbm = np.zeros((G, N))
+    for i, e in enumerate(np.asarray(m_block_group)):
+        if not 0 <= e < G:
+            continue
+        r = slice(i * block, (i + 1) * block)
+        o, d = gemm_nt(qa[r], sa[r], fa, qw[e], sw[e], fw)
+        D[r], Dm[r], dbi, dbmi = dgrad_epilogue(o, d, None if preact_bits is None else preact_bits[r], True)
+        db[e] += dbi
+        dbm[e] += dbmi
+    return D, Dm, db, dbm
+
+
 def dgrad_epilogue(o, d, preact_bits=None, bgrad: bool = False):
     """D = o * GELU'(z) (if preact given); db = column sums of D.  Returns (D, Dmag, db, dbmag)."""
     o = _c(o, np.float64); d = _c(d, np.float64)

@@ -208,12 +208,19 @@ def test_dgrad_deterministic_rejects(lib, kw, status):
     assert dgd(lib, **kw) == status
 
 
-def test_wgrad_bgrad_rejects(lib):
-    f = lib.te_fp8_wgrad_accum_bgrad
-    assert f(p(A), p(S), 1, p(B), p(S), 1, 256, 256, 256, p(O), 256, None, 1, None) == INV
-    assert f(p(A), p(S), 1, p(B), p(S), 1, 256, 256, 256, p(O), 256, p(Z + 2), 1, None) == MISAL
-    assert f(p(A), p(S), 1, p(B), p(S), 1, 256, 256, 100, p(O), 256, p(Z), 1, None) == INV
-    assert f(p(A), p(S), 1, p(B), p(S), 1, 256, 256, 256, p(O), 100, p(Z), 1, None) == INV
+def wgrad_bg(lib, a=A, sa=S, da=1, b=B, sb=S, db=1, M=256, N=256, K=256, out=O, ld=256, bg=Z, accum=1):
+    return lib.te_fp8_wgrad_accum_bgrad(p(a), p(sa), da, p(b), p(sb), db, M, N, K, p(out), ld, p(bg), accum, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bg=0), INV), (dict(bg=Z + 2), MISAL), (dict(K=100), INV), (dict(K=0), INV), (dict(ld=100), INV),
+    (dict(ld=258), MISAL), (dict(a=0), INV), (dict(b=0), INV), (dict(sa=0), INV), (dict(out=0), INV),
+    (dict(M=0), INV), (dict(N=-1), INV), (dict(da=5), INV), (dict(accum=0), INV), (dict(accum=7), INV),
+    (dict(a=MIS), MISAL), (dict(out=MIS), MISAL), (dict(sb=S + 4), MISAL), (dict(K=(1 << 22) + 128), INV),
+])
+def test_wgrad_bgrad_rejects(lib, kw, status):
+    assert wgrad_bg(lib, **kw) == status
+    assert "te_fp8_wgrad_accum_bgrad" in lib.te_last_error_message().decode()
 
 
 MB = 0xA0000  # dummy device address of the per-block experts

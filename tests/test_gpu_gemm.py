@@ -13,7 +13,8 @@ import torch
 
 import oracle
 import workloads as W
-from parity import GELU_LIP, bf16_dev, bf16_host_f64, check_bf16, check_f32, dev, host, scale_ld, sdev, shost
+from parity import (BIAS_CHAIN, GELU_CHAIN, GELU_LIP, bf16_dev, bf16_host_f64, chain_colsum, chain_gemm, chain_rowsum,
+                    check_bf16, check_f32, check_quant, dev, host, scale_ld, sdev, shost)
 
 te = pytest.importorskip("fp8_linear_layer_amd")
 pytestmark = pytest.mark.gpu
@@ -30,6 +31,12 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     te.load_library()
+
+
+def epi_chain(epi):
+    """Extra fp32 roundings of an epilogue (bias add, GELU or GELU')."""
+    return (BIAS_CHAIN if epi & te.TE_EPI_BIAS else 0) + \
+        (GELU_CHAIN if epi & (te.TE_EPI_GELU | te.TE_EPI_DGELU) else 0)
 
 
 def operand(seed, rows, K, dt, std=1.0, pow2=False):
@@ -70,7 +77,7 @@ def test_wgrad_small(accum, pow2, da, db, M, N, K):
     torch.cuda.synchronize()
     b = host(buf).numpy()
     assert (b[:M, N:] == 1234.5).all() and (b[M:] == 1234.5).all(), "wrote outside out"
-    check_f32(b[:M, :N], want, mag, "wgrad")
+    check_f32(b[:M, :N], want, mag, "wgrad", chain_gemm(K, 1))
 
 
 @pytest.mark.parametrize("accum,pow2", [(FULL, False), (FAST, True)], ids=["full", "fast-pow2"])
@@ -84,7 +91,7 @@ def test_wgrad_max_k(accum, pow2):
     want, mag = oracle.wgrad(o, d, out0)
     out = dev(out0)
     te.te_fp8_wgrad_accum(dev(qa), sdev(sa), E4, dev(qb), sdev(sb), E4, out, accum)
-    check_f32(host(out).numpy(), want, mag, "wgrad K=2^22")
+    check_f32(host(out).numpy(), want, mag, "wgrad K=2^22", chain_gemm(K, 1))
 
 
 @pytest.mark.parametrize("da", [E4, E5])
@@ -107,7 +114,7 @@ def test_wgrad_with_bias_grad(da, M, N, K):
     g = host(bg).numpy()
     assert np.all(g[M:] == 5.0)
     want, mag = oracle.operand_row_sums(qa, sa, OF[da])
-    check_f32(g[:M], want, mag, "bias grad from A")
+    check_f32(g[:M], want, mag, "bias grad from A", chain_rowsum(K), mma=False)
 
 
 def test_wgrad_pages_ones_example():
@@ -155,7 +162,8 @@ def test_wgrad_dense_workload(accum, pow2):
     rows, cols = sample_idx(sh["M"], 40, 1), sample_idx(sh["N"], 40, 2)
     o, d = grid_entries(qa, sa, oracle.E4M3, qb, sb, oracle.E4M3, rows, cols)
     init = inp["out0"][np.ix_(rows, cols)]
-    check_f32(got[np.ix_(rows, cols)], init.astype(np.float64) + o, np.abs(init) + d, "dense wgrad")
+    check_f32(got[np.ix_(rows, cols)], init.astype(np.float64) + o, np.abs(init) + d, "dense wgrad",
+              chain_gemm(sh["K"], 1))
 
 
 # ------------------------------------------------------------------ fprop
@@ -195,7 +203,7 @@ def test_fwd_small(accum, pow2, epi, ydt, M, N, K):
     yb = host(ybuf)
     assert torch.all(yb[:M, N:] == 77.0) and torch.all(yb[M:] == 77.0), "wrote outside y"
     if ydt == te.TE_DTYPE_F32:
-        check_f32(yb[:M, :N].numpy(), y, ymag, "fwd y")
+        check_f32(yb[:M, :N].numpy(), y, ymag, "fwd y", chain_gemm(K, epi_chain(epi)))
     else:
         check_bf16(bf16_host_f64(yb[:M, :N]), y, ymag, "fwd y")
     if pre is not None:
@@ -234,7 +242,8 @@ def test_fwd_quant(accum, pow2, epi, qdt, cast_pow2, M, N, K):
                              bias=bf16_dev(b) if epi & te.TE_EPI_BIAS else None, epilogue=epi & ~te.TE_EPI_AUX_PREACT,
                              y_dtype=te.TE_DTYPE_F32, accum=accum)
     y32h = host(y32).numpy()
-    check_f32(y32h, y, zmag * (GELU_LIP if epi & te.TE_EPI_GELU else 1.0), "fwd y (fp32)")
+    check_f32(y32h, y, zmag * (GELU_LIP if epi & te.TE_EPI_GELU else 1.0), "fwd y (fp32)",
+              chain_gemm(K, epi_chain(epi)))
     pre = None
     if epi & te.TE_EPI_AUX_PREACT:
         prebuf = torch.full((M, N + 8), 55.0, dtype=torch.bfloat16, device="cuda")
@@ -244,6 +253,9 @@ def test_fwd_quant(accum, pow2, epi, qdt, cast_pow2, M, N, K):
     bad = np.argwhere(q != qo)
     assert bad.size == 0, f"{len(bad)} code mismatches, first {bad[0]}"
     assert np.array_equal(s.view(np.uint32), so.view(np.uint32)), "scale mismatch"
+    # and the dequantised store against the fp64 oracle
+    check_quant(q, s, OF[qdt], y, zmag * (GELU_LIP if epi & te.TE_EPI_GELU else 1.0), "fwd quant vs oracle",
+                chain_gemm(K, epi_chain(epi)))
     if pre is not None:
         pb = host(prebuf)
         assert torch.all(pb[:, N:] == 55.0)
@@ -265,8 +277,16 @@ def test_fwd_quant_workload():
     rows = sample_idx(M, 24, 5)
     yr = host(y32[torch.from_numpy(rows).cuda()]).numpy()
     qo, so = oracle.cast_per_token_f32(yr, oracle.E4M3)
-    assert np.array_equal(host(q).numpy()[rows], qo)
-    assert np.array_equal(shost(qs, M)[rows].view(np.uint32), so.view(np.uint32))
+    qr, sr = host(q).numpy()[rows], shost(qs, M)[rows]
+    assert np.array_equal(qr, qo)
+    assert np.array_equal(sr.view(np.uint32), so.view(np.uint32))
+    # the sampled rows (every column) against the fp64 oracle: the fp32 y and the dequantised codes
+    o, d = oracle.gemm_nt(qx[rows], sx[rows], oracle.E4M3, qw, sw, oracle.E4M3)
+    y, _, zmag = oracle.fwd_epilogue(o, d, inp["b"], True)
+    K = qx.shape[1]
+    check_f32(yr, y, zmag * GELU_LIP, "fprop y32 rows", chain_gemm(K, BIAS_CHAIN + GELU_CHAIN))
+    check_quant(qr, sr, oracle.E4M3, y, zmag * GELU_LIP, "fprop quant rows vs oracle",
+                chain_gemm(K, BIAS_CHAIN + GELU_CHAIN))
 
 
 def test_fwd_tiny_workload():
@@ -279,11 +299,11 @@ def test_fwd_tiny_workload():
     for accum in (FULL, FAST):
         yg = te.te_fp8_gemm_fwd(dev(qx), sdev(sx), E4, dev(qw), sdev(sw), E4, bias=bf16_dev(inp["b"]),
                                 epilogue=te.TE_EPI_BIAS | te.TE_EPI_GELU, y_dtype=te.TE_DTYPE_F32, accum=accum)
-        check_f32(host(yg).numpy(), y, zmag * GELU_LIP, "tiny fwd")
+        check_f32(host(yg).numpy(), y, zmag * GELU_LIP, "tiny fwd", chain_gemm(512, BIAS_CHAIN + GELU_CHAIN))
     want, mag = oracle.wgrad(o, d, inp["out0"])
     out = dev(inp["out0"])
     te.te_fp8_wgrad_accum(dev(qx), sdev(sx), E4, dev(qw), sdev(sw), E4, out, FULL)
-    check_f32(host(out).numpy(), want, mag, "tiny wgrad")
+    check_f32(host(out).numpy(), want, mag, "tiny wgrad", chain_gemm(512, 1))
 
 
 @pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
@@ -330,13 +350,13 @@ def test_dgrad_small(accum, pow2, epi, dxdt, M, N, K):
     xb = host(dxbuf)
     assert torch.all(xb[:, N:] == 9.0), "wrote outside dx"
     if dxdt == te.TE_DTYPE_F32:
-        check_f32(xb[:, :N].numpy(), D, Dm, "dgrad dx")
+        check_f32(xb[:, :N].numpy(), D, Dm, "dgrad dx", chain_gemm(K, epi_chain(epi)))
     else:
         check_bf16(bf16_host_f64(xb[:, :N]), D, Dm, "dgrad dx")
     if bg is not None:
         g = host(bg).numpy()
         assert np.all(g[N:] == 3.0)
-        check_f32(g[:N], db, dbm, "bias grad")
+        check_f32(g[:N], db, dbm, "bias grad", chain_colsum(K, M, epi_chain(epi)))
 
 
 DGRAD_EPIS = [te.TE_EPI_NONE, te.TE_EPI_DGELU, te.TE_EPI_DGELU | te.TE_EPI_BGRAD]
@@ -362,7 +382,7 @@ def test_dgrad_quant(accum, pow2, epi, qdt, cast_pow2, M, N, K):
     d32 = te.te_fp8_gemm_dgrad(A, SA, E5, B, SB, E4, epilogue=epi & ~te.TE_EPI_BGRAD, preact=Z,
                                dx_dtype=te.TE_DTYPE_F32, accum=accum)
     d32h = host(d32).numpy()
-    check_f32(d32h, D, Dm, "dgrad D (fp32)")
+    check_f32(d32h, D, Dm, "dgrad D (fp32)", chain_gemm(K, epi_chain(epi)))
     qbuf = torch.full((M, N + 16), 0xA5, dtype=torch.uint8, device="cuda")
     qs = torch.full((N // 128, scale_ld(M)), -3.0, dtype=torch.float32, device="cuda")
     bg = torch.full((N + 4,), 3.0, dtype=torch.float32, device="cuda") if has_bg else None
@@ -376,10 +396,11 @@ def test_dgrad_quant(accum, pow2, epi, qdt, cast_pow2, M, N, K):
     bad = np.argwhere(qh[:, :N] != qo)
     assert bad.size == 0, f"{len(bad)} code mismatches, first {bad[0]}"
     assert np.array_equal(shost(qs, M).view(np.uint32), so.view(np.uint32)), "scale mismatch"
+    check_quant(qh[:, :N], shost(qs, M), OF[qdt], D, Dm, "dgrad quant vs oracle", chain_gemm(K, epi_chain(epi)))
     if has_bg:
         g = host(bg).numpy()
         assert np.all(g[N:] == 3.0)
-        check_f32(g[:N], db, dbm, "bias grad")
+        check_f32(g[:N], db, dbm, "bias grad", chain_colsum(K, M, epi_chain(epi)))
 
 
 @pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
@@ -410,7 +431,7 @@ def test_dgrad_deterministic_bias_grad(accum, pow2, epi, M, N, K):
         runs.append((host(bg).numpy(), host(dx).numpy()))
     for g, _ in runs[1:]:
         assert np.array_equal(g.view(np.uint32), runs[0][0].view(np.uint32)), "bias grad not deterministic"
-    check_f32(runs[0][0], db, dbm, "deterministic bias grad")
+    check_f32(runs[0][0], db, dbm, "deterministic bias grad", chain_colsum(K, M, epi_chain(epi)))
     ref = torch.empty((M, ld), dtype=torch.float32, device="cuda")[:, :N]
     te.te_fp8_gemm_dgrad(A, SA, E5, B, SB, E4, epilogue=epi & ~te.TE_EPI_BGRAD, preact=Z, dx=ref,
                          dx_dtype=te.TE_DTYPE_F32, accum=accum)
@@ -430,26 +451,41 @@ def test_dgrad_workload_dx(accum):
     check_bf16(bf16_host_f64(dx)[np.ix_(rows, cols)], o, d, "dgrad dX")
 
 
-def test_dgrad_workload_dgelu_bgrad():
-    """dZ[8192x14336] = dO (e5m2) W2^T (e4m3) through GELU'(Z), bias grad = its column sums."""
+@pytest.mark.parametrize("accum", [FULL, FAST])
+def test_dgrad_workload_dgelu_bgrad(accum):
+    """dZ[8192x14336] = dO (e5m2) W2^T (e4m3) through GELU'(Z), bias grad = its column sums.  dZ in
+    fp32 on a sampled grid against the oracle; the bias gradient on every column against the fp64
+    column sums of that same fp32 dZ, and on sampled columns against the oracle; the bf16 store is
+    the round-to-nearest-even of the fp32 one."""
     sh = W.DGRAD.shapes
     M, N, K = sh["M"], sh["K"], sh["N"]  # the pre-activation GEMM: out features 14336, contraction 4096
     inp = W.dgrad_inputs()
     qa, sa = oracle.cast_per_token(inp["do"], oracle.E5M2)
     qb, sb = oracle.cast_per_token(inp["w2t"], oracle.E4M3)
     z = inp["z"]
+    A, SA, B, SB, Z = dev(qa), sdev(sa), dev(qb), sdev(sb), bf16_dev(z)
+    epi = te.TE_EPI_DGELU | te.TE_EPI_BGRAD
     bg = torch.empty((N,), dtype=torch.float32, device="cuda")
-    dz = te.te_fp8_gemm_dgrad(dev(qa), sdev(sa), E5, dev(qb), sdev(sb), E4,
-                              epilogue=te.TE_EPI_DGELU | te.TE_EPI_BGRAD, preact=bf16_dev(z), bias_grad=bg,
-                              accum=FULL)
+    dz = te.te_fp8_gemm_dgrad(A, SA, E5, B, SB, E4, epilogue=epi, preact=Z, bias_grad=bg,
+                              dx_dtype=te.TE_DTYPE_F32, accum=accum)
     rows, cols = sample_idx(M, 16, 7), sample_idx(N, 24, 8)
     o, d = grid_entries(qa, sa, oracle.E5M2, qb, sb, oracle.E4M3, rows, cols)
     D, Dm, _, _ = oracle.dgrad_epilogue(o, d, z[np.ix_(rows, cols)])
-    check_bf16(bf16_host_f64(dz)[np.ix_(rows, cols)], D, Dm, "dZ")
+    dzh = host(dz).numpy()
+    check_f32(dzh[np.ix_(rows, cols)], D, Dm, "dZ fp32", chain_gemm(K, GELU_CHAIN))
+    g = host(bg).numpy()
+    # every column: the kernel's own fp32 dZ summed in fp64
+    cs = dzh.astype(np.float64).sum(0)
+    csm = np.abs(dzh.astype(np.float64)).sum(0)
+    check_f32(g, cs, csm, "bias grad vs colsum(dZ)", 4 + 4 + (M + 63) // 64, mma=False)
     bcols = cols[:8]
     o, d = grid_entries(qa, sa, oracle.E5M2, qb, sb, oracle.E4M3, np.arange(M), bcols)
     _, _, db, dbm = oracle.dgrad_epilogue(o, d, z[:, bcols], bgrad=True)
-    check_f32(host(bg).numpy()[bcols], db, dbm, "bias grad")
+    check_f32(g[bcols], db, dbm, "bias grad", chain_colsum(K, M, GELU_CHAIN))
+    del dz
+    if accum == FULL:
+        dzb = te.te_fp8_gemm_dgrad(A, SA, E5, B, SB, E4, epilogue=epi, preact=Z, bias_grad=bg, accum=accum)
+        assert torch.equal(host(dzb).view(torch.int16), torch.from_numpy(dzh).to(torch.bfloat16).view(torch.int16))
 
 
 # ------------------------------------------------------------------ M-grouped
@@ -497,7 +533,7 @@ def test_mgrouped_fwd(accum, pow2, epi, ydt):
     assert torch.all(yb[torch.from_numpy(~live)] == 77.0), "a skipped block was written"
     ymag = zmag * (GELU_LIP if epi & te.TE_EPI_GELU else 1.0)
     if ydt == te.TE_DTYPE_F32:
-        check_f32(yb[:, :N].numpy()[live], y[live], ymag[live], "mgrouped y")
+        check_f32(yb[:, :N].numpy()[live], y[live], ymag[live], "mgrouped y", chain_gemm(K, epi_chain(epi)))
     else:
         check_bf16(bf16_host_f64(yb[:, :N])[live], y[live], ymag[live], "mgrouped y")
     if pre is not None:
@@ -534,16 +570,7 @@ def test_mgrouped_dgrad(accum, pow2, epi, dxdt):
     qw, sw = np.stack([w[0] for w in ws]), np.stack([w[1] for w in ws])
     zb = W.normal_bf16(np.random.SeedSequence(120), (M, N), 1.28)
     has_dg, has_bg = bool(epi & te.TE_EPI_DGELU), bool(epi & te.TE_EPI_BGRAD)
-    D = np.full((M, N), np.nan); Dm = np.full((M, N), np.nan)
-    db = np.zeros((G, N)); dbm = np.zeros((G, N))
-    for i, e in enumerate(blocks):
-        if e < 0:
-            continue
-        r = slice(256 * i, 256 * (i + 1))
-        o, d = oracle.gemm_nt(qa[r], sa[r], oracle.E5M2, qw[e], sw[e], oracle.E4M3)
-        D[r], Dm[r], dbi, dbmi = oracle.dgrad_epilogue(o, d, zb[r] if has_dg else None, True)
-        db[e] += dbi
-        dbm[e] += dbmi
+    D, Dm, db, dbm = oracle.mgrouped_dgrad(qa, sa, oracle.E5M2, qw, sw, oracle.E4M3, blocks, zb if has_dg else None)
     tdt = torch.float32 if dxdt == te.TE_DTYPE_F32 else torch.bfloat16
     dxbuf = torch.full((M, N + 8), 9.0, dtype=tdt, device="cuda")
     bg = torch.full((G * N,), 3.0, dtype=torch.float32, device="cuda") if has_bg else None
@@ -558,13 +585,13 @@ def test_mgrouped_dgrad(accum, pow2, epi, dxdt):
     live = np.repeat(blocks >= 0, 256)
     assert torch.all(xb[:, N:] == 9.0) and torch.all(xb[torch.from_numpy(~live)] == 9.0)
     if dxdt == te.TE_DTYPE_F32:
-        check_f32(xb[:, :N].numpy()[live], D[live], Dm[live], "mgrouped dgrad D")
+        check_f32(xb[:, :N].numpy()[live], D[live], Dm[live], "mgrouped dgrad D", chain_gemm(K, epi_chain(epi)))
     else:
         check_bf16(bf16_host_f64(xb[:, :N])[live], D[live], Dm[live], "mgrouped dgrad D")
     if has_bg:
         g = host(bg).numpy().reshape(G, N)
         assert (g[3] == 0).all(), "an expert without blocks must get a zero bias gradient"
-        check_f32(g[:3], db[:3], dbm[:3], "per-expert bias grad")
+        check_f32(g[:3], db[:3], dbm[:3], "per-expert bias grad", chain_colsum(K, M, epi_chain(epi)))
 
 
 def test_mgrouped_same_expert_equals_dense():
@@ -596,7 +623,7 @@ def test_kgrouped_small(accum, pow2):
         if gk[g] == 0:
             assert np.array_equal(got[g].view(np.uint32), init[g].view(np.uint32)), f"empty group {g} touched"
         else:
-            check_f32(got[g], want[g], mag[g], f"group {g}")
+            check_f32(got[g], want[g], mag[g], f"group {g}", chain_gemm(gk[g], 1))
 
 
 def test_kgrouped_many_groups():
@@ -611,7 +638,7 @@ def test_kgrouped_many_groups():
     want, mag = oracle.kgrouped_wgrad(qa, sa, oracle.E4M3, qb, sb, oracle.E4M3, gk, init)
     out = dev(init)
     te.te_fp8_kgrouped_wgrad(dev(qa), sdev(sa), E4, dev(qb), sdev(sb), E4, gk.tolist(), out, FULL)
-    check_f32(host(out).numpy(), want, mag, "300 groups")
+    check_f32(host(out).numpy(), want, mag, "300 groups", chain_gemm(128, 1))
 
 
 @pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
@@ -641,7 +668,7 @@ def test_kgrouped_device_sizes_matches_host_sizes(accum, pow2):
         if gk[g] == 0:
             assert np.array_equal(got[g].view(np.uint32), init[g].view(np.uint32)), f"empty group {g} touched"
         else:
-            check_f32(got[g], want[g], mag[g], f"group {g}")
+            check_f32(got[g], want[g], mag[g], f"group {g}", chain_gemm(gk[g], 1))
 
 
 def test_kgrouped_device_sizes_follow_the_device_array():
@@ -662,7 +689,7 @@ def test_kgrouped_device_sizes_follow_the_device_array():
     want, mag = oracle.kgrouped_wgrad(np.ascontiguousarray(qa[:, :896]), np.ascontiguousarray(sa[:, :7]), oracle.E4M3,
                                       np.ascontiguousarray(qb[:, :896]), np.ascontiguousarray(sb[:, :7]), oracle.E4M3,
                                       second, o1)
-    check_f32(host(out).numpy(), want, mag + d1, "two calls")
+    check_f32(host(out).numpy(), want, mag + d1, "two calls", chain_gemm(S, 2))
 
 
 def test_kgrouped_device_sizes_workload():
@@ -681,7 +708,7 @@ def test_kgrouped_device_sizes_workload():
         rows, cols = sample_idx(sh["M"], 8, 30 + g), sample_idx(sh["N"], 12, 40 + g)
         o, d = grid_entries(qa, sa, oracle.E4M3, qb, sb, oracle.E4M3, rows, cols, int(offs[g]), int(gk[g]))
         want, mag = oracle.wgrad(o, d, inp["out0"][g][np.ix_(rows, cols)])
-        check_f32(got[g][np.ix_(rows, cols)], want, mag, f"expert {g}")
+        check_f32(got[g][np.ix_(rows, cols)], want, mag, f"expert {g}", chain_gemm(gk[g], 1))
 
 
 def test_kgrouped_workload():
@@ -698,4 +725,5 @@ def test_kgrouped_workload():
         rows, cols = sample_idx(sh["M"], 8, 10 + g), sample_idx(sh["N"], 12, 20 + g)
         o, d = grid_entries(qa, sa, oracle.E4M3, qb, sb, oracle.E4M3, rows, cols, int(offs[g]), int(gk[g]))
         init = inp["out0"][g][np.ix_(rows, cols)]
-        check_f32(got[g][np.ix_(rows, cols)], init.astype(np.float64) + o, np.abs(init) + d, f"expert {g}")
+        check_f32(got[g][np.ix_(rows, cols)], init.astype(np.float64) + o, np.abs(init) + d, f"expert {g}",
+                  chain_gemm(gk[g], 1))

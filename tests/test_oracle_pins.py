@@ -467,3 +467,96 @@ def test_kgrouped_equals_dense_per_group_and_skips_empty():
     out_p, _ = oracle.kgrouped_wgrad(qa[:, cols], sa[:, blocks], oracle.E4M3, qb[:, cols], sb[:, blocks],
                                      oracle.E4M3, gk[perm], init[perm])
     assert np.allclose(out_p, out[perm], rtol=1e-14, atol=1e-14)
+
+
+# ------------------------------------------------------------- M-grouped
+def _mgrouped_case(seed, G, nblocks, N, K, block=8, fx=oracle.E4M3):
+    """Random codes with `block`-row blocks (the oracle's block size is a parameter; the library's
+    is 256 rows, which changes nothing in the definition)."""
+    rng = np.random.default_rng(seed)
+    qx, sx = random_operand(rng, nblocks * block, K, fx)
+    ws = [random_operand(rng, N, K, oracle.E4M3) for _ in range(G)]
+    qw, sw = np.stack([w[0] for w in ws]), np.stack([w[1] for w in ws])
+    b = W.normal_bf16(np.random.SeedSequence(seed + 1), (G, N), 0.1)
+    z = W.normal_bf16(np.random.SeedSequence(seed + 2), (nblocks * block, N), 1.3)
+    return qx, sx, qw, sw, b, z
+
+
+def test_mgrouped_fwd_one_expert_is_the_dense_forward():
+    """Every block on expert e: the dense forward with W[e] and bias[e] over the whole matrix."""
+    qx, sx, qw, sw, b, _ = _mgrouped_case(11, 3, 4, 6, 256)
+    for e in range(3):
+        y, z, zm = oracle.mgrouped_fwd(qx, sx, oracle.E4M3, qw, sw, oracle.E4M3, np.full(4, e), b, True, block=8)
+        o, d = oracle.gemm_nt(qx, sx, oracle.E4M3, qw[e], sw[e], oracle.E4M3)
+        yd, zd, zmd = oracle.fwd_epilogue(o, d, b[e], True)
+        assert np.array_equal(y, yd) and np.array_equal(z, zd) and np.array_equal(zm, zmd)
+
+
+def test_mgrouped_fwd_brute_force_and_block_permutation():
+    """Per-block library Linear (torch decode, matmul, tanh-GELU) with each block's own expert; skipped
+    blocks stay NaN; permuting the blocks (rows and expert list together) permutes the output rows."""
+    blocks = np.array([2, -1, 0, 2, 1])
+    qx, sx, qw, sw, b, _ = _mgrouped_case(12, 3, len(blocks), 5, 384)
+    y, _, _ = oracle.mgrouped_fwd(qx, sx, oracle.E4M3, qw, sw, oracle.E4M3, blocks, b, True, block=8)
+    X = torch.from_numpy(dequant(qx, sx, oracle.E4M3))
+    for i, e in enumerate(blocks):
+        r = slice(8 * i, 8 * (i + 1))
+        if e < 0:
+            assert np.isnan(y[r]).all()
+            continue
+        Wt = torch.from_numpy(dequant(qw[e], sw[e], oracle.E4M3))
+        bt = torch.from_numpy(W.bf16_bits_to_f32(b[e]).astype(np.float64))
+        ref = torch.nn.functional.gelu(torch.nn.functional.linear(X[r], Wt, bt), approximate="tanh")
+        assert np.allclose(y[r], ref.numpy(), rtol=1e-12, atol=1e-12)
+    perm = np.array([3, 0, 4, 1, 2])
+    rows = np.concatenate([np.arange(8 * p, 8 * p + 8) for p in perm])
+    yp, _, _ = oracle.mgrouped_fwd(qx[rows], sx[rows], oracle.E4M3, qw, sw, oracle.E4M3, blocks[perm], b, True,
+                                   block=8)
+    assert np.array_equal(yp, y[rows], equal_nan=True)
+
+
+def test_mgrouped_dgrad_one_expert_is_the_dense_dgrad():
+    """Every block on expert e: D and the bias gradient of the dense dgrad over the whole matrix; the
+    other experts' bias gradients are zero."""
+    qa, sa, qw, sw, _, z = _mgrouped_case(13, 3, 4, 6, 256)
+    D, Dm, db, dbm = oracle.mgrouped_dgrad(qa, sa, oracle.E4M3, qw, sw, oracle.E4M3, np.full(4, 1), z, block=8)
+    o, d = oracle.gemm_nt(qa, sa, oracle.E4M3, qw[1], sw[1], oracle.E4M3)
+    Dd, Dmd, dbd, dbmd = oracle.dgrad_epilogue(o, d, z, bgrad=True)
+    assert np.array_equal(D, Dd) and np.array_equal(Dm, Dmd)
+    assert np.allclose(db[1], dbd, rtol=1e-13, atol=1e-13 * dbmd.max())
+    assert np.allclose(dbm[1], dbmd, rtol=1e-13)
+    assert (db[0] == 0).all() and (db[2] == 0).all()
+
+
+def test_mgrouped_dgrad_brute_force_skips_and_per_expert_sums():
+    """Library route per block (torch decode, matmul, autograd of the tanh-GELU); a -1 block is
+    neither written nor summed; expert e's bias gradient is the column sum over its blocks' rows;
+    permuting the blocks permutes the rows and leaves the bias gradients unchanged."""
+    blocks = np.array([1, 0, -1, 1, 2])
+    G, N, K = 4, 5, 256
+    qa, sa, qw, sw, _, z = _mgrouped_case(14, G, len(blocks), N, K, fx=oracle.E5M2)
+    D, _, db, _ = oracle.mgrouped_dgrad(qa, sa, oracle.E5M2, qw, sw, oracle.E4M3, blocks, z, block=8)
+    A = dequant(qa, sa, oracle.E5M2)
+    want_db = np.zeros((G, N))
+    for i, e in enumerate(blocks):
+        r = slice(8 * i, 8 * (i + 1))
+        if e < 0:
+            assert np.isnan(D[r]).all()
+            continue
+        dy = torch.from_numpy(A[r] @ dequant(qw[e], sw[e], oracle.E4M3).T)
+        zt = torch.from_numpy(W.bf16_bits_to_f32(z[r]).astype(np.float64)).requires_grad_(True)
+        (gz,) = torch.autograd.grad(torch.nn.functional.gelu(zt, approximate="tanh"), zt, dy)
+        assert np.allclose(D[r], gz.numpy(), rtol=1e-11, atol=1e-12 * np.abs(gz.numpy()).max())
+        want_db[e] += gz.numpy().sum(0)
+    assert np.allclose(db, want_db, rtol=1e-11, atol=1e-12 * np.abs(want_db).max())
+    assert (db[3] == 0).all()
+    live = ~np.isnan(D[:, 0])
+    for e in range(G):
+        rows_e = np.repeat(blocks == e, 8)
+        assert np.allclose(db[e], D[rows_e & live].sum(0), rtol=1e-12, atol=1e-13)
+    perm = np.array([4, 2, 0, 3, 1])
+    rows = np.concatenate([np.arange(8 * p, 8 * p + 8) for p in perm])
+    Dp, _, dbp, _ = oracle.mgrouped_dgrad(qa[rows], sa[rows], oracle.E5M2, qw, sw, oracle.E4M3, blocks[perm],
+                                          z[rows], block=8)
+    assert np.array_equal(Dp, D[rows], equal_nan=True)
+    assert np.allclose(dbp, db, rtol=1e-13, atol=1e-13 * np.abs(db).max())
