@@ -37,6 +37,7 @@ TE_CAST_POW2_SCALE = 1
 
 EXPORTED = ("te_cast_fp8_per_token", "te_cast_fp8_per_token_batch", "te_cast_fp8_per_token_transpose", "te_fp8_gemm_fwd", "te_fp8_gemm_fwd_quant",
             "te_fp8_gemm_dgrad_quant", "te_fp8_gemm_dgrad_deterministic", "te_fp8_dgrad_bgrad_workspace_bytes",
+            "te_fp8_gemm_dgrad_deterministic_noalloc",
             "te_fp8_wgrad_accum_bgrad", "te_fp8_gemm_dgrad", "te_fp8_wgrad_accum",
             "te_fp8_kgrouped_wgrad", "te_fp8_kgrouped_wgrad_device_sizes", "te_fp8_mgrouped_gemm_fwd",
             "te_fp8_mgrouped_gemm_dgrad",
@@ -84,6 +85,9 @@ def load_library():
     lib.te_fp8_gemm_dgrad_deterministic.restype = I
     lib.te_fp8_gemm_dgrad_deterministic.argtypes = [P, P, I, P, P, I, I64, I64, I64, U32, P, I64, P, P, I64, P, I,
                                                     I64, I, P]
+    lib.te_fp8_gemm_dgrad_deterministic_noalloc.restype = I
+    lib.te_fp8_gemm_dgrad_deterministic_noalloc.argtypes = [P, P, I, P, P, I, I64, I64, I64, U32, P, I64, P, P, I,
+                                                            I64, I, P]
     lib.te_fp8_gemm_dgrad.restype = I
     lib.te_fp8_gemm_dgrad.argtypes = [P, P, I, P, P, I, I64, I64, I64, U32, P, I64, P, P, I, I64, I, P]
     lib.te_fp8_wgrad_accum.restype = I
@@ -370,6 +374,25 @@ def te_fp8_gemm_dgrad_deterministic(dy, dy_scales, dy_dtype, wt, wt_scales, wt_d
         _ptr(dy), _ptr(dy_scales), dy_dtype, _ptr(wt), _ptr(wt_scales), wt_dtype, M, N, K, epilogue,
         _ptr(preact), preact.stride(0) if preact is not None else 0, _ptr(bias_grad), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(dx), dx_dtype, dx.stride(0), accum, _stream(stream)))
+    return dx
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20  # TE_NOALLOC_SCRATCH_BYTES
+
+
+def te_fp8_gemm_dgrad_deterministic_noalloc(dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, bias_grad, dx,
+                                            epilogue=TE_EPI_BGRAD, preact=None, dx_dtype=TE_DTYPE_BF16,
+                                            accum=TE_ACCUM_FULL_FP32, stream=None):
+    """te_fp8_gemm_dgrad_deterministic with the column-sum workspace in the library's static scratch
+    (the call allocates nothing; dx and bias_grad are the caller's); returns dx."""
+    M, K = dy.shape
+    N = wt.shape[0]
+    _scales_ok(dy_scales, M, K, "dy_scales")
+    _scales_ok(wt_scales, N, K, "wt_scales")
+    _check(load_library().te_fp8_gemm_dgrad_deterministic_noalloc(
+        _ptr(dy), _ptr(dy_scales), dy_dtype, _ptr(wt), _ptr(wt_scales), wt_dtype, M, N, K, epilogue,
+        _ptr(preact), preact.stride(0) if preact is not None else 0, _ptr(bias_grad), _ptr(dx), dx_dtype,
+        dx.stride(0), accum, _stream(stream)))
     return dx
 
 

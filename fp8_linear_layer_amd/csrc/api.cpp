@@ -668,6 +668,57 @@ int64_t te_fp8_dgrad_bgrad_workspace_bytes(int64_t M, int64_t N)
     return rows * ((N + 3) / 4 * 4) * (int64_t)sizeof(float);
 }
 
+// The deterministic dgrad on a given column-sum workspace (caller's or the library's scratch).
+static te_status_t dgrad_deterministic(const char* fn, const void* dy, const float* dy_scales, te_dtype_t dy_dtype,
+                                       const void* wt, const float* wt_scales, te_dtype_t wt_dtype, int64_t M,
+                                       int64_t N, int64_t K, uint32_t epilogue, const void* preact_bf16,
+                                       int64_t ld_preact, float* bias_grad, float* ws, void* dx, te_dtype_t dx_dtype,
+                                       int64_t ld_dx, te_accum_t accum, hipStream_t stream)
+{
+    if (!(epilogue & TE_EPI_BGRAD))
+        return fail(TE_ERR_INVALID_ARGUMENT, "%s: the epilogue must include TE_EPI_BGRAD", fn);
+    te_status_t st = check_operands(fn, dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, M, N, K, accum);
+    if (st != TE_OK) return st;
+    const uint32_t allowed = TE_EPI_DGELU | TE_EPI_BGRAD;
+    if (epilogue & ~allowed) return fail(TE_ERR_INVALID_ARGUMENT, "%s: epilogue flags 0x%x are not dgrad flags", fn, epilogue);
+    if (epilogue & TE_EPI_DGELU) {
+        if (!preact_bf16) return fail(TE_ERR_INVALID_ARGUMENT, "%s: TE_EPI_DGELU needs preact_bf16", fn);
+        if (ld_preact < N) return fail(TE_ERR_INVALID_ARGUMENT, "%s: ld_preact (%lld) is below N", fn, (long long)ld_preact);
+        if (!aligned(preact_bf16, 16) || ld_preact % 8 != 0)
+            return fail(TE_ERR_MISALIGNED, "%s: preact must be 16-byte aligned with ld_preact a multiple of 8", fn);
+    } else if (preact_bf16) {
+        return fail(TE_ERR_INVALID_ARGUMENT, "%s: preact given without TE_EPI_DGELU", fn);
+    }
+    if (!bias_grad) return fail(TE_ERR_INVALID_ARGUMENT, "%s: TE_EPI_BGRAD needs bias_grad", fn);
+    if (!aligned(bias_grad, 4)) return fail(TE_ERR_MISALIGNED, "%s: bias_grad must be 4-byte aligned", fn);
+    st = check_output(fn, "dx", dx, dx_dtype, ld_dx, N);
+    if (st != TE_OK) return st;
+    if (!ws) {
+        // the library's scratch (looked up once per device; no allocation)
+        void* p = nullptr;
+        hipError_t e = tefp8::noalloc_scratch(&p);
+        if (e != hipSuccess) return fail(TE_ERR_HIP, "%s: scratch lookup failed: %s", fn, hipGetErrorString(e));
+        ws = static_cast<float*>(p);
+    }
+    tefp8::GemmArgs g = base_args(dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, M, N, K, accum);
+    g.epi = tefp8::Epi::Dgrad;
+    g.flags = epilogue;
+    g.out = dx;
+    g.out_bf16 = dx_dtype == TE_DTYPE_BF16;
+    g.ld_out = ld_dx;
+    g.preact = static_cast<const uint16_t*>(preact_bf16);
+    g.ld_aux = ld_preact;
+    g.bias_grad = bias_grad;
+    g.bgrad_ws = ws;
+    g.bgrad_ws_ld = (N + 3) / 4 * 4;
+    st = launch(fn, g, stream, K, dy_dtype, wt_dtype, accum, epilogue);
+    if (st != TE_OK) return st;
+    const int64_t rows = (M + 255) / 256 * tefp8::kBgradRowsPerTile;
+    hipError_t e = tefp8::launch_bgrad_reduce(g.bgrad_ws, rows, g.bgrad_ws_ld, N, bias_grad, stream);
+    if (e != hipSuccess) return fail(TE_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
 te_status_t te_fp8_gemm_dgrad_deterministic(const void* dy, const float* dy_scales, te_dtype_t dy_dtype,
                                             const void* wt, const float* wt_scales, te_dtype_t wt_dtype,
                                             int64_t M, int64_t N, int64_t K, uint32_t epilogue,
@@ -678,49 +729,39 @@ te_status_t te_fp8_gemm_dgrad_deterministic(const void* dy, const float* dy_scal
 {
     try {
         const char* fn = "te_fp8_gemm_dgrad_deterministic";
-        if (!(epilogue & TE_EPI_BGRAD))
-            return fail(TE_ERR_INVALID_ARGUMENT, "%s: the epilogue must include TE_EPI_BGRAD", fn);
         if (!workspace) return fail(TE_ERR_INVALID_ARGUMENT, "%s: workspace is null", fn);
         if (!aligned(workspace, 16)) return fail(TE_ERR_MISALIGNED, "%s: workspace must be 16-byte aligned", fn);
         const int64_t need = te_fp8_dgrad_bgrad_workspace_bytes(M, N);
         if (M >= 1 && N >= 1 && workspace_bytes < need)
             return fail(TE_ERR_INVALID_ARGUMENT, "%s: workspace_bytes %lld below the %lld bytes needed", fn,
                         (long long)workspace_bytes, (long long)need);
-        te_status_t st = check_operands(fn, dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, M, N, K, accum);
-        if (st != TE_OK) return st;
-        const uint32_t allowed = TE_EPI_DGELU | TE_EPI_BGRAD;
-        if (epilogue & ~allowed) return fail(TE_ERR_INVALID_ARGUMENT, "%s: epilogue flags 0x%x are not dgrad flags", fn, epilogue);
-        if (epilogue & TE_EPI_DGELU) {
-            if (!preact_bf16) return fail(TE_ERR_INVALID_ARGUMENT, "%s: TE_EPI_DGELU needs preact_bf16", fn);
-            if (ld_preact < N) return fail(TE_ERR_INVALID_ARGUMENT, "%s: ld_preact (%lld) is below N", fn, (long long)ld_preact);
-            if (!aligned(preact_bf16, 16) || ld_preact % 8 != 0)
-                return fail(TE_ERR_MISALIGNED, "%s: preact must be 16-byte aligned with ld_preact a multiple of 8", fn);
-        } else if (preact_bf16) {
-            return fail(TE_ERR_INVALID_ARGUMENT, "%s: preact given without TE_EPI_DGELU", fn);
-        }
-        if (!bias_grad) return fail(TE_ERR_INVALID_ARGUMENT, "%s: TE_EPI_BGRAD needs bias_grad", fn);
-        if (!aligned(bias_grad, 4)) return fail(TE_ERR_MISALIGNED, "%s: bias_grad must be 4-byte aligned", fn);
-        st = check_output(fn, "dx", dx, dx_dtype, ld_dx, N);
-        if (st != TE_OK) return st;
-        tefp8::GemmArgs g = base_args(dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, M, N, K, accum);
-        g.epi = tefp8::Epi::Dgrad;
-        g.flags = epilogue;
-        g.out = dx;
-        g.out_bf16 = dx_dtype == TE_DTYPE_BF16;
-        g.ld_out = ld_dx;
-        g.preact = static_cast<const uint16_t*>(preact_bf16);
-        g.ld_aux = ld_preact;
-        g.bias_grad = bias_grad;
-        g.bgrad_ws = static_cast<float*>(workspace);
-        g.bgrad_ws_ld = (N + 3) / 4 * 4;
-        st = launch(fn, g, stream, K, dy_dtype, wt_dtype, accum, epilogue);
-        if (st != TE_OK) return st;
-        const int64_t rows = (M + 255) / 256 * tefp8::kBgradRowsPerTile;
-        hipError_t e = tefp8::launch_bgrad_reduce(g.bgrad_ws, rows, g.bgrad_ws_ld, N, bias_grad, stream);
-        if (e != hipSuccess) return fail(TE_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
-        return ok();
+        return dgrad_deterministic(fn, dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, M, N, K, epilogue,
+                                   preact_bf16, ld_preact, bias_grad, static_cast<float*>(workspace), dx, dx_dtype,
+                                   ld_dx, accum, stream);
     } catch (...) {
         return fail(TE_ERR_INTERNAL, "te_fp8_gemm_dgrad_deterministic: internal error");
+    }
+}
+
+te_status_t te_fp8_gemm_dgrad_deterministic_noalloc(const void* dy, const float* dy_scales, te_dtype_t dy_dtype,
+                                                    const void* wt, const float* wt_scales, te_dtype_t wt_dtype,
+                                                    int64_t M, int64_t N, int64_t K, uint32_t epilogue,
+                                                    const void* preact_bf16, int64_t ld_preact, float* bias_grad,
+                                                    void* dx, te_dtype_t dx_dtype, int64_t ld_dx,
+                                                    te_accum_t accum, hipStream_t stream)
+{
+    try {
+        const char* fn = "te_fp8_gemm_dgrad_deterministic_noalloc";
+        const int64_t need = te_fp8_dgrad_bgrad_workspace_bytes(M, N);
+        if (need > (int64_t)TE_NOALLOC_SCRATCH_BYTES)
+            return fail(TE_ERR_INVALID_ARGUMENT,
+                        "%s: an %lld x %lld output needs %lld bytes of column-sum scratch, above the library's "
+                        "%lld-byte static array; use te_fp8_gemm_dgrad_deterministic with a workspace",
+                        fn, (long long)M, (long long)N, (long long)need, (long long)TE_NOALLOC_SCRATCH_BYTES);
+        return dgrad_deterministic(fn, dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, M, N, K, epilogue,
+                                   preact_bf16, ld_preact, bias_grad, nullptr, dx, dx_dtype, ld_dx, accum, stream);
+    } catch (...) {
+        return fail(TE_ERR_INTERNAL, "te_fp8_gemm_dgrad_deterministic_noalloc: internal error");
     }
 }
 

@@ -57,6 +57,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #ifndef TE_GEMM_PART
 #define TE_GEMM_PART -1
@@ -1185,6 +1186,34 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream, LaunchInfo* info)
     if (a.fmt_a == FMT_E5M2 && a.fmt_b == FMT_E4M3) return launch_pair_e5_e4(a, grid, tiles, stream);
     if (a.fmt_a == FMT_E4M3 && a.fmt_b == FMT_E5M2) return launch_pair_e4_e5(a, grid, tiles, stream);
     return launch_pair_e5_e5(a, grid, tiles, stream);
+}
+
+// Scratch of the entry point that allocates nothing: the column-sum
+// workspace of the deterministic bias gradient.  Each GPU holds its own copy
+// for the life of the process.  In host code `scratch` names a host-side
+// stand-in, never the device memory: only the address returned by
+// hipGetSymbolAddress on the device in question may reach a kernel or a copy.
+static __device__ __align__(256) float scratch[TE_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+hipError_t noalloc_scratch(void** ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with device `dev` current
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_bgrad_reduce(const float* ws, int64_t rows, int64_t ld, int64_t N, float* bias_grad,

@@ -94,6 +94,9 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_bgrad_reduce(const float* ws, int64_t rows, int64_t ld, int64_t N, float* bias_grad,
                                hipStream_t stream);
 constexpr int kBgradRowsPerTile = 4;  // waves along M per 256-row tile
+// Device address of the library's static scratch array on the current device
+// (looked up once per device, then cached); its size is TE_NOALLOC_SCRATCH_BYTES.
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
                        bool pow2, uint8_t* q, int64_t ld_q, float* scales, int64_t ld_s, hipStream_t stream,
                        LaunchInfo* info);

@@ -15,6 +15,7 @@
  *   te_fp8_gemm_fwd_quant,            the forward / data-gradient result stored
  *   te_fp8_gemm_dgrad_quant           as the next GEMM's fp8 operand
  *   te_fp8_gemm_dgrad_deterministic   the bias gradient without atomics
+ *   te_fp8_gemm_dgrad_deterministic_noalloc   the same without a caller workspace
  *                                     (te_fp8_dgrad_bgrad_workspace_bytes)
  *   te_fp8_wgrad_accum_bgrad          the bias gradient beside the weight gradient
  *   te_fp8_kgrouped_wgrad_device_sizes  expert sizes in device memory
@@ -323,6 +324,33 @@ te_status_t te_fp8_gemm_dgrad_deterministic(const void* dy, const float* dy_scal
                                             float* bias_grad, void* workspace, int64_t workspace_bytes,
                                             void* dx, te_dtype_t dx_dtype, int64_t ld_dx,
                                             te_accum_t accum, hipStream_t stream);
+
+/*
+ * te_fp8_gemm_dgrad_deterministic for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and the same result, bit for bit, with
+ * the column-sum workspace taken from a static array inside the library
+ * instead of from the caller.  The call allocates nothing.
+ *
+ *  Limit      te_fp8_dgrad_bgrad_workspace_bytes(M, N) must not exceed
+ *             TE_NOALLOC_SCRATCH_BYTES (8 MiB, e.g. M = 8192 with N up to
+ *             16384); larger outputs are rejected (TE_ERR_INVALID_ARGUMENT)
+ *             before anything is enqueued.
+ *  Sharing    each GPU holds one such array for the life of the process and
+ *             every call on that GPU uses it: calls that can overlap on one GPU
+ *             (different streams, no ordering between them) race and give
+ *             undefined bias gradients; calls ordered on one stream are safe.
+ *             Nothing in the array has to start at zero (every slot the
+ *             reduction reads is written by the same call first).
+ *  Arguments  as te_fp8_gemm_dgrad_deterministic without the workspace.
+ */
+#define TE_NOALLOC_SCRATCH_BYTES (8 << 20)
+te_status_t te_fp8_gemm_dgrad_deterministic_noalloc(const void* dy, const float* dy_scales, te_dtype_t dy_dtype,
+                                                    const void* wt, const float* wt_scales, te_dtype_t wt_dtype,
+                                                    int64_t M, int64_t N, int64_t K, uint32_t epilogue,
+                                                    const void* preact_bf16, int64_t ld_preact, float* bias_grad,
+                                                    void* dx, te_dtype_t dx_dtype, int64_t ld_dx,
+                                                    te_accum_t accum, hipStream_t stream);
 
 /*
  * The data-gradient GEMM with a quantising store: D (after dGELU) is written

@@ -223,6 +223,29 @@ def test_wgrad_bgrad_rejects(lib, kw, status):
     assert "te_fp8_wgrad_accum_bgrad" in lib.te_last_error_message().decode()
 
 
+def dgn(lib, M=512, N=256, K=256, epi=24, pre=Z, ldpre=256, bg=O, dx=0x70000, ldx=256, accum=1):
+    return lib.te_fp8_gemm_dgrad_deterministic_noalloc(p(A), p(S), 2, p(B), p(S), 1, M, N, K, epi, p(pre), ldpre,
+                                                       p(bg), p(dx), 3, ldx, accum, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(epi=8), INV), (dict(bg=0), INV), (dict(bg=O + 2), MISAL), (dict(pre=0), INV), (dict(dx=0), INV),
+    (dict(ldx=128), INV), (dict(K=100), INV), (dict(accum=0), INV), (dict(ldpre=100), INV),
+    # outputs whose column sums exceed the 8 MiB static scratch
+    (dict(M=8192, N=16388, ldpre=16392, ldx=16392), INV), (dict(M=1 << 20, N=256), INV),
+])
+def test_dgrad_noalloc_rejects(lib, kw, status):
+    assert dgn(lib, **kw) == status
+    assert "te_fp8_gemm_dgrad_deterministic_noalloc" in lib.te_last_error_message().decode()
+
+
+def test_dgrad_noalloc_limit_is_the_header_constant(lib):
+    text = open(HEADER).read()
+    assert "#define TE_NOALLOC_SCRATCH_BYTES (8 << 20)" in text
+    assert te.NOALLOC_SCRATCH_BYTES == 8 << 20
+    assert lib.te_fp8_dgrad_bgrad_workspace_bytes(8192, 16384) <= te.NOALLOC_SCRATCH_BYTES
+
+
 MB = 0xA0000  # dummy device address of the per-block experts
 
 
