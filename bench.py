@@ -402,7 +402,9 @@ def run_case(te, torch, name, reps, warm):
             for _ in range(warm):
                 c.fn()
             torch.cuda.synchronize()
-            times = timed_interleaved({name: c.fn}, 1, reps, warm=0)
+            # (back-to-back launches between one event pair, as in the breakdown)
+            per = min(10, reps)
+            times = timed_interleaved({name: c.fn}, per, max(1, reps // per), warm=0)
             rec = {"case": name, **_summ(c, times[name])}
             print(json.dumps(rec), flush=True)
             return

@@ -107,6 +107,18 @@ struct TileSrc {
     int sa_bytes, sb_bytes;  // valid scale bytes of one block (rows past the scale array's width read zero)
 };
 
+// The scale run this wave copies per block: wave 0 the tile rows' (A), wave 1
+// the tile columns' (B), the others nothing (an empty range into the sink).
+// The stride between blocks is made opaque once per tile so that it stays in
+// a register: otherwise the compiler reloads it from the kernel arguments
+// inside the loop and the wait for that load also drains the LDS reads.
+struct ScaleSrc {
+    const float* base;
+    int64_t ld;        // floats between consecutive blocks
+    int bytes;
+    int dst;           // LDS offset of the run inside a stage
+};
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)min(bytes, (int64_t)0x7FFFFFFF),
@@ -138,32 +150,66 @@ __device__ __forceinline__ TileSrc select_src(const TileSrc& s, bool live)
     return e;
 }
 
-// Issue the global -> LDS copies of one 128-deep stage (A tile, B tile, scales).
+__device__ __forceinline__ ScaleSrc scale_src(const GemmArgs& p, const TileSrc& src, int wave)
+{
+    const bool is_a = wave == 0, is_b = wave == 1;
+    ScaleSrc c;
+    c.base = is_a ? src.sa : src.sb;
+    c.ld = is_a ? p.lsa : p.lsb;
+    c.bytes = is_a ? src.sa_bytes : (is_b ? src.sb_bytes : 0);
+    c.dst = kTileA + kTileB + (is_a ? 0 : (is_b ? 1024 : kScaleBytes));
+    asm volatile("" : "+s"(c.ld));
+    return c;
+}
+
+// Copy t (0 .. kOpPerWave-1) of this wave's share of a stage's A tile (op 0)
+// or B tile (op 1): one 1 KiB run (8 rows of 128 bytes) of contraction block kb.
+__device__ __forceinline__ void load_op_part(const GemmArgs& p, const TileSrc& src, uint8_t* stage, int kb, int wave,
+                                             int lane, int t, int op)
+{
+    const int kcol = kb * kBK;
+    const int blk = wave * kOpPerWave + t;        // 1 KiB block = 8 rows of 128 bytes
+    const int ci = blk * 64 + lane;               // 16-byte chunk index within the tile
+    const int row = ci >> 3;
+    const int chunk = (ci & 7) ^ ((row >> 1) & 7);
+    if (op == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.a, (lds_ptr_t)(stage + blk * 1024), 16,
+                                                 (uint32_t)(row * p.lda + chunk * 16), kcol, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.b, (lds_ptr_t)(stage + kTileA + blk * 1024), 16,
+                                                 (uint32_t)(row * p.ldb + chunk * 16), kcol, 0, 0);
+}
+
+// The block's scale runs: the 256 tile rows' (wave 0) and columns' (wave 1)
+// scales are contiguous in the block-major layout, one 1 KiB copy each.  The
+// other waves issue an empty copy into the stage's sink (no branch in the
+// loop body).
+__device__ __forceinline__ void load_scale_part(const ScaleSrc& sc, bool live, uint8_t* stage, int kb, int lane)
+{
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(sc.base + kb * sc.ld, live ? sc.bytes : 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(stage + sc.dst), 16, (uint32_t)(lane * 16), 0, 0, 0);
+}
+
+// The A tile and scale copies of one stage (its B tile is copied from the
+// first slots of the block before it; see block_body).
+__device__ __forceinline__ void load_stage_a_scales(const GemmArgs& p, const TileSrc& src, uint8_t* stage, int kb,
+                                                    int wave, int lane)
+{
+#pragma unroll
+    for (int t = 0; t < kOpPerWave; ++t) load_op_part(p, src, stage, kb, wave, lane, t, 0);
+    load_scale_part(scale_src(p, src, wave), true, stage, kb, lane);
+}
+
+// Issue all global -> LDS copies of one 128-deep stage (A tile, B tile, scales).
 __device__ __forceinline__ void load_stage(const GemmArgs& p, const TileSrc& src, uint8_t* stage, int kb, int wave,
                                            int lane)
 {
-    const int kcol = kb * kBK;
 #pragma unroll
     for (int t = 0; t < kOpPerWave; ++t) {
-        const int blk = wave * kOpPerWave + t;        // 1 KiB block = 8 rows of 128 bytes
-        const int ci = blk * 64 + lane;               // 16-byte chunk index within the tile
-        const int row = ci >> 3;
-        const int chunk = (ci & 7) ^ ((row >> 1) & 7);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.a, (lds_ptr_t)(stage + blk * 1024), 16,
-                                                 (uint32_t)(row * p.lda + chunk * 16), kcol, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.b, (lds_ptr_t)(stage + kTileA + blk * 1024), 16,
-                                                 (uint32_t)(row * p.ldb + chunk * 16), kcol, 0, 0);
+        load_op_part(p, src, stage, kb, wave, lane, t, 0);
+        load_op_part(p, src, stage, kb, wave, lane, t, 1);
     }
-    // scales of this block: the 256 tile rows' (wave 0) and columns' (wave 1)
-    // scales are contiguous in the block-major layout, one 1 KiB copy each.
-    // The other waves issue an empty copy into the stage's sink (no branch in
-    // the loop body).
-    const bool is_a = wave == 0, is_b = wave == 1;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(is_a ? src.sa + kb * p.lsa : src.sb + kb * p.lsb,
-                                               is_a ? src.sa_bytes : (is_b ? src.sb_bytes : 0));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (lds_ptr_t)(stage + kTileA + kTileB + (is_a ? 0 : (is_b ? 1024 : kScaleBytes))), 16, (uint32_t)(lane * 16),
-        0, 0, 0);
+    load_scale_part(scale_src(p, src, wave), true, stage, kb, lane);
 }
 
 // This lane's byte offsets inside a stage.
@@ -341,11 +387,20 @@ struct Pipe {
 
 // One contraction block held in stage S (`cur`); the next block is in `nxt`.
 // The two come from main_loop's restrict-qualified stage pointers.
+//
+// Copies, one every other slot so the address unit drains them as they come
+// instead of stalling the waves on a burst: right after the block's barrier
+// the A tile and scales of block +2 go into `cur`; in the block's first two
+// column groups the B tile of block +1 goes into `nxt` (free since the last
+// barrier, and waited for at this block's barrier, ~0.6 block later).
 template <int S, bool kChain, int kFmtA, int kFmtB>
 __device__ __forceinline__ void block_body(const GemmArgs& p, uint8_t* cur, uint8_t* nxt,
                                            v4f (&acc)[kTM][kTN], Pipe& q, const LaneOff& o, const TileSrc& src,
-                                           int kb_next2, bool has_next2, int wave, int lane)
+                                           const ScaleSrc& sc, int kb_next1, bool has_next1, int kb_next2,
+                                           bool has_next2, int wave, int lane)
 {
+    const TileSrc srcn1 = select_src(src, has_next1);
+    const TileSrc srcn2 = select_src(src, has_next2);
     int ea[kTM];
     if (kChain) {
 #pragma unroll
@@ -353,11 +408,9 @@ __device__ __forceinline__ void block_body(const GemmArgs& p, uint8_t* cur, uint
     }
 #pragma unroll
     for (int j = 0; j < kTN; ++j) {
-        if (j == kBarrierGroup) {
-            // every read of `cur` has been issued (B groups up to 7 were read two groups ago)
-            stage_barrier();
-            load_stage(p, select_src(src, has_next2), cur, kb_next2, wave, lane);
-        }
+        // every read of `cur` has been issued (B groups up to 7 were read two groups ago):
+        // past this barrier the copies of block +2 go into it, one per slot
+        if (j == kBarrierGroup) stage_barrier();
         const int eb = kChain ? e8m0(q.ebq[j & 3]) : 0;
 #pragma unroll
         for (int i = 0; i < kTM; ++i) {
@@ -377,6 +430,24 @@ __device__ __forceinline__ void block_body(const GemmArgs& p, uint8_t* cur, uint
                 q.P[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.bq[j & 3], q.ac[i],
                                                                               v4f{0.f, 0.f, 0.f, 0.f}, kFmtB, kFmtA,
                                                                               0, 0, 0, 0);
+            }
+            // this slot's copy into `cur` for block +2 (the A and B runs alternate; the
+            // scale run rides with the first), spread so the address unit drains them
+            // as they come instead of stalling the waves on a burst
+            int n_vm = 0;
+            if (j < 2 && (i & 1) == 0) {
+                load_op_part(p, srcn1, nxt, kb_next1, wave, lane, (j * kTM + i) >> 1, 1);
+                ++n_vm;
+            }
+            if (j >= kBarrierGroup) {
+                const int c = (j - kBarrierGroup) * kTM + i;
+                if ((c & 1) == 0) {
+                    load_op_part(p, srcn2, cur, kb_next2, wave, lane, c >> 1, 0);
+                    ++n_vm;
+                } else if (c == 1) {
+                    load_scale_part(sc, has_next2, cur, kb_next2, lane);
+                    ++n_vm;
+                }
             }
             // LDS reads of this slot
             if (j < kBarrierGroup) {
@@ -417,6 +488,8 @@ __device__ __forceinline__ void block_body(const GemmArgs& p, uint8_t* cur, uint
             const int n_ds = j < kBarrierGroup ? (i < 3 ? 1 : 0) : (j == kBarrierGroup && i == 3 ? kTM : 2);
             if (!kChain) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (n_vm == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            if (n_vm == 2) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
             sched_ds_reads(n_ds);
         }
     }
@@ -454,12 +527,15 @@ __device__ __forceinline__ void main_loop(const GemmArgs& p, uint8_t* __restrict
     q.ebq[2] = q.ebq[3] = 0;
     q.bq[2] = q.bq[3] = q.bq[0];
 
+    const ScaleSrc sc = scale_src(p, src, wave);
     int it = 0;
     for (; it + 2 <= nkb; it += 2) {
-        block_body<0, kChain, kFmtA, kFmtB>(p, s0, s1, acc, q, o, src, kb0 + it + 2, it + 2 < nkb, wave, lane);
-        block_body<1, kChain, kFmtA, kFmtB>(p, s1, s0, acc, q, o, src, kb0 + it + 3, it + 3 < nkb, wave, lane);
+        block_body<0, kChain, kFmtA, kFmtB>(p, s0, s1, acc, q, o, src, sc, kb0 + it + 1, it + 1 < nkb, kb0 + it + 2,
+                                            it + 2 < nkb, wave, lane);
+        block_body<1, kChain, kFmtA, kFmtB>(p, s1, s0, acc, q, o, src, sc, kb0 + it + 2, it + 2 < nkb, kb0 + it + 3,
+                                            it + 3 < nkb, wave, lane);
     }
-    if (it < nkb) block_body<0, kChain, kFmtA, kFmtB>(p, s0, s1, acc, q, o, src, 0, false, wave, lane);
+    if (it < nkb) block_body<0, kChain, kFmtA, kFmtB>(p, s0, s1, acc, q, o, src, sc, 0, false, 0, false, wave, lane);
     // the trailing copies (empty ranges) still write LDS: let them land
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (!kChain) {
@@ -1031,7 +1107,8 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p, int
         // contraction range is one.
         const bool chain = kFast && workgroup_all(ok, slots, wave, lane);
         stage_barrier();
-        load_stage(p, select_src(c.src, c.nkb > 1), smem + s1_off, c.kb0 + 1, wave, lane);
+        // (the B tile of this stage follows from the first block's first slots)
+        load_stage_a_scales(p, select_src(c.src, c.nkb > 1), smem + s1_off, c.kb0 + 1, wave, lane);
 
         v4f acc[kTM][kTN];
 #pragma unroll
