@@ -208,7 +208,7 @@ def group_fprop(te, torch, g):
     qw, sw = te.te_cast_fp8_per_token(w, E4)
     px, psx = te.te_cast_fp8_per_token(x, E4, te.TE_CAST_POW2_SCALE)
     pw, psw = te.te_cast_fp8_per_token(w, E4, te.TE_CAST_POW2_SCALE)
-    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    y = _randn(torch, g, (M, N), 1.0, 9)       # (filled: the cast-transpose case reads it)
     z = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     qy = torch.empty((M, N), dtype=torch.uint8, device="cuda")
     qys = torch.empty((N // 128, te.scale_ld(M)), dtype=torch.float32, device="cuda")
@@ -223,6 +223,8 @@ def group_fprop(te, torch, g):
 
     qxt = torch.empty((K, M), dtype=torch.uint8, device="cuda")
     sxt = torch.empty((M // 128, te.scale_ld(K)), dtype=torch.float32, device="cuda")
+    qyt = torch.empty((N, M), dtype=torch.uint8, device="cuda")
+    qyts = torch.empty((M // 128, te.scale_ld(N)), dtype=torch.float32, device="cuda")
     cast_bytes = M * K * 3 + M * (K // 128) * 4
     ct_bytes = M * K * 2 + 2 * M * K + 2 * M * (K // 128) * 4
     cases = {
@@ -236,6 +238,14 @@ def group_fprop(te, torch, g):
         "fprop_bias_gelu_quant_e4m3_fast_pow2": Case(
             lambda: te.te_fp8_gemm_fwd_quant(px, psx, E4, pw, psw, E4, bias=b, epilogue=BG, q=qy, q_scales=qys,
                                              accum=FAST), f),
+        "fprop_bias_gelu_aux_quant_both_e4m3_fast_pow2": Case(
+            lambda: te.te_fp8_gemm_fwd_quant(px, psx, E4, pw, psw, E4, bias=b, epilogue=BGA, q=qy, q_scales=qys,
+                                             preact=z, accum=FAST, transposed=True, qt=qyt, qt_scales=qyts), f,
+            note="the fused forward of an MLP's first layer: pre-activation, and the cast of GELU's output "
+                 "in both layouts"),
+        "cast_and_transpose_e4m3_8192x14336": Case(
+            lambda: te.te_cast_fp8_per_token_transpose(y, E4, q=qy, scales=qys, qt=qyt, scales_t=qyts),
+            nbytes=M * N * 4 + 2 * M * (N // 128) * 4),
         "cast_e4m3_8192x4096": Case(lambda: te.te_cast_fp8_per_token(x, E4, q=qx, scales=sx), nbytes=cast_bytes),
         "cast_and_transpose_e4m3_8192x4096": Case(
             lambda: te.te_cast_fp8_per_token_transpose(x, E4, q=qx, scales=sx, qt=qxt, scales_t=sxt), nbytes=ct_bytes),
@@ -243,7 +253,8 @@ def group_fprop(te, torch, g):
     pairs = [("fprop_none_full", "fprop_bias_gelu_full"), ("fprop_none_full", "fprop_none_fast"),
              ("fprop_none_fast_pow2", "fprop_bias_gelu_fast_pow2"),
              ("fprop_none_fast_pow2", "fprop_bias_gelu_aux_fast_pow2"),
-             ("fprop_bias_gelu_fast_pow2", "fprop_bias_gelu_quant_e4m3_fast_pow2")]
+             ("fprop_bias_gelu_fast_pow2", "fprop_bias_gelu_quant_e4m3_fast_pow2"),
+             ("fprop_bias_gelu_aux_fast_pow2", "fprop_bias_gelu_aux_quant_both_e4m3_fast_pow2")]
     return cases, pairs
 
 
@@ -265,12 +276,14 @@ def group_dgrad(te, torch, g):
         _randn(torch, g, (M2, N2), 1.28, 8)
     qo, so = te.te_cast_fp8_per_token(do, E5)
     q2, s2 = te.te_cast_fp8_per_token(w2t, E4)
-    dz = torch.empty((M2, N2), dtype=torch.bfloat16, device="cuda")
+    dz = _randn(torch, g, (M2, N2), 1e-3, 10)  # (filled: the cast-transpose case reads it)
     bg = torch.empty((N2,), dtype=torch.float32, device="cuda")
     ws = torch.empty((te.load_library().te_fp8_dgrad_bgrad_workspace_bytes(M2, N2),), dtype=torch.uint8,
                      device="cuda")
     qz = torch.empty((M2, N2), dtype=torch.uint8, device="cuda")
     qzs = torch.empty((N2 // 128, te.scale_ld(M2)), dtype=torch.float32, device="cuda")
+    qzt = torch.empty((N2, M2), dtype=torch.uint8, device="cuda")
+    qzts = torch.empty((M2 // 128, te.scale_ld(N2)), dtype=torch.float32, device="cuda")
     f2 = 2.0 * M2 * N2 * K2
     DB = te.TE_EPI_DGELU | te.TE_EPI_BGRAD
     cases = {
@@ -288,10 +301,19 @@ def group_dgrad(te, torch, g):
         "dgrad_dz_dgelu_bgrad_quant_e5m2_full": Case(
             lambda: te.te_fp8_gemm_dgrad_quant(qo, so, E5, q2, s2, E4, epilogue=DB, preact=zz, bias_grad=bg, q=qz,
                                                q_scales=qzs, accum=FULL), f2),
+        "dgrad_dz_dgelu_bgrad_quant_both_e5m2_full": Case(
+            lambda: te.te_fp8_gemm_dgrad_quant(qo, so, E5, q2, s2, E4, epilogue=DB, preact=zz, bias_grad=bg, q=qz,
+                                               q_scales=qzs, accum=FULL, transposed=True, qt=qzt, qt_scales=qzts),
+            f2, note="the data gradient at an MLP's hidden layer, cast in both layouts (the next data and "
+                     "weight gradients' operands)"),
+        "cast_and_transpose_e5m2_8192x14336": Case(
+            lambda: te.te_cast_fp8_per_token_transpose(dz, E5, q=qz, scales=qzs, qt=qzt, scales_t=qzts),
+            nbytes=M2 * N2 * 4 + 2 * M2 * (N2 // 128) * 4),
     }
     pairs = [("dgrad_dz_none_full", "dgrad_dz_dgelu_bgrad_full"),
              ("dgrad_dz_none_full", "dgrad_dz_dgelu_bgrad_deterministic_full"),
-             ("dgrad_dz_dgelu_bgrad_full", "dgrad_dz_dgelu_bgrad_quant_e5m2_full")]
+             ("dgrad_dz_dgelu_bgrad_full", "dgrad_dz_dgelu_bgrad_quant_e5m2_full"),
+             ("dgrad_dz_dgelu_bgrad_full", "dgrad_dz_dgelu_bgrad_quant_both_e5m2_full")]
     return cases, pairs
 
 
@@ -340,6 +362,22 @@ def group_mgrouped(te, torch, g):
 
 
 GROUPS = [group_tiny, group_dense_wgrad, group_fprop, group_dgrad, group_kgrouped, group_mgrouped]
+# the cases of each group (so that --case sets up only its own group's inputs)
+GROUP_CASES = {
+    group_tiny: ("tiny_fprop_bias_gelu_256x256x512", "tiny_wgrad_256x256x512"),
+    group_dense_wgrad: ("wgrad_full_7168x2112x4096", "wgrad_pow2_full_7168x2112x4096", "wgrad_pow2_fast_7168x2112x4096",
+                        "cast_batch_e4m3_7168x4096_2112x4096", "wgrad_from_token_major_7168x2112x4096"),
+    group_fprop: ("fprop_none_full", "fprop_bias_gelu_full", "fprop_none_fast", "fprop_none_fast_pow2",
+                  "fprop_bias_gelu_fast_pow2", "fprop_bias_gelu_aux_fast_pow2", "fprop_bias_gelu_quant_e4m3_fast_pow2",
+                  "fprop_bias_gelu_aux_quant_both_e4m3_fast_pow2", "cast_and_transpose_e4m3_8192x14336",
+                  "cast_e4m3_8192x4096", "cast_and_transpose_e4m3_8192x4096"),
+    group_dgrad: ("dgrad_dx_full", "dgrad_dx_fast", "cast_e5m2_8192x14336", "dgrad_dz_none_full",
+                  "dgrad_dz_dgelu_bgrad_full", "dgrad_dz_dgelu_bgrad_deterministic_full",
+                  "dgrad_dz_dgelu_bgrad_quant_e5m2_full", "dgrad_dz_dgelu_bgrad_quant_both_e5m2_full",
+                  "cast_and_transpose_e5m2_8192x14336"),
+    group_kgrouped: ("kgrouped_wgrad_full", "kgrouped_wgrad_device_sizes_full"),
+    group_mgrouped: ("mgrouped_fwd_bias_gelu_full_8x1024x4096x7168",),
+}
 
 
 def _summ(case, times):
@@ -396,6 +434,8 @@ def run_case(te, torch, name, reps, warm):
     """One case alone, `warm` + `reps` launches (the command the committed rocprofv3 summaries run)."""
     g = torch.Generator(device="cuda")
     for grp in GROUPS:
+        if name not in GROUP_CASES[grp]:
+            continue
         cases, _ = grp(te, torch, g)
         if name in cases:
             c = cases[name]
@@ -546,10 +586,11 @@ def main():
     cold_ms = float(np.median(cold))
     # The kernel's own duration: back-to-back launches between one event pair
     # on the launch stream (an event pair around a single launch also counts
-    # the dispatch gap in front of it).
-    # (median of 5 rounds of kernel_reps back-to-back launches, one event pair each)
+    # the dispatch gap in front of it): after 100 launches that bring the clock
+    # back up from the cache-flush loop, the median of 10 rounds of
+    # kernel_reps back-to-back launches, one event pair each.
     gemm_ms, _ = timed(lambda: te.te_fp8_wgrad_accum(qa, sa, E4, qb, sb, E4, out, te.TE_ACCUM_FULL_FP32),
-                       args.kernel_reps, warm=0, rounds=5)
+                       args.kernel_reps, warm=100, rounds=10)
     flop = 2.0 * M * N * K
     value = flop / (ms_step * 1e-3) / 1e12
     achieved = flop / (gemm_ms * 1e-3) / 1e12

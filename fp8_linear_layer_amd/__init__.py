@@ -77,9 +77,11 @@ def load_library():
     lib.te_fp8_gemm_fwd.restype = I
     lib.te_fp8_gemm_fwd.argtypes = [P, P, I, P, P, I, I64, I64, I64, P, U32, P, I, I64, P, I64, I, P]
     lib.te_fp8_gemm_fwd_quant.restype = I
-    lib.te_fp8_gemm_fwd_quant.argtypes = [P, P, I, P, P, I, I64, I64, I64, P, U32, I, U32, P, I64, P, P, I64, I, P]
+    lib.te_fp8_gemm_fwd_quant.argtypes = [P, P, I, P, P, I, I64, I64, I64, P, U32, I, U32, P, I64, P, P, I64, P, P,
+                                          I64, I, P]
     lib.te_fp8_gemm_dgrad_quant.restype = I
-    lib.te_fp8_gemm_dgrad_quant.argtypes = [P, P, I, P, P, I, I64, I64, I64, U32, P, I64, P, I, U32, P, I64, P, I, P]
+    lib.te_fp8_gemm_dgrad_quant.argtypes = [P, P, I, P, P, I, I64, I64, I64, U32, P, I64, P, I, U32, P, I64, P, P,
+                                            I64, P, I, P]
     lib.te_fp8_dgrad_bgrad_workspace_bytes.restype = I64
     lib.te_fp8_dgrad_bgrad_workspace_bytes.argtypes = [I64, I64]
     lib.te_fp8_gemm_dgrad_deterministic.restype = I
@@ -231,24 +233,44 @@ def te_fp8_gemm_fwd(x, x_scales, x_dtype, w, w_scales, w_dtype, bias=None, epilo
     return y
 
 
+def _quant_outputs(M, N, device, rowwise, transposed, q, q_scales, qt, qt_scales):
+    if rowwise:
+        if q is None:
+            q = torch.empty((M, N), dtype=torch.uint8, device=device)
+        if q_scales is None:
+            q_scales = torch.empty((N // 128, scale_ld(M)), dtype=torch.float32, device=device)
+        _scales_ok(q_scales, M, N, "q_scales")
+    else:
+        q = q_scales = None
+    if transposed:
+        if qt is None:
+            qt = torch.empty((N, M), dtype=torch.uint8, device=device)
+        if qt_scales is None:
+            qt_scales = torch.empty((M // 128, scale_ld(N)), dtype=torch.float32, device=device)
+        _scales_ok(qt_scales, N, M, "qt_scales")
+    else:
+        qt = qt_scales = None
+    return q, q_scales, qt, qt_scales
+
+
 def te_fp8_gemm_fwd_quant(x, x_scales, x_dtype, w, w_scales, w_dtype, bias=None, epilogue=TE_EPI_NONE,
                           q_dtype=TE_DTYPE_E4M3, cast_flags=0, q=None, q_scales=None, preact=None,
-                          accum=TE_ACCUM_FAST, stream=None):
-    """The forward GEMM whose fp32 result is stored as its per-token cast: returns (q, q_scales)."""
+                          accum=TE_ACCUM_FAST, stream=None, rowwise=True, transposed=False, qt=None,
+                          qt_scales=None):
+    """The forward GEMM whose fp32 result is stored as its per-token cast (rowwise: 1x128 groups
+    along N) and/or the cast of its transpose (transposed: groups along M, qt [N, M]).  Returns
+    (q, q_scales), or (q, q_scales, qt, qt_scales) when transposed."""
     M, K = x.shape
     N = w.shape[0]
     _scales_ok(x_scales, M, K, "x_scales")
     _scales_ok(w_scales, N, K, "w_scales")
-    if q is None:
-        q = torch.empty((M, N), dtype=torch.uint8, device=x.device)
-    if q_scales is None:
-        q_scales = torch.empty((N // 128, scale_ld(M)), dtype=torch.float32, device=x.device)
-    _scales_ok(q_scales, M, N, "q_scales")
+    q, q_scales, qt, qt_scales = _quant_outputs(M, N, x.device, rowwise, transposed, q, q_scales, qt, qt_scales)
     _check(load_library().te_fp8_gemm_fwd_quant(
         _ptr(x), _ptr(x_scales), x_dtype, _ptr(w), _ptr(w_scales), w_dtype, M, N, K,
-        _ptr(bias), epilogue, q_dtype, cast_flags, _ptr(q), q.stride(0), _ptr(q_scales),
+        _ptr(bias), epilogue, q_dtype, cast_flags, _ptr(q), q.stride(0) if q is not None else 0, _ptr(q_scales),
+        _ptr(qt), qt.stride(0) if qt is not None else 0, _ptr(qt_scales),
         _ptr(preact), preact.stride(0) if preact is not None else 0, accum, _stream(stream)))
-    return q, q_scales
+    return (q, q_scales, qt, qt_scales) if transposed else (q, q_scales)
 
 
 def te_fp8_gemm_dgrad(dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, epilogue=TE_EPI_NONE, preact=None,
@@ -336,23 +358,21 @@ def te_fp8_mgrouped_gemm_fwd(x, x_scales, x_dtype, w, w_scales, w_dtype, m_block
 
 def te_fp8_gemm_dgrad_quant(dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, epilogue=TE_EPI_NONE, preact=None,
                             bias_grad=None, q_dtype=TE_DTYPE_E5M2, cast_flags=0, q=None, q_scales=None,
-                            accum=TE_ACCUM_FULL_FP32, stream=None):
-    """The data-gradient GEMM whose fp32 D (after dGELU) is stored as its per-token cast:
-    returns (q, q_scales); bias_grad is filled as by te_fp8_gemm_dgrad."""
+                            accum=TE_ACCUM_FULL_FP32, stream=None, rowwise=True, transposed=False, qt=None,
+                            qt_scales=None):
+    """The data-gradient GEMM whose fp32 D (after dGELU) is stored as its per-token cast and/or the
+    cast of its transpose (as te_fp8_gemm_fwd_quant); bias_grad is filled as by te_fp8_gemm_dgrad."""
     M, K = dy.shape
     N = wt.shape[0]
     _scales_ok(dy_scales, M, K, "dy_scales")
     _scales_ok(wt_scales, N, K, "wt_scales")
-    if q is None:
-        q = torch.empty((M, N), dtype=torch.uint8, device=dy.device)
-    if q_scales is None:
-        q_scales = torch.empty((N // 128, scale_ld(M)), dtype=torch.float32, device=dy.device)
-    _scales_ok(q_scales, M, N, "q_scales")
+    q, q_scales, qt, qt_scales = _quant_outputs(M, N, dy.device, rowwise, transposed, q, q_scales, qt, qt_scales)
     _check(load_library().te_fp8_gemm_dgrad_quant(
         _ptr(dy), _ptr(dy_scales), dy_dtype, _ptr(wt), _ptr(wt_scales), wt_dtype, M, N, K, epilogue,
         _ptr(preact), preact.stride(0) if preact is not None else 0, _ptr(bias_grad), q_dtype, cast_flags,
-        _ptr(q), q.stride(0), _ptr(q_scales), accum, _stream(stream)))
-    return q, q_scales
+        _ptr(q), q.stride(0) if q is not None else 0, _ptr(q_scales),
+        _ptr(qt), qt.stride(0) if qt is not None else 0, _ptr(qt_scales), accum, _stream(stream)))
+    return (q, q_scales, qt, qt_scales) if transposed else (q, q_scales)
 
 
 def te_fp8_gemm_dgrad_deterministic(dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, bias_grad,

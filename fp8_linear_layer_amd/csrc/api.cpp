@@ -555,11 +555,38 @@ te_status_t te_fp8_mgrouped_gemm_fwd(const void* x, const float* x_scales, te_dt
     }
 }
 
+// The quantised outputs of the quantising GEMMs: the row-wise cast (q, q_scales) and/or the cast
+// of the transpose (qt, qt_scales); at least one pair.
+static te_status_t check_quant_outputs(const char* fn, int64_t M, int64_t N, const void* q, int64_t ld_q,
+                                       const float* q_scales, const void* qt, int64_t ld_qt, const float* qt_scales)
+{
+    if (!q && !qt) return fail(TE_ERR_INVALID_ARGUMENT, "%s: q or qt (or both) is required", fn);
+    if (q || q_scales) {
+        if (!q || !q_scales) return fail(TE_ERR_INVALID_ARGUMENT, "%s: q and q_scales go together", fn);
+        if (ld_q < N) return fail(TE_ERR_INVALID_ARGUMENT, "%s: ld_q must be >= N", fn);
+        if (!aligned(q, 16) || ld_q % 16 != 0)
+            return fail(TE_ERR_MISALIGNED, "%s: q must be 16-byte aligned with ld_q a multiple of 16", fn);
+        if (!aligned(q_scales, 16)) return fail(TE_ERR_MISALIGNED, "%s: q_scales must be 16-byte aligned", fn);
+    }
+    if (qt || qt_scales) {
+        if (!qt || !qt_scales) return fail(TE_ERR_INVALID_ARGUMENT, "%s: qt and qt_scales go together", fn);
+        if (M % 128 != 0)
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: the transposed cast needs M a multiple of 128 (got %lld)", fn,
+                        (long long)M);
+        if (ld_qt < M) return fail(TE_ERR_INVALID_ARGUMENT, "%s: ld_qt must be >= M", fn);
+        if (!aligned(qt, 16) || ld_qt % 16 != 0)
+            return fail(TE_ERR_MISALIGNED, "%s: qt must be 16-byte aligned with ld_qt a multiple of 16", fn);
+        if (!aligned(qt_scales, 16)) return fail(TE_ERR_MISALIGNED, "%s: qt_scales must be 16-byte aligned", fn);
+    }
+    return TE_OK;
+}
+
 te_status_t te_fp8_gemm_fwd_quant(const void* x, const float* x_scales, te_dtype_t x_dtype,
                                   const void* w, const float* w_scales, te_dtype_t w_dtype,
                                   int64_t M, int64_t N, int64_t K,
                                   const void* bias_bf16, uint32_t epilogue,
                                   te_dtype_t q_dtype, uint32_t cast_flags, void* q, int64_t ld_q, float* q_scales,
+                                  void* qt, int64_t ld_qt, float* qt_scales,
                                   void* preact_bf16, int64_t ld_preact,
                                   te_accum_t accum, hipStream_t stream)
 {
@@ -577,10 +604,8 @@ te_status_t te_fp8_gemm_fwd_quant(const void* x, const float* x_scales, te_dtype
         if (bias_bf16 && !aligned(bias_bf16, 16)) return fail(TE_ERR_MISALIGNED, "%s: bias must be 16-byte aligned", fn);
         if (!is_fp8(q_dtype)) return fail(TE_ERR_INVALID_ARGUMENT, "%s: q_dtype must be TE_DTYPE_E4M3 or TE_DTYPE_E5M2 (got %d)", fn, (int)q_dtype);
         if (cast_flags & ~(uint32_t)TE_CAST_POW2_SCALE) return fail(TE_ERR_INVALID_ARGUMENT, "%s: unknown cast flag bits 0x%x", fn, cast_flags);
-        if (!q || !q_scales) return fail(TE_ERR_INVALID_ARGUMENT, "%s: q and q_scales are required", fn);
-        if (ld_q < N) return fail(TE_ERR_INVALID_ARGUMENT, "%s: ld_q must be >= N", fn);
-        if (!aligned(q, 16) || ld_q % 16 != 0) return fail(TE_ERR_MISALIGNED, "%s: q must be 16-byte aligned with ld_q a multiple of 16", fn);
-        if (!aligned(q_scales, 16)) return fail(TE_ERR_MISALIGNED, "%s: q_scales must be 16-byte aligned", fn);
+        st = check_quant_outputs(fn, M, N, q, ld_q, q_scales, qt, ld_qt, qt_scales);
+        if (st != TE_OK) return st;
         if (epilogue & TE_EPI_AUX_PREACT) {
             st = check_output(fn, "preact", preact_bf16, TE_DTYPE_BF16, ld_preact, N);
             if (st != TE_OK) return st;
@@ -599,6 +624,10 @@ te_status_t te_fp8_gemm_fwd_quant(const void* x, const float* x_scales, te_dtype
         g.ld_qs = te_scale_ld(M);
         g.q_fmt = to_fmt(q_dtype);
         g.q_pow2 = (cast_flags & TE_CAST_POW2_SCALE) ? 1 : 0;
+        g.qt_out = static_cast<uint8_t*>(qt);
+        g.qt_scales = qt_scales;
+        g.ld_qt = ld_qt;
+        g.ld_qts = te_scale_ld(N);
         return launch(fn, g, stream, K, x_dtype, w_dtype, accum, epilogue);
     } catch (...) {
         return fail(TE_ERR_INTERNAL, "te_fp8_gemm_fwd_quant: internal error");
@@ -610,6 +639,7 @@ te_status_t te_fp8_gemm_dgrad_quant(const void* dy, const float* dy_scales, te_d
                                     int64_t M, int64_t N, int64_t K, uint32_t epilogue,
                                     const void* preact_bf16, int64_t ld_preact, float* bias_grad,
                                     te_dtype_t q_dtype, uint32_t cast_flags, void* q, int64_t ld_q, float* q_scales,
+                                    void* qt, int64_t ld_qt, float* qt_scales,
                                     te_accum_t accum, hipStream_t stream)
 {
     try {
@@ -635,10 +665,8 @@ te_status_t te_fp8_gemm_dgrad_quant(const void* dy, const float* dy_scales, te_d
         }
         if (!is_fp8(q_dtype)) return fail(TE_ERR_INVALID_ARGUMENT, "%s: q_dtype must be TE_DTYPE_E4M3 or TE_DTYPE_E5M2 (got %d)", fn, (int)q_dtype);
         if (cast_flags & ~(uint32_t)TE_CAST_POW2_SCALE) return fail(TE_ERR_INVALID_ARGUMENT, "%s: unknown cast flag bits 0x%x", fn, cast_flags);
-        if (!q || !q_scales) return fail(TE_ERR_INVALID_ARGUMENT, "%s: q and q_scales are required", fn);
-        if (ld_q < N) return fail(TE_ERR_INVALID_ARGUMENT, "%s: ld_q must be >= N", fn);
-        if (!aligned(q, 16) || ld_q % 16 != 0) return fail(TE_ERR_MISALIGNED, "%s: q must be 16-byte aligned with ld_q a multiple of 16", fn);
-        if (!aligned(q_scales, 16)) return fail(TE_ERR_MISALIGNED, "%s: q_scales must be 16-byte aligned", fn);
+        st = check_quant_outputs(fn, M, N, q, ld_q, q_scales, qt, ld_qt, qt_scales);
+        if (st != TE_OK) return st;
         tefp8::GemmArgs g = base_args(dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, M, N, K, accum);
         g.epi = tefp8::Epi::Dgrad;
         g.flags = epilogue;
@@ -651,6 +679,10 @@ te_status_t te_fp8_gemm_dgrad_quant(const void* dy, const float* dy_scales, te_d
         g.ld_qs = te_scale_ld(M);
         g.q_fmt = to_fmt(q_dtype);
         g.q_pow2 = (cast_flags & TE_CAST_POW2_SCALE) ? 1 : 0;
+        g.qt_out = static_cast<uint8_t*>(qt);
+        g.qt_scales = qt_scales;
+        g.ld_qt = ld_qt;
+        g.ld_qts = te_scale_ld(N);
         if (epilogue & TE_EPI_BGRAD) {
             hipError_t e = tefp8::launch_zero_f32(bias_grad, N, stream);
             if (e != hipSuccess) return fail(TE_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));

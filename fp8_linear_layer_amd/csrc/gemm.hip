@@ -568,6 +568,215 @@ __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&v)[8],
     }
 }
 
+// DPP row controls: quad_perm [1,0,3,2], [2,3,0,1], half-row mirror, row mirror.
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppRowHalfMirror = 0x141, kDppRowMirror = 0x140;
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_max(float v)
+{
+    const int o = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false);
+    return fmaxf(v, __builtin_bit_cast(float, o));
+}
+
+// max over the 16 lanes of a DPP row (the lanes that share q4: rows r16 = 0 .. 15)
+__device__ __forceinline__ float row16_max(float v)
+{
+    v = dpp_max<kDppQuadXor1>(v);
+    v = dpp_max<kDppQuadXor2>(v);
+    v = dpp_max<kDppRowHalfMirror>(v);
+    return dpp_max<kDppRowMirror>(v);
+}
+
+// Four fp32 values (already scaled) -> four fp8 codes in one dword, byte t = value t.
+__device__ __forceinline__ uint32_t quant_encode4(int fmt, float a, float b, float c, float d)
+{
+    const float fmax = fmt == FMT_E4M3 ? 448.0f : 57344.0f;
+    a = __builtin_amdgcn_fmed3f(a, -fmax, fmax);
+    b = __builtin_amdgcn_fmed3f(b, -fmax, fmax);
+    c = __builtin_amdgcn_fmed3f(c, -fmax, fmax);
+    d = __builtin_amdgcn_fmed3f(d, -fmax, fmax);
+    int w;
+    if (fmt == FMT_E4M3) {
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    } else {
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+    }
+    return (uint32_t)w;
+}
+
+// Transposed quantising store: the tile's final values v (accumulator layout)
+// cast along M in 1x128 groups, i.e. the per-token cast of the result's
+// transpose (the weight gradient's along-tokens operand): qt[n][m] codes and
+// qt_scales[m / 128][n].  A 128-row group is the wave pair (wm, wm ^ 1): their
+// column maxima meet in LDS (region X), each lane derives the scale of 2 of
+// its 32 columns and shares the multipliers through region Y; the codes of a
+// column's 64 wave rows go to region T as 16 dwords (dword r16 holds rows
+// 16 i + r16, byte i), then every thread takes two 64-byte runs of T,
+// transposes their 4x4 byte blocks in registers and stores them as 16-byte
+// runs of qt.  `xs` is a stage the epilogue may use (68 KiB).
+__device__ __forceinline__ void quant_transposed(const GemmArgs& p, const v4f (&v)[kTM][kTN], int64_t m0, int64_t n0,
+                                                 uint8_t* xs, int wave, int lane)
+{
+    // (lane-derived offsets are recomputed here: hoisted out of the tile loop
+    // they would stay live across the main loop and push it into spills)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(lane), "+v"(tid));
+    const int wm = wave / kWavesN, wn = wave % kWavesN;
+    const int r16 = lane & 15, q4 = lane >> 4;
+    float* X = reinterpret_cast<float*>(xs);          // [kWaves][kWN] column maxima
+    float* Y = reinterpret_cast<float*>(xs + 4096);   // [kWaves][kWN] multipliers
+    uint32_t* T = reinterpret_cast<uint32_t*>(xs);    // [kBN][kWavesM][16] code dwords (after X, Y are read)
+    const int64_t mg = m0 + (wm >> 1) * 128;          // this wave pair's 128-row group
+    const bool group_live = mg < p.M;                 // (M is a multiple of 128: whole groups)
+    // 1. maxima of the lane's 32 columns over the wave's 64 rows
+    {
+        float cm[kTN][4];
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                float a = fmaxf(fmaxf(fabsf(v[0][j][c]), fabsf(v[1][j][c])), fmaxf(fabsf(v[2][j][c]), fabsf(v[3][j][c])));
+                cm[j][c] = row16_max(a);
+            }
+        if (r16 == 0) {
+#pragma unroll
+            for (int j = 0; j < kTN; ++j)
+                *reinterpret_cast<float4*>(X + wave * kWN + j * 16 + q4 * 4) =
+                    make_float4(cm[j][0], cm[j][1], cm[j][2], cm[j][3]);
+        }
+    }
+    __syncthreads();
+    // 2. two columns per lane: the group max with the partner wave's rows, the
+    //    cast's scale (stored by the even wave of the pair) and multiplier
+    {
+        const int col = (r16 >> 1) * 16 + q4 * 4 + (r16 & 1) * 2;   // this lane's pair of the wave's 128 columns
+        const float2 a = *reinterpret_cast<const float2*>(X + wave * kWN + col);
+        const float2 b = *reinterpret_cast<const float2*>(X + (wave ^ kWavesN) * kWN + col);
+        float s0, m0_, s1, m1_;
+        quant_scale(p.q_fmt, p.q_pow2, fmaxf(a.x, b.x), s0, m0_);
+        quant_scale(p.q_fmt, p.q_pow2, fmaxf(a.y, b.y), s1, m1_);
+        *reinterpret_cast<float2*>(Y + wave * kWN + col) = make_float2(m0_, m1_);
+        const int64_t n = n0 + wn * kWN + col;
+        if ((wm & 1) == 0 && group_live && n < p.N)
+            *reinterpret_cast<float2*>(p.qt_scales + (mg / 128) * p.ld_qts + n) = make_float2(s0, s1);
+    }
+    // (the multipliers were written by this wave: its LDS reads see them in order)
+    uint32_t code[kTN][4];
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+        const float4 mu = *reinterpret_cast<const float4*>(Y + wave * kWN + j * 16 + q4 * 4);
+        const float mv[4] = {mu.x, mu.y, mu.z, mu.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            code[j][c] = quant_encode4(p.q_fmt, v[0][j][c] * mv[c], v[1][j][c] * mv[c], v[2][j][c] * mv[c],
+                                       v[3][j][c] * mv[c]);
+    }
+    __syncthreads();   // every wave is done with X and Y
+    // 3. codes into T: column n_t = wn * 128 + 16 j + 4 q4 + c, wave row block wm, dword r16
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int nt = wn * kWN + j * 16 + q4 * 4 + c;
+            T[(nt * kWavesM + wm) * 16 + r16] = code[j][c];
+        }
+    __syncthreads();
+    // 4. two 64-byte runs per thread: T[(n_t, w)] holds rows 16 i + r of the
+    //    block in dword r, byte i; output dword 4 i + g takes byte i of dwords
+    //    4 g .. 4 g + 3 (a 4x4 byte transpose per g)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int k = tid + h * kThreads;   // 0 .. kBN * kWavesM - 1
+        const int nt = k / kWavesM, w = k % kWavesM;
+        const int64_t n = n0 + nt, m = m0 + w * kWM;
+        const uint4* src = reinterpret_cast<const uint4*>(T + (nt * kWavesM + w) * 16);
+        uint32_t o[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint4 d = src[g];
+            // [a0 b0 a1 b1], [a2 b2 a3 b3], [c0 d0 c1 d1], [c2 d2 c3 d3]
+            const uint32_t ab_lo = __builtin_amdgcn_perm(d.y, d.x, 0x05010400u);
+            const uint32_t ab_hi = __builtin_amdgcn_perm(d.y, d.x, 0x07030602u);
+            const uint32_t cd_lo = __builtin_amdgcn_perm(d.w, d.z, 0x05010400u);
+            const uint32_t cd_hi = __builtin_amdgcn_perm(d.w, d.z, 0x07030602u);
+            o[0 * 4 + g] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u);
+            o[1 * 4 + g] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u);
+            o[2 * 4 + g] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u);
+            o[3 * 4 + g] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);
+        }
+        if (n < p.N && m < p.M) {
+            uint8_t* dst = p.qt_out + n * p.ld_qt + m;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                *reinterpret_cast<uint4*>(dst + 16 * r) = make_uint4(o[4 * r], o[4 * r + 1], o[4 * r + 2], o[4 * r + 3]);
+        }
+    }
+}
+
+// Row-wise quantising store from the accumulator layout: the wave's 128
+// columns are one 1x128 group of each of its rows, and row 16 i + r16's
+// values are the 32 held by each of the four lanes that share r16.
+template <bool kFull>
+__device__ __forceinline__ void quant_rowwise_acc(const GemmArgs& p, const v4f (&v)[kTM][kTN], int64_t m0, int64_t n0,
+                                                  int wave, int lane)
+{
+    const int wm = wave / kWavesN, wn = wave % kWavesN;
+    const int r16 = lane & 15, q4 = lane >> 4;
+    const int64_t ng = n0 + wn * kWN;
+    const bool group_in = kFull || ng < p.N;
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+        const int64_t m = m0 + wm * kWM + i * 16 + r16;
+        const bool live = group_in && (kFull || m < p.M);
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) amax = fmaxf(amax, fabsf(v[i][j][c]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        float scale, mult;
+        quant_scale(p.q_fmt, p.q_pow2, amax, scale, mult);
+        uint8_t* o = p.q_out + m * p.ld_q + ng + q4 * 4;
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            const uint32_t e = quant_encode4(p.q_fmt, v[i][j][0] * mult, v[i][j][1] * mult, v[i][j][2] * mult,
+                                             v[i][j][3] * mult);
+            if (live) *reinterpret_cast<uint32_t*>(o + j * 16) = e;
+        }
+        if (live && q4 == 0) p.q_scales[(ng / 128) * p.ld_qs + m] = scale;
+    }
+}
+
+// Bias gradient of columns n .. n + 3: the lane's partial column sums t
+// (its rows of the wave's 64) reduced over the 16 lanes that share q4, then
+// one atomic add per column, or (deterministic) one row of the workspace.
+template <bool kFull>
+__device__ __forceinline__ void bias_grad_cols4(const GemmArgs& p, float (&t)[4], int64_t n, int64_t m0, int wm, int r16,
+                                                float* bgrad_v)
+{
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        t[r] += __shfl_xor(t[r], 1);
+        t[r] += __shfl_xor(t[r], 2);
+        t[r] += __shfl_xor(t[r], 4);
+        t[r] += __shfl_xor(t[r], 8);
+    }
+    if (r16 == 0 && p.bgrad_ws) {
+        // deterministic: this wave's row of partial sums (the row is padded to a
+        // multiple of 4 columns, so the 16-byte store never passes it)
+        if (kFull || n < p.N)
+            *reinterpret_cast<float4*>(p.bgrad_ws + ((m0 / kBM) * kWavesM + wm) * p.bgrad_ws_ld + n) =
+                make_float4(t[0], t[1], t[2], t[3]);
+    } else if (r16 == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (kFull || n + r < p.N) unsafeAtomicAdd(bgrad_v + n + r, t[r]);
+    }
+}
+
 // Epilogue.  Lane (r16, q4) holds D[m][n..n+3] of every (i, j), with m = 16 i
 // + r16 and n = 16 j + 4 q4 in the wave's frame.  Wgrad adds those four
 // columns into out in place.  The Linear-layer epilogues pair column groups
@@ -576,10 +785,10 @@ __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&v)[8],
 // holds eight consecutive columns of its row (group j + (q4 & 1), columns
 // 8 (q4 >> 1) .. +7).  Each bf16 load and store is then a 16-byte run, and
 // four lanes cover 64 contiguous bytes of a row.
-template <int kEpi, bool kFull, bool kQuant>
-__device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM][kTN], int64_t m0, int64_t n0,
-                                         int64_t out_off, const uint16_t* bias_v, float* bgrad_v, int wave,
-                                         int lane)
+template <int kEpi, bool kFull, int kQuant>
+__device__ __forceinline__ void epilogue(const GemmArgs& p, v4f (&acc)[kTM][kTN], int64_t m0, int64_t n0,
+                                         int64_t out_off, const uint16_t* bias_v, float* bgrad_v, uint8_t* xs,
+                                         int wave, int lane)
 {
     const int wm = wave / kWavesN, wn = wave % kWavesN;
     // (the lane index is re-derived here so that its address arithmetic is not
@@ -681,6 +890,56 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
                         p.preact + (m0 + wm * kWM + i * 16 + r16) * p.ld_aux + n0 + wn * kWN + (2 * jp + (q4 & 1)) * 16 +
                         (q4 >> 1) * 8);
         }
+        if (kQuant == 2) {
+            // Both casts of D.  Pass by pass, so that each keeps only the
+            // accumulator and a few registers of its own live: dGELU in place,
+            // the bias gradient summed from the final values (rows in the
+            // order of the row-wise path), the transposed cast, the row-wise.
+            const int64_t ng = n0 + wn * kWN;
+            const bool group_in = kFull || ng < p.N;
+            if (has_dgelu) {
+#pragma unroll
+                for (int i = 0; i < kTM; ++i) {
+                    const int64_t m = m0 + wm * kWM + i * 16 + r16;
+                    const bool live = group_in && (kFull || m < p.M);
+                    uint4 zr[kTN / 2];
+#pragma unroll
+                    for (int jp = 0; jp < kTN / 2; ++jp) {
+                        zr[jp] = make_uint4(0u, 0u, 0u, 0u);
+                        if (live)
+                            zr[jp] = *reinterpret_cast<const uint4*>(
+                                p.preact + m * p.ld_aux + ng + (2 * jp + (q4 & 1)) * 16 + (q4 >> 1) * 8);
+                    }
+#pragma unroll
+                    for (int jp = 0; jp < kTN / 2; ++jp) {
+                        const auto lo = __builtin_amdgcn_permlane16_swap(zr[jp].x, zr[jp].z, false, false);
+                        const auto hi = __builtin_amdgcn_permlane16_swap(zr[jp].y, zr[jp].w, false, false);
+                        const uint32_t a0 = lo[0], b0 = lo[1], a1 = hi[0], b1 = hi[1];
+                        v4f& v0 = acc[i][2 * jp];
+                        v4f& v1 = acc[i][2 * jp + 1];
+                        v0[0] *= dgelu(bf16_to_f32(a0 & 0xFFFF)); v0[1] *= dgelu(bf16_to_f32(a0 >> 16));
+                        v0[2] *= dgelu(bf16_to_f32(a1 & 0xFFFF)); v0[3] *= dgelu(bf16_to_f32(a1 >> 16));
+                        v1[0] *= dgelu(bf16_to_f32(b0 & 0xFFFF)); v1[1] *= dgelu(bf16_to_f32(b0 >> 16));
+                        v1[2] *= dgelu(bf16_to_f32(b1 & 0xFFFF)); v1[3] *= dgelu(bf16_to_f32(b1 >> 16));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            if (has_bgrad) {
+#pragma unroll
+                for (int j = 0; j < kTN; ++j) {
+                    float t[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) t[c] += acc[i][j][c];
+                    bias_grad_cols4<kFull>(p, t, ng + j * 16 + q4 * 4, m0, wm, r16, bgrad_v);
+                }
+            }
+            quant_transposed(p, acc, m0, n0, xs, wave, lane);
+            if (p.q_out) quant_rowwise_acc<kFull>(p, acc, m0, n0, wave, lane);
+            return;
+        }
         if (kQuant) {
             // Quantising store of D (after dGELU): as in the forward, the
             // wave's 128 columns are one 1x128 group of each row; the lane's
@@ -729,26 +988,28 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
                         if (has_bgrad) colsum[j][c] += v[j][c];
                         amax = fmaxf(amax, fabsf(v[j][c]));
                     }
-                amax = fmaxf(amax, __shfl_xor(amax, 16));
-                amax = fmaxf(amax, __shfl_xor(amax, 32));
-                float scale, mult;
-                quant_scale(p.q_fmt, p.q_pow2, amax, scale, mult);
+                if (p.q_out) {
+                    amax = fmaxf(amax, __shfl_xor(amax, 16));
+                    amax = fmaxf(amax, __shfl_xor(amax, 32));
+                    float scale, mult;
+                    quant_scale(p.q_fmt, p.q_pow2, amax, scale, mult);
 #pragma unroll
-                for (int jp = 0; jp < kTN / 2; ++jp) {
-                    float t[8];
+                    for (int jp = 0; jp < kTN / 2; ++jp) {
+                        float t[8];
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        t[c] = v[2 * jp][c] * mult;
-                        t[4 + c] = v[2 * jp + 1][c] * mult;
+                        for (int c = 0; c < 4; ++c) {
+                            t[c] = v[2 * jp][c] * mult;
+                            t[4 + c] = v[2 * jp + 1][c] * mult;
+                        }
+                        const uint2 e = quant_encode8(p.q_fmt, t);
+                        if (live) {
+                            uint8_t* o = p.q_out + m * p.ld_q + ng + q4 * 4;
+                            *reinterpret_cast<uint32_t*>(o + (2 * jp) * 16) = e.x;
+                            *reinterpret_cast<uint32_t*>(o + (2 * jp + 1) * 16) = e.y;
+                        }
                     }
-                    const uint2 e = quant_encode8(p.q_fmt, t);
-                    if (live) {
-                        uint8_t* o = p.q_out + m * p.ld_q + ng + q4 * 4;
-                        *reinterpret_cast<uint32_t*>(o + (2 * jp) * 16) = e.x;
-                        *reinterpret_cast<uint32_t*>(o + (2 * jp + 1) * 16) = e.y;
-                    }
+                    if (live && q4 == 0) p.q_scales[(ng / 128) * p.ld_qs + m] = scale;
                 }
-                if (live && q4 == 0) p.q_scales[(ng / 128) * p.ld_qs + m] = scale;
                 // (one row at a time: keeps the next rows' Z loads and values out of this row's registers)
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -825,31 +1086,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
             }
         }
         if (has_bgrad) {
-            // column sums: reduce over the 16 lanes that share q4 (different m), one atomic per column
 #pragma unroll
-            for (int j = 0; j < kTN; ++j) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float t = colsum[j][r];
-                    t += __shfl_xor(t, 1);
-                    t += __shfl_xor(t, 2);
-                    t += __shfl_xor(t, 4);
-                    t += __shfl_xor(t, 8);
-                    colsum[j][r] = t;
-                }
-                const int64_t n = n0 + wn * kWN + j * 16 + q4 * 4;
-                if (r16 == 0 && p.bgrad_ws) {
-                    // deterministic: this wave's row of partial sums (the row is padded to a
-                    // multiple of 4 columns, so the 16-byte store never passes it)
-                    if (kFull || n < p.N)
-                        *reinterpret_cast<float4*>(p.bgrad_ws + ((m0 / kBM) * kWavesM + wm) * p.bgrad_ws_ld + n) =
-                            make_float4(colsum[j][0], colsum[j][1], colsum[j][2], colsum[j][3]);
-                } else if (r16 == 0) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (kFull || n + r < p.N) unsafeAtomicAdd(bgrad_v + n + r, colsum[j][r]);
-                }
-            }
+            for (int j = 0; j < kTN; ++j)
+                bias_grad_cols4<kFull>(p, colsum[j], n0 + wn * kWN + j * 16 + q4 * 4, m0, wm, r16, bgrad_v);
         }
         return;
     }
@@ -860,6 +1099,55 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
     const bool has_aux = (p.flags & TE_EPI_AUX_PREACT) != 0;
     uint4 bw[kTN / 2];
 
+    if (kQuant == 2) {
+        // Both casts of the result.  The final values are formed in place in
+        // the accumulator layout (bias, pre-activation store, GELU), then the
+        // transposed and the row-wise casts read them; each pass keeps only
+        // the accumulator and a few registers of its own live.
+        const int64_t ng = n0 + wn * kWN;
+        const bool group_in = kFull || ng < p.N;
+        uint2 bj[kTN];   // the bias of the lane's four columns of each group, bf16
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            bj[j] = make_uint2(0u, 0u);
+            if (has_bias && group_in) bj[j] = *reinterpret_cast<const uint2*>(bias_v + ng + j * 16 + q4 * 4);
+        }
+        // (one flag at a time over whole accumulator vectors: a vector updated
+        // element by element under per-element branches is copied and spilled)
+        if (has_bias) {
+#pragma unroll
+            for (int j = 0; j < kTN; ++j) {
+                const v4f b = {__uint_as_float(bj[j].x << 16), __uint_as_float(bj[j].x & 0xFFFF0000u),
+                               __uint_as_float(bj[j].y << 16), __uint_as_float(bj[j].y & 0xFFFF0000u)};
+#pragma unroll
+                for (int i = 0; i < kTM; ++i) acc[i][j] += b;
+            }
+        }
+        if (has_aux) {
+#pragma unroll
+            for (int i = 0; i < kTM; ++i) {
+                const int64_t m = m0 + wm * kWM + i * 16 + r16;
+                if (!(group_in && (kFull || m < p.M))) continue;
+                uint16_t* o = p.aux + m * p.ld_aux + ng + q4 * 4;
+#pragma unroll
+                for (int j = 0; j < kTN; ++j)
+                    *reinterpret_cast<uint2*>(o + j * 16) = make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]),
+                                                                       pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+            }
+        }
+        if (has_gelu) {
+#pragma unroll
+            for (int i = 0; i < kTM; ++i)
+#pragma unroll
+                for (int j = 0; j < kTN; ++j) {
+                    const v4f t = acc[i][j];
+                    acc[i][j] = v4f{gelu(t[0]), gelu(t[1]), gelu(t[2]), gelu(t[3])};
+                }
+        }
+        quant_transposed(p, acc, m0, n0, xs, wave, lane);
+        if (p.q_out) quant_rowwise_acc<kFull>(p, acc, m0, n0, wave, lane);
+        return;
+    }
     if (kQuant) {
         // Quantising store.  A wave's 128 columns are one 1x128 group of each
         // of its rows (N is a multiple of 128, tile corners of 256), so a
@@ -900,25 +1188,27 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v4f (&acc)[kTM
                     for (int r = 0; r < 8; ++r) v[jp][r] = gelu(v[jp][r]);
                 }
             }
-            float amax = 0.0f;
+            if (p.q_out) {
+                float amax = 0.0f;
 #pragma unroll
-            for (int jp = 0; jp < kTN / 2; ++jp)
+                for (int jp = 0; jp < kTN / 2; ++jp)
 #pragma unroll
-                for (int r = 0; r < 8; ++r) amax = fmaxf(amax, fabsf(v[jp][r]));
-            amax = fmaxf(amax, __shfl_xor(amax, 16));
-            amax = fmaxf(amax, __shfl_xor(amax, 32));
-            float scale, mult;
-            quant_scale(p.q_fmt, p.q_pow2, amax, scale, mult);
+                    for (int r = 0; r < 8; ++r) amax = fmaxf(amax, fabsf(v[jp][r]));
+                amax = fmaxf(amax, __shfl_xor(amax, 16));
+                amax = fmaxf(amax, __shfl_xor(amax, 32));
+                float scale, mult;
+                quant_scale(p.q_fmt, p.q_pow2, amax, scale, mult);
 #pragma unroll
-            for (int jp = 0; jp < kTN / 2; ++jp) {
-                float t[8];
+                for (int jp = 0; jp < kTN / 2; ++jp) {
+                    float t[8];
 #pragma unroll
-                for (int r = 0; r < 8; ++r) t[r] = v[jp][r] * mult;
-                const uint2 c = quant_encode8(p.q_fmt, t);
-                const int64_t n = ng + (2 * jp + (q4 & 1)) * 16 + (q4 >> 1) * 8;
-                if (live) *reinterpret_cast<uint2*>(p.q_out + m * p.ld_q + n) = c;
+                    for (int r = 0; r < 8; ++r) t[r] = v[jp][r] * mult;
+                    const uint2 c = quant_encode8(p.q_fmt, t);
+                    const int64_t n = ng + (2 * jp + (q4 & 1)) * 16 + (q4 >> 1) * 8;
+                    if (live) *reinterpret_cast<uint2*>(p.q_out + m * p.ld_q + n) = c;
+                }
+                if (live && q4 == 0) p.q_scales[(ng / 128) * p.ld_qs + m] = scale;
             }
-            if (live && q4 == 0) p.q_scales[(ng / 128) * p.ld_qs + m] = scale;
         }
         return;
     }
@@ -1075,7 +1365,7 @@ __device__ __forceinline__ bool row_scales_pow2(const GemmArgs& p, const TileCtx
 // size).  While a tile's epilogue runs, the first stage of the workgroup's
 // next tile is already being copied in; the next tile's FAST test follows the
 // epilogue.
-template <int kFmtA, int kFmtB, bool kFast, int kEpi, bool kQuant>
+template <int kFmtA, int kFmtB, bool kFast, int kEpi, int kQuant>
 __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p, int64_t total_tiles)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageBytes + kWaves * 4];
@@ -1137,10 +1427,15 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p, int
             // an expert's bias and bias gradient (M-grouped; offset 0 otherwise)
             const uint16_t* bias_v = p.bias + c.bgrp * p.bias_group_stride;
             float* bgrad_v = p.bias_grad + c.bgrp * p.bias_group_stride;
-            if (c.m0 + kBM <= p.M && c.n0 + kBN <= p.N)
-                epilogue<kEpi, true, kQuant>(p, acc, c.m0, c.n0, c.out_off, bias_v, bgrad_v, wave, lane);
+            // (the stage the next tile's first copies do not use is free during the
+            // epilogue; the quantising stores keep one copy, with bounds checks: given
+            // two copies of their long epilogues the register allocator spills in one)
+            if (kQuant == 0 && c.m0 + kBM <= p.M && c.n0 + kBN <= p.N)
+                epilogue<kEpi, kQuant == 0, kQuant>(p, acc, c.m0, c.n0, c.out_off, bias_v, bgrad_v, smem + s1_off,
+                                                    wave, lane);
             else
-                epilogue<kEpi, false, kQuant>(p, acc, c.m0, c.n0, c.out_off, bias_v, bgrad_v, wave, lane);
+                epilogue<kEpi, false, kQuant>(p, acc, c.m0, c.n0, c.out_off, bias_v, bgrad_v, smem + s1_off, wave,
+                                              lane);
         }
         if (!more) break;
         // (after the epilogue: the scale reads overlap its stores)
@@ -1174,17 +1469,21 @@ __global__ void bgrad_reduce_kernel(const float* __restrict__ ws, int64_t rows, 
 template <int kFmtA, int kFmtB, bool kFast>
 hipError_t launch_epi(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s)
 {
-    // (the quantising store is its own kernel: its registers stay out of the plain epilogues)
-    const bool qz = a.q_out != nullptr;
+    // (the quantising stores are kernels of their own: their registers stay out
+    // of the plain epilogues, and the transposed store's, which holds the whole
+    // tile until its column maxima are known, out of the row-wise one)
+    const int qz = a.qt_out != nullptr ? 2 : (a.q_out != nullptr ? 1 : 0);
     switch (a.epi) {
-    case Epi::Wgrad: gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Wgrad, false><<<grid, kThreads, 0, s>>>(a, tiles); break;
+    case Epi::Wgrad: gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Wgrad, 0><<<grid, kThreads, 0, s>>>(a, tiles); break;
     case Epi::Fwd:
-        if (qz) gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Fwd, true><<<grid, kThreads, 0, s>>>(a, tiles);
-        else gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Fwd, false><<<grid, kThreads, 0, s>>>(a, tiles);
+        if (qz == 2) gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Fwd, 2><<<grid, kThreads, 0, s>>>(a, tiles);
+        else if (qz == 1) gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Fwd, 1><<<grid, kThreads, 0, s>>>(a, tiles);
+        else gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Fwd, 0><<<grid, kThreads, 0, s>>>(a, tiles);
         break;
     case Epi::Dgrad:
-        if (qz) gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Dgrad, true><<<grid, kThreads, 0, s>>>(a, tiles);
-        else gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Dgrad, false><<<grid, kThreads, 0, s>>>(a, tiles);
+        if (qz == 2) gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Dgrad, 2><<<grid, kThreads, 0, s>>>(a, tiles);
+        else if (qz == 1) gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Dgrad, 1><<<grid, kThreads, 0, s>>>(a, tiles);
+        else gemm_nt_kernel<kFmtA, kFmtB, kFast, (int)Epi::Dgrad, 0><<<grid, kThreads, 0, s>>>(a, tiles);
         break;
     }
     return hipGetLastError();

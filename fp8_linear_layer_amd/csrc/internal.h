@@ -75,6 +75,12 @@ struct GemmArgs {
     int64_t ld_q, ld_qs;
     int q_fmt;
     int q_pow2;
+    // ... and/or the cast of its transpose (groups of 128 rows, the weight
+    // gradient's along-tokens operand): codes [N][ld_qt], scales block-major
+    // [M/128][ld_qts].  Either q_out or qt_out (or both) is set.
+    uint8_t* qt_out;
+    float* qt_scales;
+    int64_t ld_qt, ld_qts;
     // Deterministic bias gradient: when set, each wave stores its column sums
     // to row (tile_m * 4 + wave_m) of this [P][bgrad_ws_ld] workspace instead
     // of adding them atomically; a second kernel sums the rows in order.

@@ -255,20 +255,27 @@ te_status_t te_fp8_gemm_fwd(const void* x, const float* x_scales, te_dtype_t x_d
  * per-token cast the next FP8 Linear layer consumes, with no bf16 round trip
  * and no separate cast (the DeepGEMM weight-gradient page counts the unfused
  * casts around its kernel among the end-to-end costs):
- *   (q, q_scales) = te_cast_fp8_per_token applied to y[M][N] in fp32
- * i.e. 1x128 groups along N, the same scale and rounding rules, with
- * q_dtype and cast_flags (0 or TE_CAST_POW2_SCALE) as the cast takes them.
- * preact (TE_EPI_AUX_PREACT) is stored as in te_fp8_gemm_fwd.
+ *   (q, q_scales)   = te_cast_fp8_per_token applied to y[M][N] in fp32
+ *   (qt, qt_scales) = te_cast_fp8_per_token applied to y^T[N][M] in fp32
+ * i.e. 1x128 groups along N (the next layer's forward operand) and/or along
+ * M (the tokens: the operand that layer's weight gradient contracts over,
+ * what te_cast_fp8_per_token_transpose makes from a bf16 y), the same scale
+ * and rounding rules, with q_dtype and cast_flags (0 or TE_CAST_POW2_SCALE)
+ * as the cast takes them.  preact (TE_EPI_AUX_PREACT) is stored as in
+ * te_fp8_gemm_fwd.  Either output pair may be null, not both.
  *
  *  x, w, bias, epilogue, preact, accum   as te_fp8_gemm_fwd;  N % 128 == 0
  *  q         [M][ld_q] bytes, ld_q >= N, ld_q % 16 == 0
  *  q_scales  [N/128][te_scale_ld(M)] fp32 (block-major); padding untouched
+ *  qt        [N][ld_qt] bytes, ld_qt >= M, ld_qt % 16 == 0; needs M % 128 == 0
+ *  qt_scales [M/128][te_scale_ld(N)] fp32 (block-major); padding untouched
  */
 te_status_t te_fp8_gemm_fwd_quant(const void* x, const float* x_scales, te_dtype_t x_dtype,
                                   const void* w, const float* w_scales, te_dtype_t w_dtype,
                                   int64_t M, int64_t N, int64_t K,
                                   const void* bias_bf16, uint32_t epilogue,
                                   te_dtype_t q_dtype, uint32_t cast_flags, void* q, int64_t ld_q, float* q_scales,
+                                  void* qt, int64_t ld_qt, float* qt_scales,
                                   void* preact_bf16, int64_t ld_preact,
                                   te_accum_t accum, hipStream_t stream);
 
@@ -357,16 +364,21 @@ te_status_t te_fp8_gemm_dgrad_deterministic_noalloc(const void* dy, const float*
  * as its per-token cast along N, e.g. the e5m2 dZ the next data-gradient
  * GEMM consumes, instead of dx; the bias gradient is formed from the fp32 D
  * as in te_fp8_gemm_dgrad.
- *   (q, q_scales) = te_cast_fp8_per_token applied to D[M][N] in fp32
+ *   (q, q_scales)   = te_cast_fp8_per_token applied to D[M][N] in fp32
+ *   (qt, qt_scales) = te_cast_fp8_per_token applied to D^T[N][M] in fp32
+ * (e.g. e5m2 dZ for the data gradient of the layer before, and dZ^T along
+ * the tokens for its weight gradient).
  *
  *  dy, wt, epilogue, preact, bias_grad, accum   as te_fp8_gemm_dgrad;  N % 128 == 0
- *  q_dtype, cast_flags, q, ld_q, q_scales        as te_fp8_gemm_fwd_quant
+ *  q_dtype, cast_flags, q, ld_q, q_scales,
+ *  qt, ld_qt, qt_scales                          as te_fp8_gemm_fwd_quant
  */
 te_status_t te_fp8_gemm_dgrad_quant(const void* dy, const float* dy_scales, te_dtype_t dy_dtype,
                                     const void* wt, const float* wt_scales, te_dtype_t wt_dtype,
                                     int64_t M, int64_t N, int64_t K, uint32_t epilogue,
                                     const void* preact_bf16, int64_t ld_preact, float* bias_grad,
                                     te_dtype_t q_dtype, uint32_t cast_flags, void* q, int64_t ld_q, float* q_scales,
+                                    void* qt, int64_t ld_qt, float* qt_scales,
                                     te_accum_t accum, hipStream_t stream);
 
 /*

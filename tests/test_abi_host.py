@@ -153,10 +153,22 @@ def kgrouped_dev(lib, gk=GK, G=4, sum_k=512, M=256, N=256, out=O, accum=1):
 QS = 0xB0000
 
 
-def fwdq(lib, M=256, N=256, K=256, bias=0, epi=0, qdt=1, cf=0, q=B + 0x100000, ldq=256, qs=QS, pre=0, ldpre=0,
-         accum=2):
+QT, QTS = B + 0x200000, QS + 0x10000
+
+
+def fwdq(lib, M=256, N=256, K=256, bias=0, epi=0, qdt=1, cf=0, q=B + 0x100000, ldq=256, qs=QS, qt=0, ldqt=0, qts=0,
+         pre=0, ldpre=0, accum=2):
     return lib.te_fp8_gemm_fwd_quant(p(A), p(S), 1, p(B), p(S), 1, M, N, K, p(bias), epi, qdt, cf, p(q), ldq, p(qs),
-                                     p(pre), ldpre, accum, None)
+                                     p(qt), ldqt, p(qts), p(pre), ldpre, accum, None)
+
+
+# the transposed output: invalid alone or beside a valid row-wise one
+QT_BAD = [
+    (dict(q=0, qs=0), INV), (dict(q=0, qs=0, qt=QT, ldqt=256), INV), (dict(qt=QT, ldqt=256), INV),
+    (dict(qts=QTS), INV), (dict(qt=QT, ldqt=256, qts=QTS, M=200), INV), (dict(qt=QT, ldqt=128, qts=QTS), INV),
+    (dict(qt=QT + 8, ldqt=256, qts=QTS), MISAL), (dict(qt=QT, ldqt=264, qts=QTS), MISAL),
+    (dict(qt=QT, ldqt=256, qts=QTS + 4), MISAL), (dict(q=0, qs=0, qt=QT, ldqt=256, qts=QTS, M=384), INV),
+]
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -164,15 +176,15 @@ def fwdq(lib, M=256, N=256, K=256, bias=0, epi=0, qdt=1, cf=0, q=B + 0x100000, l
     (dict(bias=BIAS), INV), (dict(qdt=3), INV), (dict(cf=2), INV), (dict(q=0), INV), (dict(qs=0), INV),
     (dict(ldq=128), INV), (dict(q=MIS), MISAL), (dict(ldq=264), MISAL), (dict(qs=QS + 4), MISAL),
     (dict(pre=Z, ldpre=256), INV), (dict(epi=6), INV), (dict(accum=0), INV), (dict(K=64), INV),
-])
+] + QT_BAD)
 def test_fwd_quant_rejects(lib, kw, status):
     assert fwdq(lib, **kw) == status
 
 
 def dgq(lib, M=256, N=256, K=256, epi=0, pre=0, ldpre=0, bg=0, qdt=2, cf=0, q=B + 0x100000, ldq=256, qs=QS,
-        accum=1):
+        qt=0, ldqt=0, qts=0, accum=1):
     return lib.te_fp8_gemm_dgrad_quant(p(A), p(S), 2, p(B), p(S), 1, M, N, K, epi, p(pre), ldpre, p(bg), qdt, cf,
-                                       p(q), ldq, p(qs), accum, None)
+                                       p(q), ldq, p(qs), p(qt), ldqt, p(qts), accum, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -180,7 +192,7 @@ def dgq(lib, M=256, N=256, K=256, epi=0, pre=0, ldpre=0, bg=0, qdt=2, cf=0, q=B 
     (dict(bg=O), INV), (dict(epi=8, pre=Z, ldpre=128), INV), (dict(epi=8, pre=Z + 8, ldpre=256), MISAL),
     (dict(epi=16, bg=O + 2), MISAL), (dict(qdt=3), INV), (dict(cf=2), INV), (dict(q=0), INV), (dict(qs=0), INV),
     (dict(ldq=128), INV), (dict(q=MIS), MISAL), (dict(ldq=264), MISAL), (dict(qs=QS + 4), MISAL), (dict(accum=3), INV),
-])
+] + QT_BAD)
 def test_dgrad_quant_rejects(lib, kw, status):
     assert dgq(lib, **kw) == status
 

@@ -262,6 +262,85 @@ def test_fwd_quant(accum, pow2, epi, qdt, cast_pow2, M, N, K):
         check_bf16(bf16_host_f64(pb[:, :N]), z, zmag, "fwd preact")
 
 
+def quant_t_bufs(M, N):
+    """Sentinel-filled transposed-cast outputs (qt with 16 padding columns, the scale padding)."""
+    qt = torch.full((N, M + 16), 0x5A, dtype=torch.uint8, device="cuda")
+    qts = torch.full((M // 128, scale_ld(N)), -7.0, dtype=torch.float32, device="cuda")
+    return qt, qts
+
+
+def check_quant_t(qt, qts, M, N, y32h, y, ymag, fmt, cast_pow2, chain, what):
+    """The transposed cast: bit-exact against the oracle's cast of the kernel's own fp32 result's
+    transpose, held to the fp64 oracle, and nothing written outside it."""
+    qth, qtsh = host(qt).numpy(), host(qts).numpy()
+    assert (qth[:, M:] == 0x5A).all(), f"{what}: wrote past M"
+    assert (qtsh[:, N:] == -7.0).all(), f"{what}: wrote into the scale padding"
+    qo, so = oracle.cast_per_token_f32(np.ascontiguousarray(y32h.T), fmt, cast_pow2)
+    bad = np.argwhere(qth[:, :M] != qo)
+    assert bad.size == 0, f"{what}: {len(bad)} transposed code mismatches, first {bad[0]}"
+    st = shost(qts, N)
+    assert np.array_equal(st.view(np.uint32), so.view(np.uint32)), f"{what}: transposed scale mismatch"
+    check_quant(qth[:, :M], st, fmt, y.T, ymag.T, what + " vs oracle", chain)
+
+
+@pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
+@pytest.mark.parametrize("epi", [te.TE_EPI_NONE, te.TE_EPI_BIAS | te.TE_EPI_GELU])
+@pytest.mark.parametrize("qdt,cast_pow2", [(te.TE_DTYPE_E4M3, False), (te.TE_DTYPE_E5M2, True)])
+@pytest.mark.parametrize("M,N,K", [(384, 384, 512), (128, 128, 128), (640, 256, 256)])
+def test_fwd_quant_transposed(accum, pow2, epi, qdt, cast_pow2, M, N, K):
+    """Both casts of the forward's fp32 result from one call: the row-wise one bit-identical to the
+    row-wise-only call, the transposed one (groups of 128 rows) to the oracle's cast of y^T; the
+    transposed-only call gives the same bytes."""
+    qx, sx, qw, sw, b, y, z, zmag = fwd_case(M, N, K, epi, te.TE_DTYPE_F32, accum, pow2, seed=M + 9)
+    ymag = zmag * (GELU_LIP if epi & te.TE_EPI_GELU else 1.0)
+    X, SX, Wd, SW = dev(qx), sdev(sx), dev(qw), sdev(sw)
+    B = bf16_dev(b) if epi & te.TE_EPI_BIAS else None
+    cf = te.TE_CAST_POW2_SCALE if cast_pow2 else 0
+    y32h = host(te.te_fp8_gemm_fwd(X, SX, E4, Wd, SW, E4, bias=B, epilogue=epi, y_dtype=te.TE_DTYPE_F32,
+                                   accum=accum)).numpy()
+    q1, s1 = te.te_fp8_gemm_fwd_quant(X, SX, E4, Wd, SW, E4, bias=B, epilogue=epi, q_dtype=qdt, cast_flags=cf,
+                                      accum=accum)
+    qt, qts = quant_t_bufs(M, N)
+    q2, s2, _, _ = te.te_fp8_gemm_fwd_quant(X, SX, E4, Wd, SW, E4, bias=B, epilogue=epi, q_dtype=qdt, cast_flags=cf,
+                                            accum=accum, transposed=True, qt=qt[:, :M], qt_scales=qts)
+    torch.cuda.synchronize()
+    assert torch.equal(host(q1), host(q2)) and torch.equal(host(s1).view(torch.int32), host(s2).view(torch.int32))
+    chain = chain_gemm(K, epi_chain(epi))
+    check_quant_t(qt, qts, M, N, y32h, y, ymag, OF[qdt], cast_pow2, chain, "fwd qt")
+    qt3, qts3 = quant_t_bufs(M, N)
+    te.te_fp8_gemm_fwd_quant(X, SX, E4, Wd, SW, E4, bias=B, epilogue=epi, q_dtype=qdt, cast_flags=cf, accum=accum,
+                             rowwise=False, transposed=True, qt=qt3[:, :M], qt_scales=qts3)
+    assert torch.equal(host(qt3), host(qt)) and torch.equal(host(qts3).view(torch.int32), host(qts).view(torch.int32))
+
+
+@pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
+@pytest.mark.parametrize("epi", [te.TE_EPI_NONE, te.TE_EPI_DGELU | te.TE_EPI_BGRAD])
+@pytest.mark.parametrize("M,N,K", [(384, 384, 512), (256, 128, 256)])
+def test_dgrad_quant_transposed(accum, pow2, epi, M, N, K):
+    """dZ and dZ^T as e5m2 from one data-gradient call (the bias gradient as the plain call's)."""
+    qa, sa = operand(M + 61, M, K, E5, 1e-3, pow2)
+    qb, sb = operand(N + 62, N, K, E4, 0.02, pow2)
+    zb = W.normal_bf16(np.random.SeedSequence(M + 63), (M, N), 1.28)
+    o, d = oracle.gemm_nt(qa, sa, oracle.E5M2, qb, sb, oracle.E4M3)
+    has_dg, has_bg = bool(epi & te.TE_EPI_DGELU), bool(epi & te.TE_EPI_BGRAD)
+    D, Dm, db, dbm = oracle.dgrad_epilogue(o, d, zb if has_dg else None, has_bg)
+    A, SA, B, SB = dev(qa), sdev(sa), dev(qb), sdev(sb)
+    Z = bf16_dev(zb) if has_dg else None
+    d32h = host(te.te_fp8_gemm_dgrad(A, SA, E5, B, SB, E4, epilogue=epi & ~te.TE_EPI_BGRAD, preact=Z,
+                                     dx_dtype=te.TE_DTYPE_F32, accum=accum)).numpy()
+    bg = torch.empty((N,), dtype=torch.float32, device="cuda") if has_bg else None
+    qt, qts = quant_t_bufs(M, N)
+    q, s, _, _ = te.te_fp8_gemm_dgrad_quant(A, SA, E5, B, SB, E4, epilogue=epi, preact=Z, bias_grad=bg,
+                                            q_dtype=te.TE_DTYPE_E5M2, accum=accum, transposed=True, qt=qt[:, :M],
+                                            qt_scales=qts)
+    torch.cuda.synchronize()
+    qo, so = oracle.cast_per_token_f32(d32h, oracle.E5M2)
+    assert np.array_equal(host(q).numpy(), qo) and np.array_equal(shost(s, M).view(np.uint32), so.view(np.uint32))
+    check_quant_t(qt, qts, M, N, d32h, D, Dm, oracle.E5M2, False, chain_gemm(K, epi_chain(epi)), "dgrad qt")
+    if has_bg:
+        check_f32(host(bg).numpy(), db, dbm, "bias grad (transposed quant)", chain_colsum(K, M, epi_chain(epi)))
+
+
 def test_fwd_quant_workload():
     """8192 x 14336 x 4096 with bias + GELU, FAST on power-of-two inputs, e4m3 codes for the next
     layer; rows sampled (the cast is per row)."""
@@ -273,7 +352,15 @@ def test_fwd_quant_workload():
     epi = te.TE_EPI_BIAS | te.TE_EPI_GELU
     X, SX, Wd, SW, B = dev(qx), sdev(sx), dev(qw), sdev(sw), bf16_dev(inp["b"])
     y32 = te.te_fp8_gemm_fwd(X, SX, E4, Wd, SW, E4, bias=B, epilogue=epi, y_dtype=te.TE_DTYPE_F32, accum=FAST)
-    q, qs = te.te_fp8_gemm_fwd_quant(X, SX, E4, Wd, SW, E4, bias=B, epilogue=epi, accum=FAST)
+    q, qs, qt, qts = te.te_fp8_gemm_fwd_quant(X, SX, E4, Wd, SW, E4, bias=B, epilogue=epi, accum=FAST,
+                                              transposed=True)
+    # transposed cast on sampled columns (each is a row of qt: all M tokens of one output feature)
+    cols = sample_idx(N, 16, 6)
+    yc = host(y32[:, torch.from_numpy(cols).cuda()]).numpy()
+    qo, so = oracle.cast_per_token_f32(np.ascontiguousarray(yc.T), oracle.E4M3)
+    assert np.array_equal(host(qt).numpy()[cols], qo)
+    assert np.array_equal(shost(qts, N)[cols].view(np.uint32), so.view(np.uint32))
+    del qt, qts
     rows = sample_idx(M, 24, 5)
     yr = host(y32[torch.from_numpy(rows).cuda()]).numpy()
     qo, so = oracle.cast_per_token_f32(yr, oracle.E4M3)
