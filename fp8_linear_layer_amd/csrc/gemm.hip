@@ -873,8 +873,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, v4f (&acc)[kTM][kTN]
         // inverse: the 16-byte run of Z a lane loads for its paired columns
         // swaps back into the bf16 pairs of its own columns, and the packed
         // results swap forward into the run it stores.  Positions past M or N
-        // hold zero products (their operand rows read as zero), so only the
-        // loads and stores are masked.
+        // hold zero products (their operand rows read as zero), but a row
+        // past M may carry the scale array's padding (up to three entries of
+        // undefined content, copied with the 16-byte runs), so besides the
+        // loads and stores the column sums skip those rows.
         const bool has_dgelu = (p.flags & TE_EPI_DGELU) != 0;
         const bool has_bgrad = (p.flags & TE_EPI_BGRAD) != 0;
         float colsum[kTN][4];
@@ -931,8 +933,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, v4f (&acc)[kTM][kTN]
                     float t[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int i = 0; i < kTM; ++i)
+                        if (kFull || m0 + wm * kWM + i * 16 + r16 < p.M) {
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) t[c] += acc[i][j][c];
+                            for (int c = 0; c < 4; ++c) t[c] += acc[i][j][c];
+                        }
                     bias_grad_cols4<kFull>(p, t, ng + j * 16 + q4 * 4, m0, wm, r16, bgrad_v);
                 }
             }
@@ -985,7 +989,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, v4f (&acc)[kTM][kTN]
                 for (int j = 0; j < kTN; ++j)
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
-                        if (has_bgrad) colsum[j][c] += v[j][c];
+                        if (has_bgrad && (kFull || m < p.M)) colsum[j][c] += v[j][c];
                         amax = fmaxf(amax, fabsf(v[j][c]));
                     }
                 if (p.q_out) {
@@ -1046,7 +1050,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, v4f (&acc)[kTM][kTN]
                     v1[0] *= dgelu(bf16_to_f32(b0 & 0xFFFF)); v1[1] *= dgelu(bf16_to_f32(b0 >> 16));
                     v1[2] *= dgelu(bf16_to_f32(b1 & 0xFFFF)); v1[3] *= dgelu(bf16_to_f32(b1 >> 16));
                 }
-                if (has_bgrad) {
+                if (has_bgrad && (kFull || m < p.M)) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         colsum[j0][r] += v0[r];
