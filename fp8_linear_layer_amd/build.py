@@ -14,7 +14,7 @@ LIB = os.path.join(PKG, "libte_fp8.so")
 # (source, object, extra flags): gemm.hip is compiled once per operand-format pair and once for its
 # host side (TE_GEMM_PART), so its kernel instantiations build in parallel
 SOURCES = [("api.cpp", "api.o", []), ("cast.hip", "cast.o", [])] + \
-    [("gemm.hip", f"gemm_p{i}.o", [f"-DTE_GEMM_PART={i}"]) for i in range(5)]
+    [("gemm.hip", f"gemm_p{i}.o", [f"-DTE_GEMM_PART={i}"]) for i in range(9)]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -58,6 +58,8 @@
 
 #include <algorithm>
 #include <mutex>
+#include <cstdlib>
+#include <cstring>
 
 #ifndef TE_GEMM_PART
 #define TE_GEMM_PART -1
@@ -1449,6 +1451,199 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p, int
     }
 }
 
+// ---------------------------------------------------------------------------
+// Wave-per-workgroup path, for GEMMs with few 256 x 256 tiles (the persistent
+// kernel would leave most compute units idle: one 256 x 256 x 512 product
+// runs on one of 256).  Each workgroup is a single wave computing one wave
+// tile (64 rows x 128 columns) of the same tile grid, with three LDS stages
+// of its own, so the eight wave tiles of a tile run on up to eight compute
+// units.  Fragments, promotion order, matrix-core chain and epilogue are the
+// persistent kernel's, with the wave's place in its tile, so both paths give
+// the same bits wherever the chain decision agrees (the persistent kernel
+// takes it per 256 x 256 tile, this path per wave tile).
+constexpr int kVA = kWM * kBK;                         // 8 KiB: the wave tile's A rows of one block
+constexpr int kVB = kWN * kBK;                         // 16 KiB: its B rows
+constexpr int kVScale = kVA + kVB;                     // sA run (1 KiB copy, 64 floats used), then sB's
+constexpr int kVStage = kVA + kVB + 2 * 1024;          // 26 KiB
+constexpr int kVStages = 3;
+constexpr int kVCopies = kVA / 1024 + kVB / 1024 + 2;  // copies per block: 8 A + 16 B + 2 scale runs
+
+struct WaveSrc {
+    __amdgpu_buffer_rsrc_t a, b;
+    const float* sa;   // the wave tile's first row in block 0 of the block-major scales
+    const float* sb;
+    int sa_bytes, sb_bytes;
+};
+
+// One block's copies into a stage (empty ranges when `live` is false: the
+// count of copies per block stays fixed, which the waits rely on).
+__device__ __forceinline__ void wave_load_block(const GemmArgs& p, const WaveSrc& s, uint8_t* stage, int kb, bool live,
+                                                int lane)
+{
+    const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ra = live ? s.a : none, rb = live ? s.b : none;
+    const int kcol = live ? kb * kBK : 0;
+#pragma unroll
+    for (int t = 0; t < kVA / 1024; ++t) {
+        const int ci = t * 64 + lane, row = ci >> 3, chunk = (ci & 7) ^ ((row >> 1) & 7);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + t * 1024), 16,
+                                                 (uint32_t)(row * p.lda + chunk * 16), kcol, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < kVB / 1024; ++t) {
+        const int ci = t * 64 + lane, row = ci >> 3, chunk = (ci & 7) ^ ((row >> 1) & 7);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + kVA + t * 1024), 16,
+                                                 (uint32_t)(row * p.ldb + chunk * 16), kcol, 0, 0);
+    }
+    const int64_t kbl = live ? kb : 0;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(s.sa + kbl * p.lsa, live ? s.sa_bytes : 0),
+                                             (lds_ptr_t)(stage + kVScale), 16, (uint32_t)(lane * 16), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(s.sb + kbl * p.lsb, live ? s.sb_bytes : 0),
+                                             (lds_ptr_t)(stage + kVScale + 1024), 16, (uint32_t)(lane * 16), 0, 0, 0);
+}
+
+// Every scale of the wave tile's rows and columns over the contraction range
+// is a power of two (rows past M and columns past N do not count).
+__device__ __forceinline__ bool wave_scales_pow2(const GemmArgs& p, int64_t m0, int64_t n0, int kb0, int nkb,
+                                                 int lane)
+{
+    const int rows = (int)min((int64_t)kWM, p.M - m0), cols = (int)min((int64_t)kWN, p.N - n0);
+    bool ok = true;
+    for (int kb = kb0; kb < kb0 + nkb; ++kb) {
+        const float* a = p.sa + (int64_t)kb * p.lsa + m0;
+        const float* b = p.sb + (int64_t)kb * p.lsb + n0;
+        if (lane < rows) ok = ok && is_pow2_scale(a[lane]);
+        if (lane < cols) ok = ok && is_pow2_scale(b[lane]);
+        if (lane + 64 < cols) ok = ok && is_pow2_scale(b[lane + 64]);
+    }
+    return __builtin_amdgcn_ballot_w64(!ok) == 0;
+}
+
+// One block from stage `st`: its fragments and scales, the 32 products
+// (promoted, or chained on power-of-two scales), then the stage is refilled
+// with block kb_refill (an empty copy when it is past the range).
+struct WaveLane {
+    int a_lo, a_hi, b_lo, b_hi;   // fragment offsets in a stage (row group i / column group j: + 2048 each)
+    int r16, q4;
+};
+
+template <bool kChain, int kFmtA, int kFmtB>
+__device__ __forceinline__ void wave_block(const GemmArgs& p, const WaveSrc& s, uint8_t* st, v4f (&acc)[kTM][kTN],
+                                           const WaveLane& o, int kb_refill, bool refill, int lane)
+{
+    // (the copies into this stage were issued two blocks of copies ago; the
+    // compiler derives the same wait from the stages' separate alias scopes)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kVCopies) : "memory");
+    v8i ac[kTM];
+    float sa[kTM];
+    int ea[kTM];
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+        ac[i] = lds_frag(st, o.a_lo, o.a_hi, i * 2048);
+        const uint32_t bits = lds_u32(st + kVScale + (i * 16 + o.r16) * 4);
+        sa[i] = __builtin_bit_cast(float, bits);
+        ea[i] = e8m0(bits);
+    }
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+        const v8i bq = lds_frag(st, o.b_lo, o.b_hi, j * 2048);
+        if (kChain) {
+            const int eb = e8m0(lds_u32(st + kVScale + 1024 + (j * 16 + o.r16) * 4));
+#pragma unroll
+            for (int i = 0; i < kTM; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq, ac[i], acc[i][j], kFmtB, kFmtA, 0, eb,
+                                                                             0, ea[i]);
+        } else {
+            const float4 sbq = lds_f32x4(st + kVScale + 1024 + (j * 16 + o.q4 * 4) * 4);
+#pragma unroll
+            for (int i = 0; i < kTM; ++i) {
+                const v4f P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq, ac[i], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                               kFmtB, kFmtA, 0, 0, 0, 0);
+                promote(acc[i][j], P, sa[i], sbq);
+            }
+        }
+    }
+    // every read of this stage has returned: refill it
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    wave_load_block(p, s, st, kb_refill, refill, lane);
+}
+
+// The K loop over three stages, unrolled by three so that each stage is its
+// own restrict-qualified pointer: reads of one stage then wait only for the
+// copies into that stage, not for the two blocks in flight behind them.
+template <bool kChain, int kFmtA, int kFmtB>
+__device__ __forceinline__ void wave_main_loop(const GemmArgs& p, const WaveSrc& s, uint8_t* __restrict__ s0,
+                                               uint8_t* __restrict__ s1, uint8_t* __restrict__ s2,
+                                               v4f (&acc)[kTM][kTN], const WaveLane& o, int kb0, int nkb, int lane)
+{
+    int it = 0;
+    for (; it + 3 <= nkb; it += 3) {
+        wave_block<kChain, kFmtA, kFmtB>(p, s, s0, acc, o, kb0 + it + 3, it + 3 < nkb, lane);
+        wave_block<kChain, kFmtA, kFmtB>(p, s, s1, acc, o, kb0 + it + 4, it + 4 < nkb, lane);
+        wave_block<kChain, kFmtA, kFmtB>(p, s, s2, acc, o, kb0 + it + 5, it + 5 < nkb, lane);
+    }
+    if (it < nkb) wave_block<kChain, kFmtA, kFmtB>(p, s, s0, acc, o, 0, false, lane);
+    if (it + 1 < nkb) wave_block<kChain, kFmtA, kFmtB>(p, s, s1, acc, o, 0, false, lane);
+    // the trailing copies (empty ranges) still write LDS: let them land
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int kFmtA, int kFmtB, bool kFast, int kEpi, int kQuant>
+__global__ __launch_bounds__(64) void gemm_nt_wave_kernel(const GemmArgs p)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kVStages * kVStage];
+    const int lane = threadIdx.x;
+    const int wave = (int)(blockIdx.x % kWaves);          // the wave's place in its 256 x 256 tile
+    const TileCtx c = tile_ctx(p, (int64_t)(blockIdx.x / kWaves));
+    const int wm = wave / kWavesN, wn = wave % kWavesN;
+    const int64_t m0 = c.m0 + wm * kWM, n0 = c.n0 + wn * kWN;
+    if (n0 >= p.N) return;
+    if (m0 >= p.M) {
+        // no rows: only the deterministic bias gradient's workspace row of this
+        // wave place is due (zero, as the persistent kernel's wave writes it)
+        if (kEpi == (int)Epi::Dgrad && (p.flags & TE_EPI_BGRAD) && p.bgrad_ws) {
+            float* row = p.bgrad_ws + ((c.m0 / kBM) * kWavesM + wm) * p.bgrad_ws_ld;
+            for (int n = lane; n < kWN; n += 64)
+                if (n0 + n < p.N) row[n0 + n] = 0.0f;
+        }
+        return;
+    }
+    WaveSrc s;
+    s.a = make_rsrc(p.a + m0 * p.lda, min((int64_t)kWM, p.M - m0) * p.lda);
+    s.b = make_rsrc(p.b + n0 * p.ldb, min((int64_t)kWN, p.N - n0) * p.ldb);
+    s.sa = p.sa + m0;
+    s.sb = p.sb + n0;
+    s.sa_bytes = (int)(min((int64_t)kWM, p.lsa - m0) * 4);
+    s.sb_bytes = (int)(min((int64_t)kWN, p.lsb - n0) * 4);
+    const int kb0 = c.kb0, nkb = c.nkb;
+    const bool chain = kFast && wave_scales_pow2(p, m0, n0, kb0, nkb, lane);
+
+    WaveLane o;
+    o.r16 = lane & 15;
+    o.q4 = lane >> 4;
+    o.a_lo = swz(o.r16, o.q4);
+    o.a_hi = swz(o.r16, o.q4 + 4);
+    o.b_lo = kVA + swz(o.r16, o.q4);
+    o.b_hi = kVA + swz(o.r16, o.q4 + 4);
+    // (stage offsets hidden from the compiler: folded to constants they lose
+    // the restrict scopes the loop's waits rely on)
+    int s0_off = 0, s1_off = kVStage, s2_off = 2 * kVStage;
+    asm volatile("" : "+s"(s0_off), "+s"(s1_off), "+s"(s2_off));
+#pragma unroll
+    for (int b = 0; b < kVStages; ++b) wave_load_block(p, s, smem + b * kVStage, kb0 + b, b < nkb, lane);
+
+    v4f acc[kTM][kTN];
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (chain)
+        wave_main_loop<true, kFmtA, kFmtB>(p, s, smem + s0_off, smem + s1_off, smem + s2_off, acc, o, kb0, nkb, lane);
+    else
+        wave_main_loop<false, kFmtA, kFmtB>(p, s, smem + s0_off, smem + s1_off, smem + s2_off, acc, o, kb0, nkb, lane);
+    epilogue<kEpi, false, kQuant>(p, acc, c.m0, c.n0, c.out_off, p.bias, p.bias_grad, smem, wave, lane);
+}
+
 #if TE_GEMM_PART < 0 || TE_GEMM_PART == 4
 __global__ void zero_f32_kernel(float* p, int64_t n)
 {
@@ -1493,6 +1688,25 @@ hipError_t launch_epi(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s
     return hipGetLastError();
 }
 
+// (dense products without the transposed store: launch_gemm's choice)
+template <int kFmtA, int kFmtB, bool kFast>
+hipError_t launch_wave_epi(const GemmArgs& a, dim3 grid, hipStream_t s)
+{
+    const bool q = a.q_out != nullptr;
+    switch (a.epi) {
+    case Epi::Wgrad: gemm_nt_wave_kernel<kFmtA, kFmtB, kFast, (int)Epi::Wgrad, 0><<<grid, 64, 0, s>>>(a); break;
+    case Epi::Fwd:
+        if (q) gemm_nt_wave_kernel<kFmtA, kFmtB, kFast, (int)Epi::Fwd, 1><<<grid, 64, 0, s>>>(a);
+        else gemm_nt_wave_kernel<kFmtA, kFmtB, kFast, (int)Epi::Fwd, 0><<<grid, 64, 0, s>>>(a);
+        break;
+    case Epi::Dgrad:
+        if (q) gemm_nt_wave_kernel<kFmtA, kFmtB, kFast, (int)Epi::Dgrad, 1><<<grid, 64, 0, s>>>(a);
+        else gemm_nt_wave_kernel<kFmtA, kFmtB, kFast, (int)Epi::Dgrad, 0><<<grid, 64, 0, s>>>(a);
+        break;
+    }
+    return hipGetLastError();
+}
+
 template <int kFmtA, int kFmtB>
 hipError_t launch_policy(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s)
 {
@@ -1500,19 +1714,37 @@ hipError_t launch_policy(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_
                   : launch_epi<kFmtA, kFmtB, false>(a, grid, tiles, s);
 }
 
+template <int kFmtA, int kFmtB>
+hipError_t launch_wave_policy(const GemmArgs& a, dim3 grid, hipStream_t s)
+{
+    return a.fast ? launch_wave_epi<kFmtA, kFmtB, true>(a, grid, s) : launch_wave_epi<kFmtA, kFmtB, false>(a, grid, s);
+}
+
 }  // namespace
 
-// One translation unit per operand-format pair (TE_GEMM_PART 0-3) and one for
-// the host side (4), so the kernel instantiations compile in parallel; without
-// TE_GEMM_PART everything is in one unit.
+// One translation unit per operand-format pair for the persistent kernels
+// (TE_GEMM_PART 0-3), one per pair for the wave kernels (5-8: in a unit of
+// their own, the persistent kernels' register allocation stays as it is) and
+// one for the host side (4), so the instantiations compile in parallel;
+// without TE_GEMM_PART everything is in one unit.
 hipError_t launch_pair_e4_e4(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s);
+hipError_t launch_wave_pair_e4_e4(const GemmArgs& a, dim3 grid, hipStream_t s);
 hipError_t launch_pair_e5_e4(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s);
+hipError_t launch_wave_pair_e5_e4(const GemmArgs& a, dim3 grid, hipStream_t s);
 hipError_t launch_pair_e4_e5(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s);
+hipError_t launch_wave_pair_e4_e5(const GemmArgs& a, dim3 grid, hipStream_t s);
 hipError_t launch_pair_e5_e5(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s);
+hipError_t launch_wave_pair_e5_e5(const GemmArgs& a, dim3 grid, hipStream_t s);
 #if TE_GEMM_PART < 0 || TE_GEMM_PART == 0
 hipError_t launch_pair_e4_e4(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s)
 {
     return launch_policy<FMT_E4M3, FMT_E4M3>(a, grid, tiles, s);
+}
+#endif
+#if TE_GEMM_PART < 0 || TE_GEMM_PART == 5
+hipError_t launch_wave_pair_e4_e4(const GemmArgs& a, dim3 grid, hipStream_t s)
+{
+    return launch_wave_policy<FMT_E4M3, FMT_E4M3>(a, grid, s);
 }
 #endif
 #if TE_GEMM_PART < 0 || TE_GEMM_PART == 1
@@ -1521,16 +1753,34 @@ hipError_t launch_pair_e5_e4(const GemmArgs& a, dim3 grid, int64_t tiles, hipStr
     return launch_policy<FMT_E5M2, FMT_E4M3>(a, grid, tiles, s);
 }
 #endif
+#if TE_GEMM_PART < 0 || TE_GEMM_PART == 6
+hipError_t launch_wave_pair_e5_e4(const GemmArgs& a, dim3 grid, hipStream_t s)
+{
+    return launch_wave_policy<FMT_E5M2, FMT_E4M3>(a, grid, s);
+}
+#endif
 #if TE_GEMM_PART < 0 || TE_GEMM_PART == 2
 hipError_t launch_pair_e4_e5(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s)
 {
     return launch_policy<FMT_E4M3, FMT_E5M2>(a, grid, tiles, s);
 }
 #endif
+#if TE_GEMM_PART < 0 || TE_GEMM_PART == 7
+hipError_t launch_wave_pair_e4_e5(const GemmArgs& a, dim3 grid, hipStream_t s)
+{
+    return launch_wave_policy<FMT_E4M3, FMT_E5M2>(a, grid, s);
+}
+#endif
 #if TE_GEMM_PART < 0 || TE_GEMM_PART == 3
 hipError_t launch_pair_e5_e5(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s)
 {
     return launch_policy<FMT_E5M2, FMT_E5M2>(a, grid, tiles, s);
+}
+#endif
+#if TE_GEMM_PART < 0 || TE_GEMM_PART == 8
+hipError_t launch_wave_pair_e5_e5(const GemmArgs& a, dim3 grid, hipStream_t s)
+{
+    return launch_wave_policy<FMT_E5M2, FMT_E5M2>(a, grid, s);
 }
 #endif
 
@@ -1549,19 +1799,50 @@ int device_cus()
     return cached[dev];
 }
 
+// Which kernel takes a dense product: the wave-per-workgroup one when the
+// 256 x 256 tiles are too few to give every compute unit one (each of their
+// eight wave tiles then gets one) and the contraction is short, the
+// persistent one otherwise.  Measured on 256 x 256 and 512 x 512 outputs (one
+// and four tiles): the wave path's fixed cost is ~5 us lower, but one wave
+// alone on its compute unit takes ~1.7 us per 128-deep block against ~1.3 us
+// for eight waves sharing one, so past ~11 blocks the persistent kernel is
+// ahead; the cut is at 8.  The environment variable TE_FP8_GEMM_PATH ("wave"
+// or "persistent") overrides the choice for the products the wave kernel
+// supports.
+constexpr int kWavePathMaxBlocks = 8;
+
+bool use_wave_path(const GemmArgs& a, int64_t tiles, int cus)
+{
+    const bool supported = a.num_groups == 1 && !a.group_k_dev && !a.m_block_group && !a.qt_out;
+    if (!supported) return false;
+    const char* env = std::getenv("TE_FP8_GEMM_PATH");
+    if (env && std::strcmp(env, "wave") == 0) return true;
+    if (env && std::strcmp(env, "persistent") == 0) return false;
+    return tiles * kWaves <= cus && a.groups[0].kb_len <= kWavePathMaxBlocks;
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream, LaunchInfo* info)
 {
     const int64_t tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN) * a.num_groups;
-    // one persistent workgroup per compute unit (the two stages fill most of its LDS)
-    const int64_t blocks = std::min<int64_t>(tiles, device_cus());
+    const int cus = device_cus();
+    const bool wave_path = use_wave_path(a, tiles, cus);
+    // persistent: one workgroup per compute unit (the two stages fill most of its
+    // LDS); wave path: one single-wave workgroup per wave tile
+    const int64_t blocks = wave_path ? tiles * kWaves : std::min<int64_t>(tiles, cus);
     if (info) {
-        info->tile_m = kBM;
-        info->tile_n = kBN;
-        info->threads = kThreads;
+        info->tile_m = wave_path ? kWM : kBM;
+        info->tile_n = wave_path ? kWN : kBN;
+        info->threads = wave_path ? 64 : kThreads;
         info->grid = blocks;
     }
     if (blocks <= 0) return hipSuccess;
     const dim3 grid((unsigned)blocks);
+    if (wave_path) {
+        if (a.fmt_a == FMT_E4M3 && a.fmt_b == FMT_E4M3) return launch_wave_pair_e4_e4(a, grid, stream);
+        if (a.fmt_a == FMT_E5M2 && a.fmt_b == FMT_E4M3) return launch_wave_pair_e5_e4(a, grid, stream);
+        if (a.fmt_a == FMT_E4M3 && a.fmt_b == FMT_E5M2) return launch_wave_pair_e4_e5(a, grid, stream);
+        return launch_wave_pair_e5_e5(a, grid, stream);
+    }
     if (a.fmt_a == FMT_E4M3 && a.fmt_b == FMT_E4M3) return launch_pair_e4_e4(a, grid, tiles, stream);
     if (a.fmt_a == FMT_E5M2 && a.fmt_b == FMT_E4M3) return launch_pair_e5_e4(a, grid, tiles, stream);
     if (a.fmt_a == FMT_E4M3 && a.fmt_b == FMT_E5M2) return launch_pair_e4_e5(a, grid, tiles, stream);

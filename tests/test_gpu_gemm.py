@@ -39,6 +39,14 @@ def epi_chain(epi):
         (GELU_CHAIN if epi & (te.TE_EPI_GELU | te.TE_EPI_DGELU) else 0)
 
 
+@pytest.fixture(params=["wave", "persistent"])
+def gemm_path(request, monkeypatch):
+    """Small products run on both GEMM kernels: the wave-per-workgroup one (the library's choice for
+    products with few 256 x 256 tiles) and, forced through TE_FP8_GEMM_PATH, the persistent one."""
+    monkeypatch.setenv("TE_FP8_GEMM_PATH", request.param)
+    return request.param
+
+
 def operand(seed, rows, K, dt, std=1.0, pow2=False):
     bits = W.normal_bf16(np.random.SeedSequence(seed), (rows, K), std)
     q, s = oracle.cast_per_token(bits, OF[dt], pow2)
@@ -63,7 +71,7 @@ def grid_entries(qa, sa, fa, qb, sb, fb, rows, cols, k0=0, K=None):
 @pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
 @pytest.mark.parametrize("da,db", [(E4, E4), (E5, E4), (E4, E5), (E5, E5)])
 @pytest.mark.parametrize("M,N,K", [(300, 520, 384), (1, 1, 128), (256, 256, 512), (513, 200, 256)])
-def test_wgrad_small(accum, pow2, da, db, M, N, K):
+def test_wgrad_small(accum, pow2, da, db, M, N, K, gemm_path):
     qa, sa = operand(M * 3 + K, M, K, da, pow2=pow2)
     qb, sb = operand(N * 5 + K + 1, N, K, db, pow2=pow2)
     out0 = W.normal_f32(np.random.SeedSequence(M + N), (M, N))
@@ -96,7 +104,7 @@ def test_wgrad_max_k(accum, pow2):
 
 @pytest.mark.parametrize("da", [E4, E5])
 @pytest.mark.parametrize("M,N,K", [(300, 200, 384), (7, 16, 1024), (513, 64, 128)])
-def test_wgrad_with_bias_grad(da, M, N, K):
+def test_wgrad_with_bias_grad(da, M, N, K, gemm_path):
     """out += A B^T exactly as the plain call, plus bias_grad[m] = the dequantised row sums of A."""
     qa, sa = operand(M + K + 7, M, K, da)
     qb, sb = operand(N + K + 8, N, K, E4)
@@ -185,7 +193,7 @@ def fwd_case(M, N, K, epi, ydt, accum, pow2, xs=1.0, ws=1.0, seed=0):
 @pytest.mark.parametrize("epi", FWD_EPIS)
 @pytest.mark.parametrize("ydt", [te.TE_DTYPE_F32, te.TE_DTYPE_BF16])
 @pytest.mark.parametrize("M,N,K", [(300, 264, 512), (17, 36, 128)])
-def test_fwd_small(accum, pow2, epi, ydt, M, N, K):
+def test_fwd_small(accum, pow2, epi, ydt, M, N, K, gemm_path):
     qx, sx, qw, sw, b, y, z, zmag = fwd_case(M, N, K, epi, ydt, accum, pow2, seed=M)
     ymag = zmag * (GELU_LIP if epi & te.TE_EPI_GELU else 1.0)
     tdt = torch.float32 if ydt == te.TE_DTYPE_F32 else torch.bfloat16
@@ -233,7 +241,7 @@ def quant_fwd(qx, sx, qw, sw, b, epi, accum, qdt, cast_pow2, M, N, pre=None):
 @pytest.mark.parametrize("qdt,cast_pow2", [(te.TE_DTYPE_E4M3, False), (te.TE_DTYPE_E5M2, False),
                                            (te.TE_DTYPE_E4M3, True)])
 @pytest.mark.parametrize("M,N,K", [(300, 384, 512), (17, 128, 128)])
-def test_fwd_quant(accum, pow2, epi, qdt, cast_pow2, M, N, K):
+def test_fwd_quant(accum, pow2, epi, qdt, cast_pow2, M, N, K, gemm_path):
     """The quantised forward equals the per-token cast of the forward's own fp32 result (the oracle's
     fp32-input cast of the fp32 y the plain forward call returns: the codes are decided in the
     kernel's fp32), and that fp32 y matches the fp64 oracle."""
@@ -418,7 +426,7 @@ DG_EPIS = [te.TE_EPI_NONE, te.TE_EPI_DGELU, te.TE_EPI_BGRAD, te.TE_EPI_DGELU | t
 @pytest.mark.parametrize("epi", DG_EPIS)
 @pytest.mark.parametrize("dxdt", [te.TE_DTYPE_F32, te.TE_DTYPE_BF16])
 @pytest.mark.parametrize("M,N,K", [(260, 300, 640), (3, 20, 128)])
-def test_dgrad_small(accum, pow2, epi, dxdt, M, N, K):
+def test_dgrad_small(accum, pow2, epi, dxdt, M, N, K, gemm_path):
     qa, sa = operand(M + 21, M, K, E5, 1e-3, pow2)
     qb, sb = operand(N + 22, N, K, E4, 0.02, pow2)
     zb = W.normal_bf16(np.random.SeedSequence(M + 23), (M, N), 1.28)
@@ -448,7 +456,7 @@ def test_dgrad_small(accum, pow2, epi, dxdt, M, N, K):
 
 @pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
 @pytest.mark.parametrize("M", [3, 301])
-def test_dgrad_bias_grad_ignores_scale_padding(accum, pow2, M):
+def test_dgrad_bias_grad_ignores_scale_padding(accum, pow2, M, gemm_path):
     """Entries of a scale array past the last row are padding the library never uses.  With M not a
     multiple of 4 the last 16-byte run of every block's row scales holds some; NaN there must leave
     dx, its quantised cast and the deterministic bias gradient bit-identical to the calls whose
@@ -489,7 +497,7 @@ DGRAD_EPIS = [te.TE_EPI_NONE, te.TE_EPI_DGELU, te.TE_EPI_DGELU | te.TE_EPI_BGRAD
 @pytest.mark.parametrize("qdt,cast_pow2", [(te.TE_DTYPE_E5M2, False), (te.TE_DTYPE_E4M3, False),
                                            (te.TE_DTYPE_E5M2, True)])
 @pytest.mark.parametrize("M,N,K", [(300, 384, 512), (40, 128, 256)])
-def test_dgrad_quant(accum, pow2, epi, qdt, cast_pow2, M, N, K):
+def test_dgrad_quant(accum, pow2, epi, qdt, cast_pow2, M, N, K, gemm_path):
     """The quantised dgrad equals the per-token cast of the dgrad's own fp32 D (the oracle's
     fp32-input cast of the fp32 dx the plain call returns), that fp32 D and the bias gradient match
     the fp64 oracle, and nothing outside q, its scales and the bias gradient is written."""
@@ -528,7 +536,7 @@ def test_dgrad_quant(accum, pow2, epi, qdt, cast_pow2, M, N, K):
 @pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
 @pytest.mark.parametrize("epi", [te.TE_EPI_BGRAD, te.TE_EPI_DGELU | te.TE_EPI_BGRAD])
 @pytest.mark.parametrize("M,N,K", [(300, 264, 512), (600, 37, 128)])
-def test_dgrad_deterministic_bias_grad(accum, pow2, epi, M, N, K):
+def test_dgrad_deterministic_bias_grad(accum, pow2, epi, M, N, K, gemm_path):
     """The atomic-free bias gradient: within tolerance of the oracle, bit-identical from run to run,
     and the dx it writes is the plain call's dx bit for bit."""
     qa, sa = operand(M + 41, M, K, E5, 1e-3, pow2)

@@ -1,0 +1,125 @@
+"""The wave-per-workgroup GEMM path (products with few 256 x 256 tiles) against the persistent one.
+
+Both kernels take the same fragments, promote in the same order (FULL) or chain through the matrix
+core (FAST on power-of-two scales) and share the epilogue, so on the same inputs every output that is
+not summed with atomics must come out bit for bit the same; the oracle parity of each path is
+covered by test_gpu_gemm.py, which runs its small products on both.  Shapes: the tiny Linear
+(256 x 256 x 512, one tile), one wave tile exactly, one element past it in both dimensions, and a
+ragged product spanning two tiles each way.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import bf16_dev, dev, host, sdev
+
+te = pytest.importorskip("fp8_linear_layer_amd")
+pytestmark = pytest.mark.gpu
+
+E4, E5 = te.TE_DTYPE_E4M3, te.TE_DTYPE_E5M2
+FULL, FAST = te.TE_ACCUM_FULL_FP32, te.TE_ACCUM_FAST
+SHAPES = [(256, 256, 512), (64, 128, 256), (65, 129, 128), (300, 264, 384)]
+POL = [(FULL, False), (FAST, True), (FAST, False)]
+PID = ["full", "fast-pow2", "fast-ieee"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    te.load_library()
+
+
+def operand(seed, rows, K, fmt, std, pow2):
+    bits = W.normal_bf16(np.random.SeedSequence(seed), (rows, K), std)
+    q, s = oracle.cast_per_token(bits, fmt, pow2)
+    return dev(q), sdev(s)
+
+
+def both(monkeypatch, run):
+    """run() on the wave path, then on the persistent one; each returns a list of tensors."""
+    out = {}
+    for path in ("wave", "persistent"):
+        monkeypatch.setenv("TE_FP8_GEMM_PATH", path)
+        out[path] = [host(t).contiguous() for t in run()]
+        torch.cuda.synchronize()
+    return out["wave"], out["persistent"]
+
+
+def padded(M, N, dtype, fill=0.0):
+    """An [M, N] view of a buffer whose rows are padded to 16 bytes (the ABI's stride rule)."""
+    per = 16 // torch.tensor([], dtype=dtype).element_size()
+    return torch.full((M, (N + per - 1) // per * per), fill, dtype=dtype, device="cuda")[:, :N]
+
+
+def same_bits(a, b, what):
+    for i, (x, y) in enumerate(zip(a, b)):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"{what}: output {i} differs between the paths"
+
+
+@pytest.mark.parametrize("accum,pow2", POL, ids=PID)
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_wgrad_paths_agree(monkeypatch, accum, pow2, M, N, K):
+    A, SA = operand(M + 1, M, K, oracle.E4M3, 1.0, pow2)
+    B, SB = operand(N + 2, N, K, oracle.E4M3, 1.0, pow2)
+    out0 = dev(W.normal_f32(np.random.SeedSequence(M + N + 3), (M, N)))
+
+    def run():
+        out = padded(M, N, torch.float32)
+        out.copy_(out0)
+        te.te_fp8_wgrad_accum(A, SA, E4, B, SB, E4, out, accum)
+        return [out]
+    same_bits(*both(monkeypatch, run), "wgrad")
+
+
+@pytest.mark.parametrize("accum,pow2", POL, ids=PID)
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("ydt", [te.TE_DTYPE_BF16, te.TE_DTYPE_F32])
+def test_fwd_paths_agree(monkeypatch, accum, pow2, M, N, K, ydt):
+    X, SX = operand(M + 11, M, K, oracle.E4M3, 1.0, pow2)
+    Wt, SW = operand(N + 12, N, K, oracle.E4M3, 0.02, pow2)
+    b = bf16_dev(W.normal_bf16(np.random.SeedSequence(N + 13), (N,), 0.1))
+    epi = te.TE_EPI_BIAS | te.TE_EPI_GELU | te.TE_EPI_AUX_PREACT
+
+    def run():
+        z = padded(M, N, torch.bfloat16)
+        y = padded(M, N, torch.bfloat16 if ydt == te.TE_DTYPE_BF16 else torch.float32)
+        te.te_fp8_gemm_fwd(X, SX, E4, Wt, SW, E4, bias=b, epilogue=epi, y=y, y_dtype=ydt, preact=z, accum=accum)
+        return [y, z]
+    same_bits(*both(monkeypatch, run), "fwd")
+
+
+@pytest.mark.parametrize("accum,pow2", POL, ids=PID)
+@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (300, 384, 256)])
+def test_fwd_quant_paths_agree(monkeypatch, accum, pow2, M, N, K):
+    X, SX = operand(M + 21, M, K, oracle.E4M3, 1.0, pow2)
+    Wt, SW = operand(N + 22, N, K, oracle.E4M3, 0.02, pow2)
+    b = bf16_dev(W.normal_bf16(np.random.SeedSequence(N + 23), (N,), 0.1))
+
+    def run():
+        q, s = te.te_fp8_gemm_fwd_quant(X, SX, E4, Wt, SW, E4, bias=b, epilogue=te.TE_EPI_BIAS | te.TE_EPI_GELU,
+                                        accum=accum)
+        return [q, s[:, :M]]
+    same_bits(*both(monkeypatch, run), "fwd quant")
+
+
+@pytest.mark.parametrize("accum,pow2", POL, ids=PID)
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_dgrad_paths_agree(monkeypatch, accum, pow2, M, N, K):
+    """dX (fp32, after dGELU) and the deterministic bias gradient, whose workspace rows the wave
+    path fills per wave place (zero for a place past M) exactly as the persistent kernel's waves."""
+    D, SD = operand(M + 31, M, K, oracle.E5M2, 1e-3, pow2)
+    Wt, SW = operand(N + 32, N, K, oracle.E4M3, 0.02, pow2)
+    z = padded(M, N, torch.bfloat16)
+    z.copy_(bf16_dev(W.normal_bf16(np.random.SeedSequence(M + 33), (M, N), 1.28)))
+    epi = te.TE_EPI_DGELU | te.TE_EPI_BGRAD
+
+    def run():
+        bg = torch.full((N,), 7.0, dtype=torch.float32, device="cuda")
+        dx = padded(M, N, torch.float32)
+        te.te_fp8_gemm_dgrad_deterministic(D, SD, E5, Wt, SW, E4, bg, epilogue=epi, preact=z, dx=dx,
+                                           dx_dtype=te.TE_DTYPE_F32, accum=accum)
+        return [dx, bg]
+    same_bits(*both(monkeypatch, run), "dgrad")
