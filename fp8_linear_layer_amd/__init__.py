@@ -41,6 +41,7 @@ EXPORTED = ("te_cast_fp8_per_token", "te_cast_fp8_per_token_batch", "te_cast_fp8
             "te_fp8_wgrad_accum_bgrad", "te_fp8_gemm_dgrad", "te_fp8_wgrad_accum",
             "te_fp8_kgrouped_wgrad", "te_fp8_kgrouped_wgrad_device_sizes", "te_fp8_mgrouped_gemm_fwd",
             "te_fp8_mgrouped_gemm_dgrad",
+            "te_fp8_mgrouped_gemm_dgrad_deterministic",
             "te_status_string", "te_last_error_message", "te_scale_ld")
 
 
@@ -105,6 +106,9 @@ def load_library():
     lib.te_fp8_mgrouped_gemm_dgrad.restype = I
     lib.te_fp8_mgrouped_gemm_dgrad.argtypes = [P, P, I, P, P, I, I64, I64, I64, I32, P, U32, P, I64, P, P, I, I64, I,
                                                P]
+    lib.te_fp8_mgrouped_gemm_dgrad_deterministic.restype = I
+    lib.te_fp8_mgrouped_gemm_dgrad_deterministic.argtypes = [P, P, I, P, P, I, I64, I64, I64, I32, P, U32, P, I64, P,
+                                                             P, I64, P, I, I64, I, P]
     _lib = lib
     return lib
 
@@ -439,6 +443,35 @@ def te_fp8_mgrouped_gemm_dgrad(dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype,
         _ptr(dy), _ptr(dy_scales), dy_dtype, _ptr(wt), _ptr(wt_scales), wt_dtype, sum_m, N, K, G, _ptr(m_block_group),
         epilogue, _ptr(preact), preact.stride(0) if preact is not None else 0, _ptr(bias_grad), _ptr(dx), dx_dtype,
         dx.stride(0), accum, _stream(stream)))
+    return dx
+
+
+def te_fp8_mgrouped_gemm_dgrad_deterministic(dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, m_block_group,
+                                             bias_grad, epilogue=TE_EPI_BGRAD, preact=None, workspace=None, dx=None,
+                                             dx_dtype=TE_DTYPE_BF16, accum=TE_ACCUM_FULL_FP32, stream=None):
+    """te_fp8_mgrouped_gemm_dgrad with the per-expert bias gradients summed in a fixed order through a
+    workspace (allocated here when not given); returns dx."""
+    sum_m, K = dy.shape
+    G, N, K2 = wt.shape
+    assert K2 == K and wt.is_contiguous()
+    assert m_block_group.dtype == torch.int32 and m_block_group.is_cuda and m_block_group.is_contiguous()
+    assert m_block_group.numel() * 256 == sum_m
+    want = (G, K // 128, scale_ld(N))
+    if wt_scales.dtype != torch.float32 or not wt_scales.is_contiguous() or tuple(wt_scales.shape) != want:
+        raise TeFp8Error(1, f"wt_scales: expected contiguous fp32 scales of shape {want}")
+    _scales_ok(dy_scales, sum_m, K, "dy_scales")
+    assert bias_grad.dtype == torch.float32 and bias_grad.is_contiguous() and bias_grad.numel() == G * N
+    lib = load_library()
+    need = int(lib.te_fp8_dgrad_bgrad_workspace_bytes(sum_m, N))
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dy.device)
+    if dx is None:
+        dx = torch.empty((sum_m, N), dtype=torch.bfloat16 if dx_dtype == TE_DTYPE_BF16 else torch.float32,
+                         device=dy.device)
+    _check(lib.te_fp8_mgrouped_gemm_dgrad_deterministic(
+        _ptr(dy), _ptr(dy_scales), dy_dtype, _ptr(wt), _ptr(wt_scales), wt_dtype, sum_m, N, K, G, _ptr(m_block_group),
+        epilogue, _ptr(preact), preact.stride(0) if preact is not None else 0, _ptr(bias_grad), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(dx), dx_dtype, dx.stride(0), accum, _stream(stream)))
     return dx
 
 

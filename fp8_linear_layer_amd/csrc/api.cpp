@@ -797,6 +797,72 @@ te_status_t te_fp8_gemm_dgrad_deterministic_noalloc(const void* dy, const float*
     }
 }
 
+// The M-grouped data gradient; with `ws` set the per-expert bias gradient
+// goes through that column-sum workspace and an ordered reduction instead of
+// atomics.
+static te_status_t mgrouped_dgrad(const char* fn, const void* dy, const float* dy_scales, te_dtype_t dy_dtype,
+                                  const void* wt, const float* wt_scales, te_dtype_t wt_dtype, int64_t sum_m,
+                                  int64_t N, int64_t K, int32_t G, const int32_t* m_block_group, uint32_t epilogue,
+                                  const void* preact_bf16, int64_t ld_preact, float* bias_grad, float* ws, void* dx,
+                                  te_dtype_t dx_dtype, int64_t ld_dx, te_accum_t accum, hipStream_t stream)
+{
+    if (!m_block_group) return fail(TE_ERR_INVALID_ARGUMENT, "%s: m_block_group is null", fn);
+    if (!aligned(m_block_group, 4)) return fail(TE_ERR_MISALIGNED, "%s: m_block_group must be 4-byte aligned", fn);
+    if (G < 1 || G > 1024) return fail(TE_ERR_INVALID_ARGUMENT, "%s: G must be in [1, 1024] (got %d)", fn, (int)G);
+    if (sum_m < tefp8::kMGroupRows || sum_m % tefp8::kMGroupRows != 0)
+        return fail(TE_ERR_INVALID_ARGUMENT, "%s: sum_m must be a positive multiple of %d (got %lld)", fn,
+                    tefp8::kMGroupRows, (long long)sum_m);
+    te_status_t st = check_operands(fn, dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, sum_m, N, K, accum);
+    if (st != TE_OK) return st;
+    const uint32_t allowed = TE_EPI_DGELU | TE_EPI_BGRAD;
+    if (epilogue & ~allowed) return fail(TE_ERR_INVALID_ARGUMENT, "%s: epilogue flags 0x%x are not dgrad flags", fn, epilogue);
+    if (ws && !(epilogue & TE_EPI_BGRAD))
+        return fail(TE_ERR_INVALID_ARGUMENT, "%s: the epilogue must include TE_EPI_BGRAD", fn);
+    if (epilogue & TE_EPI_DGELU) {
+        if (!preact_bf16) return fail(TE_ERR_INVALID_ARGUMENT, "%s: TE_EPI_DGELU needs preact_bf16", fn);
+        if (ld_preact < N) return fail(TE_ERR_INVALID_ARGUMENT, "%s: ld_preact (%lld) is below N", fn, (long long)ld_preact);
+        if (!aligned(preact_bf16, 16) || ld_preact % 8 != 0)
+            return fail(TE_ERR_MISALIGNED, "%s: preact must be 16-byte aligned with ld_preact a multiple of 8", fn);
+    } else if (preact_bf16) {
+        return fail(TE_ERR_INVALID_ARGUMENT, "%s: preact given without TE_EPI_DGELU", fn);
+    }
+    if (epilogue & TE_EPI_BGRAD) {
+        if (!bias_grad) return fail(TE_ERR_INVALID_ARGUMENT, "%s: TE_EPI_BGRAD needs bias_grad", fn);
+        if (!aligned(bias_grad, 4)) return fail(TE_ERR_MISALIGNED, "%s: bias_grad must be 4-byte aligned", fn);
+    } else if (bias_grad) {
+        return fail(TE_ERR_INVALID_ARGUMENT, "%s: bias_grad given without TE_EPI_BGRAD", fn);
+    }
+    st = check_output(fn, "dx", dx, dx_dtype, ld_dx, N);
+    if (st != TE_OK) return st;
+    tefp8::GemmArgs g = base_args(dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, sum_m, N, K, accum);
+    g.epi = tefp8::Epi::Dgrad;
+    g.flags = epilogue;
+    g.out = dx;
+    g.out_bf16 = dx_dtype == TE_DTYPE_BF16;
+    g.ld_out = ld_dx;
+    g.preact = static_cast<const uint16_t*>(preact_bf16);
+    g.ld_aux = ld_preact;
+    g.bias_grad = bias_grad;
+    g.m_block_group = m_block_group;
+    g.num_b_groups = G;
+    g.b_group_stride = N * K;
+    g.sb_group_stride = (K / 128) * te_scale_ld(N);
+    g.bias_group_stride = N;
+    if (ws) {
+        g.bgrad_ws = ws;
+        g.bgrad_ws_ld = (N + 3) / 4 * 4;
+    } else if (epilogue & TE_EPI_BGRAD) {
+        hipError_t e = tefp8::launch_zero_f32(bias_grad, (int64_t)G * N, stream);
+        if (e != hipSuccess) return fail(TE_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+    }
+    st = launch(fn, g, stream, K, dy_dtype, wt_dtype, accum, epilogue);
+    if (st != TE_OK || !ws) return st;
+    hipError_t e = tefp8::launch_mgrouped_bgrad_reduce(ws, sum_m / tefp8::kMGroupRows, g.bgrad_ws_ld, N, G,
+                                                       m_block_group, bias_grad, stream);
+    if (e != hipSuccess) return fail(TE_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
 te_status_t te_fp8_mgrouped_gemm_dgrad(const void* dy, const float* dy_scales, te_dtype_t dy_dtype,
                                        const void* wt, const float* wt_scales, te_dtype_t wt_dtype,
                                        int64_t sum_m, int64_t N, int64_t K, int32_t G, const int32_t* m_block_group,
@@ -805,54 +871,36 @@ te_status_t te_fp8_mgrouped_gemm_dgrad(const void* dy, const float* dy_scales, t
                                        te_accum_t accum, hipStream_t stream)
 {
     try {
-        const char* fn = "te_fp8_mgrouped_gemm_dgrad";
-        if (!m_block_group) return fail(TE_ERR_INVALID_ARGUMENT, "%s: m_block_group is null", fn);
-        if (!aligned(m_block_group, 4)) return fail(TE_ERR_MISALIGNED, "%s: m_block_group must be 4-byte aligned", fn);
-        if (G < 1 || G > 1024) return fail(TE_ERR_INVALID_ARGUMENT, "%s: G must be in [1, 1024] (got %d)", fn, (int)G);
-        if (sum_m < tefp8::kMGroupRows || sum_m % tefp8::kMGroupRows != 0)
-            return fail(TE_ERR_INVALID_ARGUMENT, "%s: sum_m must be a positive multiple of %d (got %lld)", fn,
-                        tefp8::kMGroupRows, (long long)sum_m);
-        te_status_t st = check_operands(fn, dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, sum_m, N, K, accum);
-        if (st != TE_OK) return st;
-        const uint32_t allowed = TE_EPI_DGELU | TE_EPI_BGRAD;
-        if (epilogue & ~allowed) return fail(TE_ERR_INVALID_ARGUMENT, "%s: epilogue flags 0x%x are not dgrad flags", fn, epilogue);
-        if (epilogue & TE_EPI_DGELU) {
-            if (!preact_bf16) return fail(TE_ERR_INVALID_ARGUMENT, "%s: TE_EPI_DGELU needs preact_bf16", fn);
-            if (ld_preact < N) return fail(TE_ERR_INVALID_ARGUMENT, "%s: ld_preact (%lld) is below N", fn, (long long)ld_preact);
-            if (!aligned(preact_bf16, 16) || ld_preact % 8 != 0)
-                return fail(TE_ERR_MISALIGNED, "%s: preact must be 16-byte aligned with ld_preact a multiple of 8", fn);
-        } else if (preact_bf16) {
-            return fail(TE_ERR_INVALID_ARGUMENT, "%s: preact given without TE_EPI_DGELU", fn);
-        }
-        if (epilogue & TE_EPI_BGRAD) {
-            if (!bias_grad) return fail(TE_ERR_INVALID_ARGUMENT, "%s: TE_EPI_BGRAD needs bias_grad", fn);
-            if (!aligned(bias_grad, 4)) return fail(TE_ERR_MISALIGNED, "%s: bias_grad must be 4-byte aligned", fn);
-        } else if (bias_grad) {
-            return fail(TE_ERR_INVALID_ARGUMENT, "%s: bias_grad given without TE_EPI_BGRAD", fn);
-        }
-        st = check_output(fn, "dx", dx, dx_dtype, ld_dx, N);
-        if (st != TE_OK) return st;
-        tefp8::GemmArgs g = base_args(dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, sum_m, N, K, accum);
-        g.epi = tefp8::Epi::Dgrad;
-        g.flags = epilogue;
-        g.out = dx;
-        g.out_bf16 = dx_dtype == TE_DTYPE_BF16;
-        g.ld_out = ld_dx;
-        g.preact = static_cast<const uint16_t*>(preact_bf16);
-        g.ld_aux = ld_preact;
-        g.bias_grad = bias_grad;
-        g.m_block_group = m_block_group;
-        g.num_b_groups = G;
-        g.b_group_stride = N * K;
-        g.sb_group_stride = (K / 128) * te_scale_ld(N);
-        g.bias_group_stride = N;
-        if (epilogue & TE_EPI_BGRAD) {
-            hipError_t e = tefp8::launch_zero_f32(bias_grad, (int64_t)G * N, stream);
-            if (e != hipSuccess) return fail(TE_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
-        }
-        return launch(fn, g, stream, K, dy_dtype, wt_dtype, accum, epilogue);
+        return mgrouped_dgrad("te_fp8_mgrouped_gemm_dgrad", dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, sum_m,
+                              N, K, G, m_block_group, epilogue, preact_bf16, ld_preact, bias_grad, nullptr, dx,
+                              dx_dtype, ld_dx, accum, stream);
     } catch (...) {
         return fail(TE_ERR_INTERNAL, "te_fp8_mgrouped_gemm_dgrad: internal error");
+    }
+}
+
+te_status_t te_fp8_mgrouped_gemm_dgrad_deterministic(const void* dy, const float* dy_scales, te_dtype_t dy_dtype,
+                                                     const void* wt, const float* wt_scales, te_dtype_t wt_dtype,
+                                                     int64_t sum_m, int64_t N, int64_t K, int32_t G,
+                                                     const int32_t* m_block_group, uint32_t epilogue,
+                                                     const void* preact_bf16, int64_t ld_preact, float* bias_grad,
+                                                     void* workspace, int64_t workspace_bytes, void* dx,
+                                                     te_dtype_t dx_dtype, int64_t ld_dx, te_accum_t accum,
+                                                     hipStream_t stream)
+{
+    try {
+        const char* fn = "te_fp8_mgrouped_gemm_dgrad_deterministic";
+        if (!workspace) return fail(TE_ERR_INVALID_ARGUMENT, "%s: workspace is null", fn);
+        if (!aligned(workspace, 16)) return fail(TE_ERR_MISALIGNED, "%s: workspace must be 16-byte aligned", fn);
+        const int64_t need = te_fp8_dgrad_bgrad_workspace_bytes(sum_m, N);
+        if (sum_m >= 1 && N >= 1 && workspace_bytes < need)
+            return fail(TE_ERR_INVALID_ARGUMENT, "%s: workspace_bytes %lld below the %lld bytes needed", fn,
+                        (long long)workspace_bytes, (long long)need);
+        return mgrouped_dgrad(fn, dy, dy_scales, dy_dtype, wt, wt_scales, wt_dtype, sum_m, N, K, G, m_block_group,
+                              epilogue, preact_bf16, ld_preact, bias_grad, static_cast<float*>(workspace), dx,
+                              dx_dtype, ld_dx, accum, stream);
+    } catch (...) {
+        return fail(TE_ERR_INTERNAL, "te_fp8_mgrouped_gemm_dgrad_deterministic: internal error");
     }
 }
 

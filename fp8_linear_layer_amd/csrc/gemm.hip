@@ -1663,6 +1663,25 @@ __global__ void bgrad_reduce_kernel(const float* __restrict__ ws, int64_t rows, 
     bias_grad[n] = s;
 }
 
+// The M-grouped form: bias_grad[e][n] sums, in block order, the four
+// workspace rows of every 256-row block whose expert is e (a skipped block's
+// rows were never written and are not read; an expert with no block gets 0).
+__global__ void mgrouped_bgrad_reduce_kernel(const float* __restrict__ ws, int64_t blocks, int64_t ld, int64_t N,
+                                             int32_t G, const int32_t* __restrict__ m_block_group,
+                                             float* __restrict__ bias_grad)
+{
+    const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int32_t e = (int32_t)blockIdx.y;
+    if (n >= N || e >= G) return;
+    float s = 0.0f;
+    for (int64_t b = 0; b < blocks; ++b) {
+        if (m_block_group[b] != e) continue;
+#pragma unroll
+        for (int r = 0; r < kBgradRowsPerTile; ++r) s += ws[(b * kBgradRowsPerTile + r) * ld + n];
+    }
+    bias_grad[(int64_t)e * N + n] = s;
+}
+
 #endif
 
 template <int kFmtA, int kFmtB, bool kFast>
@@ -1882,6 +1901,15 @@ hipError_t launch_bgrad_reduce(const float* ws, int64_t rows, int64_t ld, int64_
 {
     if (N <= 0) return hipSuccess;
     bgrad_reduce_kernel<<<(unsigned)((N + 255) / 256), 256, 0, stream>>>(ws, rows, ld, N, bias_grad);
+    return hipGetLastError();
+}
+
+hipError_t launch_mgrouped_bgrad_reduce(const float* ws, int64_t blocks, int64_t ld, int64_t N, int32_t G,
+                                        const int32_t* m_block_group, float* bias_grad, hipStream_t stream)
+{
+    if (N <= 0 || G <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((N + 255) / 256), (unsigned)G);
+    mgrouped_bgrad_reduce_kernel<<<grid, 256, 0, stream>>>(ws, blocks, ld, N, G, m_block_group, bias_grad);
     return hipGetLastError();
 }
 

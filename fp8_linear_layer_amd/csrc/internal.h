@@ -100,6 +100,10 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_bgrad_reduce(const float* ws, int64_t rows, int64_t ld, int64_t N, float* bias_grad,
                                hipStream_t stream);
 constexpr int kBgradRowsPerTile = 4;  // waves along M per 256-row tile
+// bias_grad[e][n] = sum over the 256-row blocks b with m_block_group[b] == e,
+// in order, of their kBgradRowsPerTile workspace rows (G experts, [G][N] out)
+hipError_t launch_mgrouped_bgrad_reduce(const float* ws, int64_t blocks, int64_t ld, int64_t N, int32_t G,
+                                        const int32_t* m_block_group, float* bias_grad, hipStream_t stream);
 // Device address of the library's static scratch array on the current device
 // (looked up once per device, then cached); its size is TE_NOALLOC_SCRATCH_BYTES.
 hipError_t noalloc_scratch(void** ptr);

@@ -22,6 +22,8 @@
  *   te_fp8_mgrouped_gemm_fwd          the experts' forward (and plain data gradient)
  *   te_fp8_mgrouped_gemm_dgrad        the experts' data gradient with dGELU and
  *                                     per-expert bias gradients
+ *   te_fp8_mgrouped_gemm_dgrad_deterministic   the same with the per-expert
+ *                                     bias gradients summed without atomics
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -514,6 +516,29 @@ te_status_t te_fp8_mgrouped_gemm_dgrad(const void* dy, const float* dy_scales, t
                                        uint32_t epilogue, const void* preact_bf16, int64_t ld_preact,
                                        float* bias_grad, void* dx, te_dtype_t dx_dtype, int64_t ld_dx,
                                        te_accum_t accum, hipStream_t stream);
+
+/*
+ * te_fp8_mgrouped_gemm_dgrad with run-to-run deterministic per-expert bias
+ * gradients, as te_fp8_gemm_dgrad_deterministic does it for the dense call:
+ * every 64-row slice of D stores its column sums to a row of the caller's
+ * workspace, and a second kernel sums, for each expert e and column n, the
+ * rows of expert e's blocks in block order (bias_grad is overwritten; an
+ * expert with no block gets zeros; a skipped block's rows are neither written
+ * nor read).  The epilogue must include TE_EPI_BGRAD.
+ *
+ *  workspace        device memory, 16-byte aligned, at least
+ *                   te_fp8_dgrad_bgrad_workspace_bytes(sum_m, N) bytes
+ *                   (contents on entry irrelevant; clobbered)
+ *  everything else  as te_fp8_mgrouped_gemm_dgrad
+ */
+te_status_t te_fp8_mgrouped_gemm_dgrad_deterministic(const void* dy, const float* dy_scales, te_dtype_t dy_dtype,
+                                                     const void* wt, const float* wt_scales, te_dtype_t wt_dtype,
+                                                     int64_t sum_m, int64_t N, int64_t K, int32_t G,
+                                                     const int32_t* m_block_group, uint32_t epilogue,
+                                                     const void* preact_bf16, int64_t ld_preact, float* bias_grad,
+                                                     void* workspace, int64_t workspace_bytes, void* dx,
+                                                     te_dtype_t dx_dtype, int64_t ld_dx, te_accum_t accum,
+                                                     hipStream_t stream);
 
 /* Static description of a status code. */
 const char* te_status_string(te_status_t status);

@@ -14,6 +14,11 @@ int device_cus() { return 256; }
 hipError_t launch_gemm(const GemmArgs&, hipStream_t, LaunchInfo*) { return hipErrorNoDevice; }
 hipError_t launch_zero_f32(float*, int64_t, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_bgrad_reduce(const float*, int64_t, int64_t, int64_t, float*, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_mgrouped_bgrad_reduce(const float*, int64_t, int64_t, int64_t, int32_t, const int32_t*, float*,
+                                        hipStream_t)
+{
+    return hipErrorNoDevice;
+}
 hipError_t noalloc_scratch(void**) { return hipErrorNoDevice; }
 hipError_t launch_cast(const uint16_t*, int64_t, int64_t, int64_t, int, bool, uint8_t*, int64_t, float*, int64_t,
                        hipStream_t, LaunchInfo*) { return hipErrorNoDevice; }

@@ -282,6 +282,33 @@ def test_mgrouped_dgrad_rejects(lib, kw, status):
     assert mgrouped_dg(lib, **kw) == status
 
 
+WSM = 0xB0000  # dummy device address of the M-grouped column-sum workspace
+
+
+def mgrouped_dgd(lib, mb=MB, G=4, sum_m=512, N=256, K=256, epi=16, pre=0, ldpre=0, bg=O, ws=WSM, wsb=1 << 20, dx=Z,
+                 dxdt=3, ldx=256, accum=1):
+    return lib.te_fp8_mgrouped_gemm_dgrad_deterministic(p(A), p(S), 2, p(B), p(S), 1, sum_m, N, K, G, p(mb), epi,
+                                                        p(pre), ldpre, p(bg), p(ws), wsb, p(dx), dxdt, ldx, accum,
+                                                        None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=0), INV), (dict(ws=WSM + 8), MISAL), (dict(wsb=8 * 256 * 4 - 4), INV), (dict(epi=0), INV),
+    (dict(epi=8), INV), (dict(bg=0), INV), (dict(bg=O + 2), MISAL), (dict(mb=0), INV), (dict(G=0), INV),
+    (dict(sum_m=300), INV), (dict(dx=0), INV), (dict(ldx=128), INV), (dict(accum=0), INV),
+    (dict(epi=24, pre=0), INV),
+])
+def test_mgrouped_dgrad_deterministic_rejects(lib, kw, status):
+    assert mgrouped_dgd(lib, **kw) == status
+    assert "te_fp8_mgrouped_gemm_dgrad_deterministic" in lib.te_last_error_message().decode()
+
+
+def test_mgrouped_dgrad_deterministic_workspace_is_the_dense_size(lib):
+    # one row of N (padded to 4) fp32 column sums per 64 token rows, as the dense call
+    assert lib.te_fp8_dgrad_bgrad_workspace_bytes(512, 256) == 8 * 256 * 4
+    assert lib.te_fp8_dgrad_bgrad_workspace_bytes(512, 250) == 8 * 252 * 4
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(mb=0), INV), (dict(mb=MB + 2), MISAL), (dict(G=0), INV), (dict(G=1025), INV), (dict(sum_m=0), INV),
     (dict(sum_m=300), INV), (dict(K=100), INV), (dict(epi=8), INV), (dict(epi=4), INV), (dict(epi=1), INV),

@@ -724,6 +724,49 @@ def test_mgrouped_dgrad(accum, pow2, epi, dxdt):
         check_f32(g[:3], db[:3], dbm[:3], "per-expert bias grad", chain_colsum(K, M, epi_chain(epi)))
 
 
+@pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
+@pytest.mark.parametrize("epi", [te.TE_EPI_BGRAD, te.TE_EPI_DGELU | te.TE_EPI_BGRAD])
+def test_mgrouped_dgrad_deterministic(accum, pow2, epi):
+    """The atomic-free per-expert bias gradient: within the oracle bound, bit-identical from run to
+    run (with the workspace refilled with garbage in between), an expert with no block gets zeros,
+    and dx is the atomic call's dx bit for bit."""
+    blocks = np.array([2, 0, -1, 2, 0, 5], np.int32)     # expert 1 has no block; -1 and 5 (>= G) are skipped
+    G, N, K = 4, 200, 256
+    M = 256 * len(blocks)
+    qa, sa = operand(130, M, K, E5, 1e-3, pow2)
+    ws = [operand(131 + e, N, K, E4, 0.02, pow2) for e in range(G)]
+    qw, sw = np.stack([w[0] for w in ws]), np.stack([w[1] for w in ws])
+    zb = W.normal_bf16(np.random.SeedSequence(140), (M, N), 1.28)
+    has_dg = bool(epi & te.TE_EPI_DGELU)
+    D, Dm, db, dbm = oracle.mgrouped_dgrad(qa, sa, oracle.E5M2, qw, sw, oracle.E4M3, blocks, zb if has_dg else None)
+    zpad = np.zeros((M, N + 8), np.uint16)
+    zpad[:, :N] = zb
+    Z = bf16_dev(zpad)[:, :N] if has_dg else None
+    A, SA = dev(qa), sdev(sa)
+    wq, wsd = w_dev(qw, sw)
+    mb = torch.from_numpy(blocks).cuda()
+    work = torch.empty((te.load_library().te_fp8_dgrad_bgrad_workspace_bytes(M, N),), dtype=torch.uint8,
+                       device="cuda")
+    runs = []
+    for r in range(2):
+        work.fill_(0xFF if r else 0x7F)          # NaN / large garbage: unwritten rows must not be read
+        bg = torch.full((G * N,), 3.0, dtype=torch.float32, device="cuda")
+        dx = te.te_fp8_mgrouped_gemm_dgrad_deterministic(A, SA, E5, wq, wsd, E4, mb, bg, epilogue=epi, preact=Z,
+                                                         workspace=work, accum=accum)
+        torch.cuda.synchronize()
+        runs.append((host(bg), host(dx)))
+    assert torch.equal(runs[0][0].view(torch.int32), runs[1][0].view(torch.int32)), "bias gradient not reproducible"
+    g = runs[0][0].numpy().reshape(G, N)
+    assert (g[1] == 0).all() and (g[3] == 0).all(), "an expert without blocks must get a zero bias gradient"
+    check_f32(g[[0, 2]], db[[0, 2]], dbm[[0, 2]], "per-expert bias grad (deterministic)",
+              chain_colsum(K, M, epi_chain(epi)))
+    bga = torch.empty((G * N,), dtype=torch.float32, device="cuda")
+    dxa = te.te_fp8_mgrouped_gemm_dgrad(A, SA, E5, wq, wsd, E4, mb, epilogue=epi, preact=Z, bias_grad=bga,
+                                        accum=accum)
+    live = torch.from_numpy(np.repeat((blocks >= 0) & (blocks < G), 256))
+    assert torch.equal(host(dxa)[live].view(torch.int16), runs[0][1][live].view(torch.int16))
+
+
 def test_mgrouped_same_expert_equals_dense():
     """With every block on one expert the call is the dense forward GEMM, bit for bit."""
     blocks = np.zeros(4, np.int32)
