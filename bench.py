@@ -353,15 +353,57 @@ def group_mgrouped(te, torch, g):
     sw = sw.view(K // 128, G, N).permute(1, 0, 2).contiguous()
     blocks = torch.arange(T // 256, device="cuda", dtype=torch.int32) // ((T // 256) // G)
     yg = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    # the experts' data gradient at the hidden layer: dZ [T, 7168] = dO [T, 4096] W2[e]^T, dGELU on the
+    # saved pre-activation, per-expert bias gradients (atomic and deterministic)
+    E5 = te.TE_DTYPE_E5M2
+    F = K
+    qdo, sdo = te.te_cast_fp8_per_token(_randn(torch, g, (T, N), 1e-3, 16), E5)
+    qw2, sw2 = te.te_cast_fp8_per_token(_randn(torch, g, (G * F, N), 0.02, 17), te.TE_DTYPE_E4M3)
+    qw2 = qw2.view(G, F, N)
+    sw2 = sw2.view(N // 128, G, F).permute(1, 0, 2).contiguous()
+    zg = _randn(torch, g, (T, F), 1.28, 18)
+    dzg = torch.empty((T, F), dtype=torch.bfloat16, device="cuda")
+    bgg = torch.empty((G * F,), dtype=torch.float32, device="cuda")
+    wsg = torch.empty((te.load_library().te_fp8_dgrad_bgrad_workspace_bytes(T, F),), dtype=torch.uint8, device="cuda")
+    DB = te.TE_EPI_DGELU | te.TE_EPI_BGRAD
+    fd = 2.0 * T * F * N
     return {
         "mgrouped_fwd_bias_gelu_full_8x1024x4096x7168": Case(
             lambda: te.te_fp8_mgrouped_gemm_fwd(qx, sx, E4, qw, sw, E4, blocks, bias=bgs,
                                                 epilogue=te.TE_EPI_BIAS | te.TE_EPI_GELU, y=yg,
                                                 accum=te.TE_ACCUM_FULL_FP32), 2.0 * T * N * K),
-    }, []
+        "mgrouped_dgrad_dgelu_bgrad_full_8x1024x7168x4096": Case(
+            lambda: te.te_fp8_mgrouped_gemm_dgrad(qdo, sdo, E5, qw2, sw2, te.TE_DTYPE_E4M3, blocks, epilogue=DB,
+                                                  preact=zg, bias_grad=bgg, dx=dzg, accum=te.TE_ACCUM_FULL_FP32), fd),
+        "mgrouped_dgrad_dgelu_bgrad_deterministic_full_8x1024x7168x4096": Case(
+            lambda: te.te_fp8_mgrouped_gemm_dgrad_deterministic(qdo, sdo, E5, qw2, sw2, te.TE_DTYPE_E4M3, blocks, bgg,
+                                                                epilogue=DB, preact=zg, workspace=wsg, dx=dzg,
+                                                                accum=te.TE_ACCUM_FULL_FP32), fd),
+    }, [("mgrouped_dgrad_dgelu_bgrad_full_8x1024x7168x4096",
+         "mgrouped_dgrad_dgelu_bgrad_deterministic_full_8x1024x7168x4096")]
 
 
-GROUPS = [group_tiny, group_dense_wgrad, group_fprop, group_dgrad, group_kgrouped, group_mgrouped]
+def group_modules(te, torch, g):
+    """One training step (forward + backward) of the library's MLP block, fc1 4096 -> 14336, GELU,
+    fc2 14336 -> 4096, on 8192 tokens: every GEMM, cast and epilogue is a library call (the modules
+    add autograd's bookkeeping); the fp8 weights come from the cache."""
+    from fp8_linear_layer_amd import linear as lin
+    T, D, H = 8192, 4096, 14336
+    gen = torch.Generator(device="cuda").manual_seed(19)
+    m = lin.Fp8Mlp(D, H, D, generator=gen)
+    x = _randn(torch, g, (T, D), 1.0, 20).requires_grad_(True)
+    dy = _randn(torch, g, (T, D), 1e-3, 21)
+
+    def step():
+        m(x).backward(dy)
+        x.grad = None
+        m.b1.grad = None
+        m.b2.grad = None
+    return {"mlp_step_8192x4096x14336": Case(step, 6 * 2.0 * T * D * H,
+                                              note="forward (2 GEMMs) + backward (4 GEMMs) + casts")}, []
+
+
+GROUPS = [group_tiny, group_dense_wgrad, group_fprop, group_dgrad, group_kgrouped, group_mgrouped, group_modules]
 # the cases of each group (so that --case sets up only its own group's inputs)
 GROUP_CASES = {
     group_tiny: ("tiny_fprop_bias_gelu_256x256x512", "tiny_wgrad_256x256x512"),
@@ -376,7 +418,9 @@ GROUP_CASES = {
                   "dgrad_dz_dgelu_bgrad_quant_e5m2_full", "dgrad_dz_dgelu_bgrad_quant_both_e5m2_full",
                   "cast_and_transpose_e5m2_8192x14336"),
     group_kgrouped: ("kgrouped_wgrad_full", "kgrouped_wgrad_device_sizes_full"),
-    group_mgrouped: ("mgrouped_fwd_bias_gelu_full_8x1024x4096x7168",),
+    group_mgrouped: ("mgrouped_fwd_bias_gelu_full_8x1024x4096x7168", "mgrouped_dgrad_dgelu_bgrad_full_8x1024x7168x4096",
+                     "mgrouped_dgrad_dgelu_bgrad_deterministic_full_8x1024x7168x4096"),
+    group_modules: ("mlp_step_8192x4096x14336",),
 }
 
 
