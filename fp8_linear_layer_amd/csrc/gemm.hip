@@ -1452,21 +1452,27 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p, int
 }
 
 // ---------------------------------------------------------------------------
-// Wave-per-workgroup path, for GEMMs with few 256 x 256 tiles (the persistent
-// kernel would leave most compute units idle: one 256 x 256 x 512 product
-// runs on one of 256).  Each workgroup is a single wave computing one wave
-// tile (64 rows x 128 columns) of the same tile grid, with three LDS stages
-// of its own, so the eight wave tiles of a tile run on up to eight compute
-// units.  Fragments, promotion order, matrix-core chain and epilogue are the
-// persistent kernel's, with the wave's place in its tile, so both paths give
-// the same bits wherever the chain decision agrees (the persistent kernel
-// takes it per 256 x 256 tile, this path per wave tile).
+// Wave-tile path, for GEMMs with few 256 x 256 tiles (the persistent kernel
+// would leave most compute units idle: one 256 x 256 x 512 product runs on
+// one of 256).  Each workgroup computes one wave tile (64 rows x 128 columns)
+// of the same tile grid, so the eight wave tiles of a tile run on up to eight
+// compute units, with four waves, one per SIMD: wave w runs the products of
+// column groups 2w and 2w + 1 of every block from three LDS stages the four
+// share, and after the K loop the four hand their accumulators to wave 0
+// through LDS, which runs the epilogue with the wave tile's place in its
+// tile.  Fragments, promotion order, matrix-core chain and epilogue are the
+// persistent kernel's, so both paths give the same bits wherever the chain
+// decision agrees (the persistent kernel takes it per 256 x 256 tile, this
+// path per wave tile).
 constexpr int kVA = kWM * kBK;                         // 8 KiB: the wave tile's A rows of one block
 constexpr int kVB = kWN * kBK;                         // 16 KiB: its B rows
 constexpr int kVScale = kVA + kVB;                     // sA run (1 KiB copy, 64 floats used), then sB's
 constexpr int kVStage = kVA + kVB + 2 * 1024;          // 26 KiB
 constexpr int kVStages = 3;
 constexpr int kVCopies = kVA / 1024 + kVB / 1024 + 2;  // copies per block: 8 A + 16 B + 2 scale runs
+constexpr int kVWaves = 4;                             // waves of a workgroup (one per SIMD)
+constexpr int kVJ = kTN / kVWaves;                     // column groups per wave (2)
+constexpr int kVThreads = 64 * kVWaves;
 
 struct WaveSrc {
     __amdgpu_buffer_rsrc_t a, b;
@@ -1475,31 +1481,38 @@ struct WaveSrc {
     int sa_bytes, sb_bytes;
 };
 
-// One block's copies into a stage (empty ranges when `live` is false: the
-// count of copies per block stays fixed, which the waits rely on).
-__device__ __forceinline__ void wave_load_block(const GemmArgs& p, const WaveSrc& s, uint8_t* stage, int kb, bool live,
-                                                int lane)
+// Wave w's share of one block's copies into a stage: copies w, w + 4, ...
+// (7 for waves 0 and 1, 6 for waves 2 and 3; empty ranges when `live` is
+// false, so each wave's count per block stays fixed, which the waits rely on).
+__device__ __forceinline__ void wave_load_part(const GemmArgs& p, const WaveSrc& s, uint8_t* stage, int kb, bool live,
+                                               int w, int lane)
 {
     const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, 0x00020000);
     const __amdgpu_buffer_rsrc_t ra = live ? s.a : none, rb = live ? s.b : none;
     const int kcol = live ? kb * kBK : 0;
-#pragma unroll
-    for (int t = 0; t < kVA / 1024; ++t) {
-        const int ci = t * 64 + lane, row = ci >> 3, chunk = (ci & 7) ^ ((row >> 1) & 7);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + t * 1024), 16,
-                                                 (uint32_t)(row * p.lda + chunk * 16), kcol, 0, 0);
-    }
-#pragma unroll
-    for (int t = 0; t < kVB / 1024; ++t) {
-        const int ci = t * 64 + lane, row = ci >> 3, chunk = (ci & 7) ^ ((row >> 1) & 7);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + kVA + t * 1024), 16,
-                                                 (uint32_t)(row * p.ldb + chunk * 16), kcol, 0, 0);
-    }
     const int64_t kbl = live ? kb : 0;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(s.sa + kbl * p.lsa, live ? s.sa_bytes : 0),
-                                             (lds_ptr_t)(stage + kVScale), 16, (uint32_t)(lane * 16), 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(s.sb + kbl * p.lsb, live ? s.sb_bytes : 0),
-                                             (lds_ptr_t)(stage + kVScale + 1024), 16, (uint32_t)(lane * 16), 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < (kVCopies + kVWaves - 1) / kVWaves; ++u) {
+        const int t = w + kVWaves * u;
+        if (t < kVA / 1024) {
+            const int ci = t * 64 + lane, row = ci >> 3, chunk = (ci & 7) ^ ((row >> 1) & 7);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + t * 1024), 16,
+                                                     (uint32_t)(row * p.lda + chunk * 16), kcol, 0, 0);
+        } else if (t < (kVA + kVB) / 1024) {
+            const int tb = t - kVA / 1024;
+            const int ci = tb * 64 + lane, row = ci >> 3, chunk = (ci & 7) ^ ((row >> 1) & 7);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + kVA + tb * 1024), 16,
+                                                     (uint32_t)(row * p.ldb + chunk * 16), kcol, 0, 0);
+        } else if (t == (kVA + kVB) / 1024) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(s.sa + kbl * p.lsa, live ? s.sa_bytes : 0),
+                                                     (lds_ptr_t)(stage + kVScale), 16, (uint32_t)(lane * 16), 0, 0,
+                                                     0);
+        } else if (t == (kVA + kVB) / 1024 + 1) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(s.sb + kbl * p.lsb, live ? s.sb_bytes : 0),
+                                                     (lds_ptr_t)(stage + kVScale + 1024), 16, (uint32_t)(lane * 16),
+                                                     0, 0, 0);
+        }
+    }
 }
 
 // Every scale of the wave tile's rows and columns over the contraction range
@@ -1519,21 +1532,26 @@ __device__ __forceinline__ bool wave_scales_pow2(const GemmArgs& p, int64_t m0, 
     return __builtin_amdgcn_ballot_w64(!ok) == 0;
 }
 
-// One block from stage `st`: its fragments and scales, the 32 products
-// (promoted, or chained on power-of-two scales), then the stage is refilled
-// with block kb_refill (an empty copy when it is past the range).
 struct WaveLane {
     int a_lo, a_hi, b_lo, b_hi;   // fragment offsets in a stage (row group i / column group j: + 2048 each)
     int r16, q4;
 };
 
+// One block from stage `st`: wait for this wave's copies of it, meet the other
+// waves (everyone's copies have landed and everyone is done with the stage of
+// the block before, `nx`), refill `nx` with block kb_refill, then this wave's
+// products of the block (its two column groups; promoted, or chained on
+// power-of-two scales).
 template <bool kChain, int kFmtA, int kFmtB>
-__device__ __forceinline__ void wave_block(const GemmArgs& p, const WaveSrc& s, uint8_t* st, v4f (&acc)[kTM][kTN],
-                                           const WaveLane& o, int kb_refill, bool refill, int lane)
+__device__ __forceinline__ void wave_block(const GemmArgs& p, const WaveSrc& s, uint8_t* st, uint8_t* nx,
+                                           v4f (&acc)[kTM][kVJ], const WaveLane& o, int w, int kb_refill, bool refill,
+                                           int lane)
 {
-    // (the copies into this stage were issued two blocks of copies ago; the
-    // compiler derives the same wait from the stages' separate alias scopes)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kVCopies) : "memory");
+    // (the next block's copies, issued after this block's, may stay in flight)
+    if (w < 2) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");
+    wave_load_part(p, s, nx, kb_refill, refill, w, lane);
     v8i ac[kTM];
     float sa[kTM];
     int ea[kTM];
@@ -1545,55 +1563,56 @@ __device__ __forceinline__ void wave_block(const GemmArgs& p, const WaveSrc& s, 
         ea[i] = e8m0(bits);
     }
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) {
+    for (int jj = 0; jj < kVJ; ++jj) {
+        const int j = w * kVJ + jj;
         const v8i bq = lds_frag(st, o.b_lo, o.b_hi, j * 2048);
         if (kChain) {
             const int eb = e8m0(lds_u32(st + kVScale + 1024 + (j * 16 + o.r16) * 4));
 #pragma unroll
             for (int i = 0; i < kTM; ++i)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq, ac[i], acc[i][j], kFmtB, kFmtA, 0, eb,
-                                                                             0, ea[i]);
+                acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq, ac[i], acc[i][jj], kFmtB, kFmtA, 0,
+                                                                              eb, 0, ea[i]);
         } else {
             const float4 sbq = lds_f32x4(st + kVScale + 1024 + (j * 16 + o.q4 * 4) * 4);
 #pragma unroll
             for (int i = 0; i < kTM; ++i) {
                 const v4f P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq, ac[i], v4f{0.f, 0.f, 0.f, 0.f},
                                                                                kFmtB, kFmtA, 0, 0, 0, 0);
-                promote(acc[i][j], P, sa[i], sbq);
+                promote(acc[i][jj], P, sa[i], sbq);
             }
         }
     }
-    // every read of this stage has returned: refill it
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    wave_load_block(p, s, st, kb_refill, refill, lane);
 }
 
 // The K loop over three stages, unrolled by three so that each stage is its
 // own restrict-qualified pointer: reads of one stage then wait only for the
-// copies into that stage, not for the two blocks in flight behind them.
+// copies into that stage, not for the block in flight behind them.  Blocks 0
+// and 1 are in stages 0 and 1 on entry.
 template <bool kChain, int kFmtA, int kFmtB>
 __device__ __forceinline__ void wave_main_loop(const GemmArgs& p, const WaveSrc& s, uint8_t* __restrict__ s0,
                                                uint8_t* __restrict__ s1, uint8_t* __restrict__ s2,
-                                               v4f (&acc)[kTM][kTN], const WaveLane& o, int kb0, int nkb, int lane)
+                                               v4f (&acc)[kTM][kVJ], const WaveLane& o, int w, int kb0, int nkb,
+                                               int lane)
 {
     int it = 0;
     for (; it + 3 <= nkb; it += 3) {
-        wave_block<kChain, kFmtA, kFmtB>(p, s, s0, acc, o, kb0 + it + 3, it + 3 < nkb, lane);
-        wave_block<kChain, kFmtA, kFmtB>(p, s, s1, acc, o, kb0 + it + 4, it + 4 < nkb, lane);
-        wave_block<kChain, kFmtA, kFmtB>(p, s, s2, acc, o, kb0 + it + 5, it + 5 < nkb, lane);
+        wave_block<kChain, kFmtA, kFmtB>(p, s, s0, s2, acc, o, w, kb0 + it + 2, it + 2 < nkb, lane);
+        wave_block<kChain, kFmtA, kFmtB>(p, s, s1, s0, acc, o, w, kb0 + it + 3, it + 3 < nkb, lane);
+        wave_block<kChain, kFmtA, kFmtB>(p, s, s2, s1, acc, o, w, kb0 + it + 4, it + 4 < nkb, lane);
     }
-    if (it < nkb) wave_block<kChain, kFmtA, kFmtB>(p, s, s0, acc, o, 0, false, lane);
-    if (it + 1 < nkb) wave_block<kChain, kFmtA, kFmtB>(p, s, s1, acc, o, 0, false, lane);
+    if (it < nkb) wave_block<kChain, kFmtA, kFmtB>(p, s, s0, s2, acc, o, w, kb0 + it + 2, it + 2 < nkb, lane);
+    if (it + 1 < nkb) wave_block<kChain, kFmtA, kFmtB>(p, s, s1, s0, acc, o, w, kb0 + it + 3, it + 3 < nkb, lane);
     // the trailing copies (empty ranges) still write LDS: let them land
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <int kFmtA, int kFmtB, bool kFast, int kEpi, int kQuant>
-__global__ __launch_bounds__(64) void gemm_nt_wave_kernel(const GemmArgs p)
+__global__ __launch_bounds__(kVThreads) void gemm_nt_wave_kernel(const GemmArgs p)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kVStages * kVStage];
-    const int lane = threadIdx.x;
-    const int wave = (int)(blockIdx.x % kWaves);          // the wave's place in its 256 x 256 tile
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = (int)(blockIdx.x % kWaves);          // the wave tile's place in its 256 x 256 tile
     const TileCtx c = tile_ctx(p, (int64_t)(blockIdx.x / kWaves));
     const int wm = wave / kWavesN, wn = wave % kWavesN;
     const int64_t m0 = c.m0 + wm * kWM, n0 = c.n0 + wn * kWN;
@@ -1601,7 +1620,7 @@ __global__ __launch_bounds__(64) void gemm_nt_wave_kernel(const GemmArgs p)
     if (m0 >= p.M) {
         // no rows: only the deterministic bias gradient's workspace row of this
         // wave place is due (zero, as the persistent kernel's wave writes it)
-        if (kEpi == (int)Epi::Dgrad && (p.flags & TE_EPI_BGRAD) && p.bgrad_ws) {
+        if (w == 0 && kEpi == (int)Epi::Dgrad && (p.flags & TE_EPI_BGRAD) && p.bgrad_ws) {
             float* row = p.bgrad_ws + ((c.m0 / kBM) * kWavesM + wm) * p.bgrad_ws_ld;
             for (int n = lane; n < kWN; n += 64)
                 if (n0 + n < p.N) row[n0 + n] = 0.0f;
@@ -1629,18 +1648,48 @@ __global__ __launch_bounds__(64) void gemm_nt_wave_kernel(const GemmArgs p)
     // the restrict scopes the loop's waits rely on)
     int s0_off = 0, s1_off = kVStage, s2_off = 2 * kVStage;
     asm volatile("" : "+s"(s0_off), "+s"(s1_off), "+s"(s2_off));
-#pragma unroll
-    for (int b = 0; b < kVStages; ++b) wave_load_block(p, s, smem + b * kVStage, kb0 + b, b < nkb, lane);
+    wave_load_part(p, s, smem, kb0, 0 < nkb, w, lane);
+    wave_load_part(p, s, smem + kVStage, kb0 + 1, 1 < nkb, w, lane);
 
+    v4f part[kTM][kVJ];
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < kVJ; ++jj) part[i][jj] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (chain)
+        wave_main_loop<true, kFmtA, kFmtB>(p, s, smem + s0_off, smem + s1_off, smem + s2_off, part, o, w, kb0, nkb,
+                                           lane);
+    else
+        wave_main_loop<false, kFmtA, kFmtB>(p, s, smem + s0_off, smem + s1_off, smem + s2_off, part, o, w, kb0, nkb,
+                                            lane);
+
+    // the four waves' column groups meet in wave 0 (value r of wave w at
+    // [(w * 32 + r) * 64 + lane]: one dword per lane, no bank conflicts)
+    float* G = reinterpret_cast<float*>(smem);
+    __syncthreads();   // every wave is done reading the stages
+    if (w != 0) {
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < kVJ; ++jj)
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) G[(w * 32 + (i * kVJ + jj) * 4 + cc) * 64 + lane] = part[i][jj][cc];
+    }
+    __syncthreads();
+    if (w != 0) return;
     v4f acc[kTM][kTN];
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
-        for (int j = 0; j < kTN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-    if (chain)
-        wave_main_loop<true, kFmtA, kFmtB>(p, s, smem + s0_off, smem + s1_off, smem + s2_off, acc, o, kb0, nkb, lane);
-    else
-        wave_main_loop<false, kFmtA, kFmtB>(p, s, smem + s0_off, smem + s1_off, smem + s2_off, acc, o, kb0, nkb, lane);
+        for (int j = 0; j < kTN; ++j) {
+            const int ww = j / kVJ, jj = j % kVJ;
+            if (ww == 0) {
+                acc[i][j] = part[i][jj];
+            } else {
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) acc[i][j][cc] = G[(ww * 32 + (i * kVJ + jj) * 4 + cc) * 64 + lane];
+            }
+        }
     epilogue<kEpi, false, kQuant>(p, acc, c.m0, c.n0, c.out_off, p.bias, p.bias_grad, smem, wave, lane);
 }
 
@@ -1713,14 +1762,14 @@ hipError_t launch_wave_epi(const GemmArgs& a, dim3 grid, hipStream_t s)
 {
     const bool q = a.q_out != nullptr;
     switch (a.epi) {
-    case Epi::Wgrad: gemm_nt_wave_kernel<kFmtA, kFmtB, kFast, (int)Epi::Wgrad, 0><<<grid, 64, 0, s>>>(a); break;
+    case Epi::Wgrad: gemm_nt_wave_kernel<kFmtA, kFmtB, kFast, (int)Epi::Wgrad, 0><<<grid, kVThreads, 0, s>>>(a); break;
     case Epi::Fwd:
-        if (q) gemm_nt_wave_kernel<kFmtA, kFmtB, kFast, (int)Epi::Fwd, 1><<<grid, 64, 0, s>>>(a);
-        else gemm_nt_wave_kernel<kFmtA, kFmtB, kFast, (int)Epi::Fwd, 0><<<grid, 64, 0, s>>>(a);
+        if (q) gemm_nt_wave_kernel<kFmtA, kFmtB, kFast, (int)Epi::Fwd, 1><<<grid, kVThreads, 0, s>>>(a);
+        else gemm_nt_wave_kernel<kFmtA, kFmtB, kFast, (int)Epi::Fwd, 0><<<grid, kVThreads, 0, s>>>(a);
         break;
     case Epi::Dgrad:
-        if (q) gemm_nt_wave_kernel<kFmtA, kFmtB, kFast, (int)Epi::Dgrad, 1><<<grid, 64, 0, s>>>(a);
-        else gemm_nt_wave_kernel<kFmtA, kFmtB, kFast, (int)Epi::Dgrad, 0><<<grid, 64, 0, s>>>(a);
+        if (q) gemm_nt_wave_kernel<kFmtA, kFmtB, kFast, (int)Epi::Dgrad, 1><<<grid, kVThreads, 0, s>>>(a);
+        else gemm_nt_wave_kernel<kFmtA, kFmtB, kFast, (int)Epi::Dgrad, 0><<<grid, kVThreads, 0, s>>>(a);
         break;
     }
     return hipGetLastError();
@@ -1818,18 +1867,16 @@ int device_cus()
     return cached[dev];
 }
 
-// Which kernel takes a dense product: the wave-per-workgroup one when the
-// 256 x 256 tiles are too few to give every compute unit one (each of their
-// eight wave tiles then gets one) and the contraction is short, the
-// persistent one otherwise.  Measured on 256 x 256 and 512 x 512 outputs (one
-// and four tiles): the wave path's fixed cost is ~5 us lower, but one wave
-// alone on its compute unit takes ~1.7 us per 128-deep block against ~1.3 us
-// for eight waves sharing one, so past ~11 blocks the persistent kernel is
-// ahead; the cut is at 8.  The environment variable TE_FP8_GEMM_PATH ("wave"
-// or "persistent") overrides the choice for the products the wave kernel
-// supports.
-constexpr int kWavePathMaxBlocks = 8;
-
+// Which kernel takes a dense product: the wave-tile one when the 256 x 256
+// tiles number at most a quarter of the compute units (its workgroups, one
+// per wave tile, then fill every CU at most twice over), the persistent one
+// otherwise.  Kernel trace, out += A B^T (FULL): 1 and 4 tiles, K = 512:
+// 14.0 vs 21.4-21.7 us; K = 2048: 21.7 vs 36.4-36.8 us; 32 tiles (1024 x
+// 2048), K = 4096: 37.3 vs 60.1 us; 64 tiles (2048 x 2048): 45.8 vs 61.9 us;
+// 128 tiles (2048 x 4096): 83.4 vs 64.5 us, where the persistent kernel's
+// eight waves per tile are ahead.  The environment variable TE_FP8_GEMM_PATH
+// ("wave" or "persistent") overrides the choice for the products the wave
+// kernel supports.
 bool use_wave_path(const GemmArgs& a, int64_t tiles, int cus)
 {
     const bool supported = a.num_groups == 1 && !a.group_k_dev && !a.m_block_group && !a.qt_out;
@@ -1837,7 +1884,7 @@ bool use_wave_path(const GemmArgs& a, int64_t tiles, int cus)
     const char* env = std::getenv("TE_FP8_GEMM_PATH");
     if (env && std::strcmp(env, "wave") == 0) return true;
     if (env && std::strcmp(env, "persistent") == 0) return false;
-    return tiles * kWaves <= cus && a.groups[0].kb_len <= kWavePathMaxBlocks;
+    return tiles * 4 <= cus;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream, LaunchInfo* info)
@@ -1846,12 +1893,12 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream, LaunchInfo* info)
     const int cus = device_cus();
     const bool wave_path = use_wave_path(a, tiles, cus);
     // persistent: one workgroup per compute unit (the two stages fill most of its
-    // LDS); wave path: one single-wave workgroup per wave tile
+    // LDS); wave path: one four-wave workgroup per wave tile
     const int64_t blocks = wave_path ? tiles * kWaves : std::min<int64_t>(tiles, cus);
     if (info) {
         info->tile_m = wave_path ? kWM : kBM;
         info->tile_n = wave_path ? kWN : kBN;
-        info->threads = wave_path ? 64 : kThreads;
+        info->threads = wave_path ? kVThreads : kThreads;
         info->grid = blocks;
     }
     if (blocks <= 0) return hipSuccess;
