@@ -123,3 +123,42 @@ def test_dgrad_paths_agree(monkeypatch, accum, pow2, M, N, K):
                                            dx_dtype=te.TE_DTYPE_F32, accum=accum)
         return [dx, bg]
     same_bits(*both(monkeypatch, run), "dgrad")
+
+
+def _random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.integers(1, 700))
+        N = int(rng.integers(1, 700))
+        K = 128 * int(rng.integers(1, 9))
+        out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", _random_shapes(16, 2026))
+def test_random_shapes_paths_agree(monkeypatch, M, N, K):
+    """Seeded random ragged shapes (M, N in [1, 700), K a multiple of 128 up to 1024): the
+    wave-tile and persistent kernels agree bit for bit on the weight gradient under FULL and FAST
+    (power-of-two scales), and on the forward with bias + GELU."""
+    for accum, pow2 in ((FULL, False), (FAST, True)):
+        A, SA = operand(M * 7 + K, M, K, oracle.E4M3, 1.0, pow2)
+        B, SB = operand(N * 11 + K, N, K, oracle.E4M3, 1.0, pow2)
+        out0 = dev(W.normal_f32(np.random.SeedSequence(M + 3 * N), (M, N)))
+
+        def run_w():
+            out = padded(M, N, torch.float32)
+            out.copy_(out0)
+            te.te_fp8_wgrad_accum(A, SA, E4, B, SB, E4, out, accum)
+            return [out]
+        same_bits(*both(monkeypatch, run_w), f"wgrad {M}x{N}x{K}")
+    X, SX = operand(M + 5, M, K, oracle.E4M3, 1.0, False)
+    Wt, SW = operand(N + 6, N, K, oracle.E4M3, 0.02, False)
+    b = bf16_dev(W.normal_bf16(np.random.SeedSequence(N + 7), (N,), 0.1))
+
+    def run_f():
+        y = padded(M, N, torch.bfloat16)
+        te.te_fp8_gemm_fwd(X, SX, E4, Wt, SW, E4, bias=b, epilogue=te.TE_EPI_BIAS | te.TE_EPI_GELU, y=y,
+                           accum=FULL)
+        return [y]
+    same_bits(*both(monkeypatch, run_f), f"fwd {M}x{N}x{K}")
