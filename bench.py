@@ -235,6 +235,7 @@ def group_fprop(te, torch, g):
         "fprop_none_fast_pow2": Case(fw(px, psx, pw, psw, te.TE_EPI_NONE, FAST), f),
         "fprop_bias_gelu_fast_pow2": Case(fw(px, psx, pw, psw, BG, FAST), f),
         "fprop_bias_gelu_aux_fast_pow2": Case(fw(px, psx, pw, psw, BGA, FAST), f),
+        "fprop_bias_gelu_aux_full": Case(fw(qx, sx, qw, sw, BGA, FULL), f),
         "fprop_bias_gelu_quant_e4m3_fast_pow2": Case(
             lambda: te.te_fp8_gemm_fwd_quant(px, psx, E4, pw, psw, E4, bias=b, epilogue=BG, q=qy, q_scales=qys,
                                              accum=FAST), f),
@@ -253,6 +254,7 @@ def group_fprop(te, torch, g):
     pairs = [("fprop_none_full", "fprop_bias_gelu_full"), ("fprop_none_full", "fprop_none_fast"),
              ("fprop_none_fast_pow2", "fprop_bias_gelu_fast_pow2"),
              ("fprop_none_fast_pow2", "fprop_bias_gelu_aux_fast_pow2"),
+             ("fprop_bias_gelu_full", "fprop_bias_gelu_aux_full"),
              ("fprop_bias_gelu_fast_pow2", "fprop_bias_gelu_quant_e4m3_fast_pow2"),
              ("fprop_bias_gelu_aux_fast_pow2", "fprop_bias_gelu_aux_quant_both_e4m3_fast_pow2")]
     return cases, pairs
@@ -410,7 +412,8 @@ GROUP_CASES = {
     group_dense_wgrad: ("wgrad_full_7168x2112x4096", "wgrad_pow2_full_7168x2112x4096", "wgrad_pow2_fast_7168x2112x4096",
                         "cast_batch_e4m3_7168x4096_2112x4096", "wgrad_from_token_major_7168x2112x4096"),
     group_fprop: ("fprop_none_full", "fprop_bias_gelu_full", "fprop_none_fast", "fprop_none_fast_pow2",
-                  "fprop_bias_gelu_fast_pow2", "fprop_bias_gelu_aux_fast_pow2", "fprop_bias_gelu_quant_e4m3_fast_pow2",
+                  "fprop_bias_gelu_fast_pow2", "fprop_bias_gelu_aux_fast_pow2", "fprop_bias_gelu_aux_full",
+                  "fprop_bias_gelu_quant_e4m3_fast_pow2",
                   "fprop_bias_gelu_aux_quant_both_e4m3_fast_pow2", "cast_and_transpose_e4m3_8192x14336",
                   "cast_e4m3_8192x4096", "cast_and_transpose_e4m3_8192x4096"),
     group_dgrad: ("dgrad_dx_full", "dgrad_dx_fast", "cast_e5m2_8192x14336", "dgrad_dz_none_full",
