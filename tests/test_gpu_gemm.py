@@ -41,7 +41,7 @@ def epi_chain(epi):
 
 @pytest.fixture(params=["wave", "persistent"])
 def gemm_path(request, monkeypatch):
-    """Small products run on both GEMM kernels: the wave-per-workgroup one (the library's choice for
+    """Small products run on both GEMM kernels: the wave-tile one (the library's choice for
     products with few 256 x 256 tiles) and, forced through TE_FP8_GEMM_PATH, the persistent one."""
     monkeypatch.setenv("TE_FP8_GEMM_PATH", request.param)
     return request.param

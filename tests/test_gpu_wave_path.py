@@ -1,4 +1,4 @@
-"""The wave-per-workgroup GEMM path (products with few 256 x 256 tiles) against the persistent one.
+"""The wave-tile GEMM path (products with few 256 x 256 tiles) against the persistent one.
 
 Both kernels take the same fragments, promote in the same order (FULL) or chain through the matrix
 core (FAST on power-of-two scales) and share the epilogue, so on the same inputs every output that is
