@@ -103,3 +103,66 @@ def test_training_step_replays_match_eager():
                 assert torch.equal(v.view(torch.uint8) if v.dtype != torch.uint8 else v,
                                    eager[r][k].view(torch.uint8) if v.dtype != torch.uint8 else eager[r][k]), \
                     f"replay {r}: {k}"
+
+
+def test_quantising_and_deterministic_calls_replay_match_eager():
+    """The two-layout quantising forward, the deterministic dense and M-grouped data gradients
+    (workspace-based bias gradients) under capture: every replay bit-identical to the eager calls."""
+    T, IN, OUT, G = 512, 384, 640, 2
+    s = W.spawn(41, 6)
+    qx, sx = te.te_cast_fp8_per_token(bf16_dev(W.normal_bf16(s[0], (T, IN))), E4)
+    qw, sw = te.te_cast_fp8_per_token(bf16_dev(W.normal_bf16(s[1], (OUT, IN), 0.05)), E4)
+    b = bf16_dev(W.normal_bf16(s[2], (OUT,), 0.1))
+    qdy, sdy = te.te_cast_fp8_per_token(bf16_dev(W.normal_bf16(s[3], (T, OUT), 1e-2)), E5)
+    qwt, swt = te.te_cast_fp8_per_token(bf16_dev(W.normal_bf16(s[4], (G * IN, OUT), 0.05)), E4)
+    z = bf16_dev(W.normal_bf16(s[5], (T, IN), 1.28))
+    qwt_g = qwt.view(G, IN, OUT)
+    swt_g = swt.view(OUT // 128, G, IN).permute(1, 0, 2).contiguous()
+    blocks = torch.tensor([1, 0], dtype=torch.int32, device="cuda")
+    lib = te.load_library()
+    DB = te.TE_EPI_DGELU | te.TE_EPI_BGRAD
+
+    def buffers():
+        return {
+            "q": torch.empty((T, OUT), dtype=torch.uint8, device="cuda"),
+            "qs": torch.empty((OUT // 128, te.scale_ld(T)), dtype=torch.float32, device="cuda"),
+            "qt": torch.empty((OUT, T), dtype=torch.uint8, device="cuda"),
+            "qts": torch.empty((T // 128, te.scale_ld(OUT)), dtype=torch.float32, device="cuda"),
+            "dx": torch.empty((T, IN), dtype=torch.bfloat16, device="cuda"),
+            "db": torch.empty((IN,), dtype=torch.float32, device="cuda"),
+            "ws": torch.empty((lib.te_fp8_dgrad_bgrad_workspace_bytes(T, IN),), dtype=torch.uint8, device="cuda"),
+            "dxg": torch.empty((T, IN), dtype=torch.bfloat16, device="cuda"),
+            "dbg": torch.empty((G * IN,), dtype=torch.float32, device="cuda"),
+            "wsg": torch.empty((lib.te_fp8_dgrad_bgrad_workspace_bytes(T, IN),), dtype=torch.uint8, device="cuda"),
+        }
+
+    def step(o):
+        te.te_fp8_gemm_fwd_quant(qx, sx, E4, qw, sw, E4, bias=b, epilogue=te.TE_EPI_BIAS | te.TE_EPI_GELU,
+                                 q=o["q"], q_scales=o["qs"], transposed=True, qt=o["qt"], qt_scales=o["qts"],
+                                 accum=te.TE_ACCUM_FAST)
+        te.te_fp8_gemm_dgrad_deterministic(qdy, sdy, E5, qwt[:IN], swt[:, :te.scale_ld(IN)].contiguous(), E4,
+                                           o["db"], epilogue=DB, preact=z, workspace=o["ws"], dx=o["dx"])
+        te.te_fp8_mgrouped_gemm_dgrad_deterministic(qdy, sdy, E5, qwt_g, swt_g, E4, blocks, o["dbg"], epilogue=DB,
+                                                    preact=z, workspace=o["wsg"], dx=o["dxg"])
+
+    ref = buffers()
+    step(ref)
+    torch.cuda.synchronize()
+    g_out = buffers()
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step(g_out)
+    torch.cuda.synchronize()
+    for r in range(3):
+        for k in ("ws", "wsg"):
+            g_out[k].fill_(0xFF)                       # the workspaces start as garbage every time
+        graph.replay()
+        torch.cuda.synchronize()
+        _ = torch.ones(1000, device="cuda").sum().item()
+        for k in ("q", "qs", "qt", "qts", "dx", "db", "dxg", "dbg"):
+            v, e = g_out[k], ref[k]
+            if k in ("qs", "qts"):
+                rows = T if k == "qs" else OUT
+                v, e = v[:, :rows], e[:, :rows]
+            assert torch.equal(v.contiguous().view(torch.uint8), e.contiguous().view(torch.uint8)), f"replay {r}: {k}"
