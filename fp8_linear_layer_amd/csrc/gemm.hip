@@ -787,11 +787,13 @@ __device__ __forceinline__ void bias_grad_cols4(const GemmArgs& p, float (&t)[4]
 // holds eight consecutive columns of its row (group j + (q4 & 1), columns
 // 8 (q4 >> 1) .. +7).  Each bf16 load and store is then a 16-byte run, and
 // four lanes cover 64 contiguous bytes of a row.
-template <int kEpi, bool kFull, int kQuant>
-__device__ __forceinline__ void epilogue(const GemmArgs& p, v4f (&acc)[kTM][kTN], int64_t m0, int64_t n0,
+template <int kEpi, bool kFull, int kQuant, int kJ = kTN>
+__device__ __forceinline__ void epilogue(const GemmArgs& p, v4f (&acc)[kTM][kJ], int64_t m0, int64_t n0,
                                          int64_t out_off, const uint16_t* bias_v, float* bgrad_v, uint8_t* xs,
                                          int wave, int lane)
 {
+    static_assert(kJ % 2 == 0 && kJ <= kTN && (kQuant == 0 || kJ == kTN),
+                  "pairs of column groups; the quantising stores take a wave's whole 128 columns");
     const int wm = wave / kWavesN, wn = wave % kWavesN;
     // (the lane index is re-derived here so that its address arithmetic is not
     // hoisted out of the tile loop and held in registers across the K loop)
@@ -802,7 +804,26 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, v4f (&acc)[kTM][kTN]
     // before the first store.  Stores count in the same vmcnt as loads, so a
     // load issued after a store cannot be waited for without also waiting for
     // that store to complete.
-    if (kFull && kEpi == (int)Epi::Wgrad) {
+    if constexpr (kFull && kEpi == (int)Epi::Wgrad && kJ < kTN) {
+        // A few column groups (one wave's share of the wave-tile kernel): all
+        // loads in one batch, then the sums and the stores.
+        float* o = reinterpret_cast<float*>(p.out) + out_off + (m0 + wm * kWM + r16) * p.ld_out + n0 + wn * kWN + q4 * 4;
+        float4 c[kTM][kJ];
+#pragma unroll
+        for (int j = 0; j < kJ; ++j)
+#pragma unroll
+            for (int i = 0; i < kTM; ++i) c[i][j] = *reinterpret_cast<const float4*>(o + i * 16 * p.ld_out + j * 16);
+#pragma unroll
+        for (int j = 0; j < kJ; ++j)
+#pragma unroll
+            for (int i = 0; i < kTM; ++i) {
+                const v4f& a = acc[i][j];
+                float4& d = c[i][j];
+                d.x += a[0]; d.y += a[1]; d.z += a[2]; d.w += a[3];
+                *reinterpret_cast<float4*>(o + i * 16 * p.ld_out + j * 16) = d;
+            }
+        return;
+    } else if constexpr (kFull && kEpi == (int)Epi::Wgrad) {
         // Four quarters of the column groups, each read in one batch and
         // added.  A quarter's loads are issued before the previous quarter's
         // stores: the load/store counter retires in issue order, so waiting
@@ -848,7 +869,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, v4f (&acc)[kTM][kTN]
 
     if (kEpi == (int)Epi::Wgrad) {
 #pragma unroll
-        for (int j = 0; j < kTN; ++j) {
+        for (int j = 0; j < kJ; ++j) {
             const int64_t n = n0 + wn * kWN + j * 16 + q4 * 4;
             const bool full4 = kFull || n + 3 < p.N;
 #pragma unroll
@@ -881,20 +902,20 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, v4f (&acc)[kTM][kTN]
         // loads and stores the column sums skip those rows.
         const bool has_dgelu = (p.flags & TE_EPI_DGELU) != 0;
         const bool has_bgrad = (p.flags & TE_EPI_BGRAD) != 0;
-        float colsum[kTN][4];
+        float colsum[kJ][4];
 #pragma unroll
-        for (int j = 0; j < kTN; ++j) colsum[j][0] = colsum[j][1] = colsum[j][2] = colsum[j][3] = 0.f;
-        uint4 zq[kTN / 2][kTM];
+        for (int j = 0; j < kJ; ++j) colsum[j][0] = colsum[j][1] = colsum[j][2] = colsum[j][3] = 0.f;
+        uint4 zq[kJ / 2][kTM];
         if (kFull && has_dgelu && !kQuant) {
 #pragma unroll
-            for (int jp = 0; jp < kTN / 2; ++jp)
+            for (int jp = 0; jp < kJ / 2; ++jp)
 #pragma unroll
                 for (int i = 0; i < kTM; ++i)
                     zq[jp][i] = *reinterpret_cast<const uint4*>(
                         p.preact + (m0 + wm * kWM + i * 16 + r16) * p.ld_aux + n0 + wn * kWN + (2 * jp + (q4 & 1)) * 16 +
                         (q4 >> 1) * 8);
         }
-        if (kQuant == 2) {
+        if constexpr (kQuant == 2) {
             // Both casts of D.  Pass by pass, so that each keeps only the
             // accumulator and a few registers of its own live: dGELU in place,
             // the bias gradient summed from the final values (rows in the
@@ -946,7 +967,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, v4f (&acc)[kTM][kTN]
             if (p.q_out) quant_rowwise_acc<kFull>(p, acc, m0, n0, wave, lane);
             return;
         }
-        if (kQuant) {
+        if constexpr (kQuant != 0) {
             // Quantising store of D (after dGELU): as in the forward, the
             // wave's 128 columns are one 1x128 group of each row; the lane's
             // 32 values of a row are its 8 column groups x 4 columns.
@@ -1021,7 +1042,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, v4f (&acc)[kTM][kTN]
             }
         } else
 #pragma unroll
-        for (int jp = 0; jp < kTN / 2; ++jp) {
+        for (int jp = 0; jp < kJ / 2; ++jp) {
             const int j0 = 2 * jp, j1 = 2 * jp + 1;
             const int64_t np = n0 + wn * kWN + (j0 + (q4 & 1)) * 16 + (q4 >> 1) * 8;  // this lane's run
             const bool fullp = kFull || np + 7 < p.N;
@@ -1093,7 +1114,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, v4f (&acc)[kTM][kTN]
         }
         if (has_bgrad) {
 #pragma unroll
-            for (int j = 0; j < kTN; ++j)
+            for (int j = 0; j < kJ; ++j)
                 bias_grad_cols4<kFull>(p, colsum[j], n0 + wn * kWN + j * 16 + q4 * 4, m0, wm, r16, bgrad_v);
         }
         return;
@@ -1103,9 +1124,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, v4f (&acc)[kTM][kTN]
     const bool has_bias = (p.flags & TE_EPI_BIAS) != 0;
     const bool has_gelu = (p.flags & TE_EPI_GELU) != 0;
     const bool has_aux = (p.flags & TE_EPI_AUX_PREACT) != 0;
-    uint4 bw[kTN / 2];
+    uint4 bw[kJ / 2];
 
-    if (kQuant == 2) {
+    if constexpr (kQuant == 2) {
         // Both casts of the result.  The final values are formed in place in
         // the accumulator layout (bias, pre-activation store, GELU), then the
         // transposed and the row-wise casts read them; each pass keeps only
@@ -1154,7 +1175,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, v4f (&acc)[kTM][kTN]
         if (p.q_out) quant_rowwise_acc<kFull>(p, acc, m0, n0, wave, lane);
         return;
     }
-    if (kQuant) {
+    if constexpr (kQuant != 0) {
         // Quantising store.  A wave's 128 columns are one 1x128 group of each
         // of its rows (N is a multiple of 128, tile corners of 256), so a
         // group is wholly inside or outside the matrix, and a row's amax is
@@ -1221,11 +1242,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, v4f (&acc)[kTM][kTN]
 
     if (kFull && has_bias) {
 #pragma unroll
-        for (int jp = 0; jp < kTN / 2; ++jp)
+        for (int jp = 0; jp < kJ / 2; ++jp)
             bw[jp] = *reinterpret_cast<const uint4*>(bias_v + n0 + wn * kWN + (2 * jp + (q4 & 1)) * 16 + (q4 >> 1) * 8);
     }
 #pragma unroll
-    for (int jp = 0; jp < kTN / 2; ++jp) {
+    for (int jp = 0; jp < kJ / 2; ++jp) {
         const int64_t n = n0 + wn * kWN + (2 * jp + (q4 & 1)) * 16 + (q4 >> 1) * 8;
         const bool full8 = kFull || n + 7 < p.N;
         float bias[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -1458,8 +1479,11 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const GemmArgs p, int
 // of the same tile grid, so the eight wave tiles of a tile run on up to eight
 // compute units, with four waves, one per SIMD: wave w runs the products of
 // column groups 2w and 2w + 1 of every block from three LDS stages the four
-// share, and after the K loop the four hand their accumulators to wave 0
-// through LDS, which runs the epilogue with the wave tile's place in its
+// share.  After the K loop each wave runs the Linear-layer and weight-
+// gradient epilogues on its own two column groups (a pair, the unit those
+// epilogues work on); the quantising stores, whose 1 x 128 groups span the
+// wave tile's 128 columns, take the four waves' accumulators in wave 0
+// through LDS.  Either way the epilogue sees the wave tile's place in its
 // tile.  Fragments, promotion order, matrix-core chain and epilogue are the
 // persistent kernel's, so both paths give the same bits wherever the chain
 // decision agrees (the persistent kernel takes it per 256 x 256 tile, this
@@ -1663,6 +1687,15 @@ __global__ __launch_bounds__(kVThreads) void gemm_nt_wave_kernel(const GemmArgs 
         wave_main_loop<false, kFmtA, kFmtB>(p, s, smem + s0_off, smem + s1_off, smem + s2_off, part, o, w, kb0, nkb,
                                             lane);
 
+    if constexpr (kQuant == 0) {
+        // wave w's share: columns 32 w .. 32 w + 31 of the wave tile
+        const int64_t nw = c.n0 + w * (kVJ * 16);
+        if (m0 + kWM <= p.M && n0 + (w + 1) * (kVJ * 16) <= p.N)
+            epilogue<kEpi, true, 0, kVJ>(p, part, c.m0, nw, c.out_off, p.bias, p.bias_grad, smem, wave, lane);
+        else
+            epilogue<kEpi, false, 0, kVJ>(p, part, c.m0, nw, c.out_off, p.bias, p.bias_grad, smem, wave, lane);
+        return;
+    }
     // the four waves' column groups meet in wave 0 (value r of wave w at
     // [(w * 32 + r) * 64 + lane]: one dword per lane, no bank conflicts)
     float* G = reinterpret_cast<float*>(smem);
