@@ -1541,14 +1541,14 @@ __device__ __forceinline__ void wave_load_part(const GemmArgs& p, const WaveSrc&
 
 // Every scale of the wave tile's rows and columns over the contraction range
 // is a power of two (rows past M and columns past N do not count).
-__device__ __forceinline__ bool wave_scales_pow2(const GemmArgs& p, int64_t m0, int64_t n0, int kb0, int nkb,
-                                                 int lane)
+__device__ __forceinline__ bool wave_scales_pow2(const GemmArgs& p, const WaveSrc& s, int64_t m0, int64_t n0,
+                                                 int kb0, int nkb, int lane)
 {
     const int rows = (int)min((int64_t)kWM, p.M - m0), cols = (int)min((int64_t)kWN, p.N - n0);
     bool ok = true;
     for (int kb = kb0; kb < kb0 + nkb; ++kb) {
-        const float* a = p.sa + (int64_t)kb * p.lsa + m0;
-        const float* b = p.sb + (int64_t)kb * p.lsb + n0;
+        const float* a = s.sa + (int64_t)kb * p.lsa;
+        const float* b = s.sb + (int64_t)kb * p.lsb;
         if (lane < rows) ok = ok && is_pow2_scale(a[lane]);
         if (lane < cols) ok = ok && is_pow2_scale(b[lane]);
         if (lane + 64 < cols) ok = ok && is_pow2_scale(b[lane + 64]);
@@ -1640,7 +1640,8 @@ __global__ __launch_bounds__(kVThreads) void gemm_nt_wave_kernel(const GemmArgs 
     const TileCtx c = tile_ctx(p, (int64_t)(blockIdx.x / kWaves));
     const int wm = wave / kWavesN, wn = wave % kWavesN;
     const int64_t m0 = c.m0 + wm * kWM, n0 = c.n0 + wn * kWN;
-    if (n0 >= p.N) return;
+    // (an empty group's or a skipped block's tile leaves its output untouched)
+    if (n0 >= p.N || c.nkb == 0) return;
     if (m0 >= p.M) {
         // no rows: only the deterministic bias gradient's workspace row of this
         // wave place is due (zero, as the persistent kernel's wave writes it)
@@ -1653,13 +1654,13 @@ __global__ __launch_bounds__(kVThreads) void gemm_nt_wave_kernel(const GemmArgs 
     }
     WaveSrc s;
     s.a = make_rsrc(p.a + m0 * p.lda, min((int64_t)kWM, p.M - m0) * p.lda);
-    s.b = make_rsrc(p.b + n0 * p.ldb, min((int64_t)kWN, p.N - n0) * p.ldb);
+    s.b = make_rsrc(p.b + c.bgrp * p.b_group_stride + n0 * p.ldb, min((int64_t)kWN, p.N - n0) * p.ldb);
     s.sa = p.sa + m0;
-    s.sb = p.sb + n0;
+    s.sb = p.sb + c.bgrp * p.sb_group_stride + n0;
     s.sa_bytes = (int)(min((int64_t)kWM, p.lsa - m0) * 4);
     s.sb_bytes = (int)(min((int64_t)kWN, p.lsb - n0) * 4);
     const int kb0 = c.kb0, nkb = c.nkb;
-    const bool chain = kFast && wave_scales_pow2(p, m0, n0, kb0, nkb, lane);
+    const bool chain = kFast && wave_scales_pow2(p, s, m0, n0, kb0, nkb, lane);
 
     WaveLane o;
     o.r16 = lane & 15;
@@ -1687,13 +1688,15 @@ __global__ __launch_bounds__(kVThreads) void gemm_nt_wave_kernel(const GemmArgs 
         wave_main_loop<false, kFmtA, kFmtB>(p, s, smem + s0_off, smem + s1_off, smem + s2_off, part, o, w, kb0, nkb,
                                             lane);
 
+    const uint16_t* bias_v = p.bias + c.bgrp * p.bias_group_stride;
+    float* bgrad_v = p.bias_grad + c.bgrp * p.bias_group_stride;
     if constexpr (kQuant == 0) {
         // wave w's share: columns 32 w .. 32 w + 31 of the wave tile
         const int64_t nw = c.n0 + w * (kVJ * 16);
         if (m0 + kWM <= p.M && n0 + (w + 1) * (kVJ * 16) <= p.N)
-            epilogue<kEpi, true, 0, kVJ>(p, part, c.m0, nw, c.out_off, p.bias, p.bias_grad, smem, wave, lane);
+            epilogue<kEpi, true, 0, kVJ>(p, part, c.m0, nw, c.out_off, bias_v, bgrad_v, smem, wave, lane);
         else
-            epilogue<kEpi, false, 0, kVJ>(p, part, c.m0, nw, c.out_off, p.bias, p.bias_grad, smem, wave, lane);
+            epilogue<kEpi, false, 0, kVJ>(p, part, c.m0, nw, c.out_off, bias_v, bgrad_v, smem, wave, lane);
         return;
     }
     // the four waves' column groups meet in wave 0 (value r of wave w at
@@ -1723,7 +1726,7 @@ __global__ __launch_bounds__(kVThreads) void gemm_nt_wave_kernel(const GemmArgs 
                 for (int cc = 0; cc < 4; ++cc) acc[i][j][cc] = G[(ww * 32 + (i * kVJ + jj) * 4 + cc) * 64 + lane];
             }
         }
-    epilogue<kEpi, false, kQuant>(p, acc, c.m0, c.n0, c.out_off, p.bias, p.bias_grad, smem, wave, lane);
+    epilogue<kEpi, false, kQuant>(p, acc, c.m0, c.n0, c.out_off, bias_v, bgrad_v, smem, wave, lane);
 }
 
 #if TE_GEMM_PART < 0 || TE_GEMM_PART == 4
@@ -1912,7 +1915,7 @@ int device_cus()
 // kernel supports.
 bool use_wave_path(const GemmArgs& a, int64_t tiles, int cus)
 {
-    const bool supported = a.num_groups == 1 && !a.group_k_dev && !a.m_block_group && !a.qt_out;
+    const bool supported = !a.qt_out;
     if (!supported) return false;
     const char* env = std::getenv("TE_FP8_GEMM_PATH");
     if (env && std::strcmp(env, "wave") == 0) return true;

@@ -82,7 +82,7 @@
  *  Logging.  With the environment variable TE_FP8_LOG=1 every call prints one
  *            line to stderr (operation, sizes, formats, policy, epilogue,
  *            tile, grid).  Logging never changes results.
- *  Kernels.  A dense product whose 256 x 256 output tiles number at most a
+ *  Kernels.  A product whose 256 x 256 output tiles number at most a
  *            quarter of the device's compute units runs on a kernel that
  *            gives each 64 x 128 part of a tile a workgroup of its own (the
  *            others: one persistent workgroup per compute unit).  Both
@@ -90,8 +90,9 @@
  *            agrees (it is taken per output tile of the kernel that runs).
  *            The environment variable TE_FP8_GEMM_PATH=wave or =persistent
  *            forces one of the two for the products the first supports
- *            (dense, without the transposed quantising store); it is read on
- *            every call.
+ *            (every call but the quantising store of the transpose); it is
+ *            read on every call.  The tile count of a grouped call is that of
+ *            all its groups together.
  *
  * Sources: the Linear layer's forward and backward equations and the bias
  * length are those of the maintainer's explanation on "Replaced cublasLt calls

@@ -638,7 +638,7 @@ def w_dev(qw, sw):
 @pytest.mark.parametrize("epi,ydt", [(te.TE_EPI_NONE, te.TE_DTYPE_F32),
                                      (te.TE_EPI_BIAS | te.TE_EPI_GELU, te.TE_DTYPE_F32),
                                      (te.TE_EPI_BIAS | te.TE_EPI_GELU | te.TE_EPI_AUX_PREACT, te.TE_DTYPE_BF16)])
-def test_mgrouped_fwd(accum, pow2, epi, ydt):
+def test_mgrouped_fwd(accum, pow2, epi, ydt, gemm_path):
     """Blocks of 256 token rows, each with its expert (or -1: skipped, rows untouched); N ragged."""
     blocks = np.array([2, 0, -1, 2, 1], np.int32)
     G, N, K = 3, 200, 384
@@ -688,7 +688,7 @@ def test_mgrouped_dgrad_form_e5m2():
 @pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
 @pytest.mark.parametrize("epi,dxdt", [(te.TE_EPI_DGELU | te.TE_EPI_BGRAD, te.TE_DTYPE_F32),
                                       (te.TE_EPI_BGRAD, te.TE_DTYPE_BF16), (te.TE_EPI_DGELU, te.TE_DTYPE_BF16)])
-def test_mgrouped_dgrad(accum, pow2, epi, dxdt):
+def test_mgrouped_dgrad(accum, pow2, epi, dxdt, gemm_path):
     """Per-expert data gradient through GELU' with per-expert bias gradients: each live block is
     the dense dgrad epilogue with its expert's W^T; bias_grad[e] sums expert e's blocks (an expert
     with no block gets zeros); skipped blocks are not written."""
@@ -726,7 +726,7 @@ def test_mgrouped_dgrad(accum, pow2, epi, dxdt):
 
 @pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
 @pytest.mark.parametrize("epi", [te.TE_EPI_BGRAD, te.TE_EPI_DGELU | te.TE_EPI_BGRAD])
-def test_mgrouped_dgrad_deterministic(accum, pow2, epi):
+def test_mgrouped_dgrad_deterministic(accum, pow2, epi, gemm_path):
     """The atomic-free per-expert bias gradient: within the oracle bound, bit-identical from run to
     run (with the workspace refilled with garbage in between), an expert with no block gets zeros,
     and dx is the atomic call's dx bit for bit."""
@@ -767,7 +767,7 @@ def test_mgrouped_dgrad_deterministic(accum, pow2, epi):
     assert torch.equal(host(dxa)[live].view(torch.int16), runs[0][1][live].view(torch.int16))
 
 
-def test_mgrouped_same_expert_equals_dense():
+def test_mgrouped_same_expert_equals_dense(gemm_path):
     """With every block on one expert the call is the dense forward GEMM, bit for bit."""
     blocks = np.zeros(4, np.int32)
     qx, sx, qw, sw, b = mgrouped_case(90, 1, blocks, 384, 512)
@@ -782,7 +782,7 @@ def test_mgrouped_same_expert_equals_dense():
 
 # ------------------------------------------------------------------ K-grouped
 @pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
-def test_kgrouped_small(accum, pow2):
+def test_kgrouped_small(accum, pow2, gemm_path):
     gk = np.array([256, 0, 128, 384, 0, 128], np.int64)
     M, N, S = 200, 300, int(gk.sum())
     qa, sa = operand(31, M, S, E4, pow2=pow2)
@@ -799,7 +799,7 @@ def test_kgrouped_small(accum, pow2):
             check_f32(got[g], want[g], mag[g], f"group {g}", chain_gemm(gk[g], 1))
 
 
-def test_kgrouped_many_groups():
+def test_kgrouped_many_groups(gemm_path):
     """More groups than one launch carries: 300 groups of 128 or 0 columns."""
     rng = np.random.default_rng(4)
     gk = (rng.integers(0, 2, 300) * 128).astype(np.int64)
@@ -815,7 +815,7 @@ def test_kgrouped_many_groups():
 
 
 @pytest.mark.parametrize("accum,pow2", POLICIES, ids=PID)
-def test_kgrouped_device_sizes_matches_host_sizes(accum, pow2):
+def test_kgrouped_device_sizes_matches_host_sizes(accum, pow2, gemm_path):
     """Group sizes read from device memory: bit-identical to the host-sized call (the tiles do the
     same arithmetic; only their order differs), within tolerance of the oracle, empty groups untouched
     (including the sign of zero), and columns past the groups' sum unused."""

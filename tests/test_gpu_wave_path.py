@@ -5,7 +5,8 @@ core (FAST on power-of-two scales) and share the epilogue, so on the same inputs
 not summed with atomics must come out bit for bit the same; the oracle parity of each path is
 covered by test_gpu_gemm.py, which runs its small products on both.  Shapes: the tiny Linear
 (256 x 256 x 512, one tile), one wave tile exactly, one element past it in both dimensions, and a
-ragged product spanning two tiles each way.
+ragged product spanning two tiles each way; then the grouped calls (K-grouped with host and device
+sizes, M-grouped forward and deterministic data gradient).
 """
 import numpy as np
 import pytest
@@ -162,3 +163,84 @@ def test_random_shapes_paths_agree(monkeypatch, M, N, K):
                            accum=FULL)
         return [y]
     same_bits(*both(monkeypatch, run_f), f"fwd {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("accum,pow2", POL, ids=PID)
+@pytest.mark.parametrize("sizes", ["host", "device"])
+def test_kgrouped_paths_agree(monkeypatch, accum, pow2, sizes):
+    """K-grouped weight gradient (empty groups among them, one output holding -0.0 that an empty
+    group must leave as it is): each tile's group, contraction range and output come from the same
+    tile context on both kernels."""
+    gk = np.array([256, 0, 384, 128, 0, 512], np.int64)
+    M, N, S = 300, 200, int(gk.sum())
+    A, SA = operand(71, M, S, oracle.E4M3, 1.0, pow2)
+    B, SB = operand(72, N, S, oracle.E4M3, 1.0, pow2)
+    init = W.normal_f32(np.random.SeedSequence(73), (len(gk), M, N))
+    init[1, :5, :3] = -0.0
+    gkd = torch.from_numpy(gk).cuda()
+
+    def run():
+        out = dev(init)
+        if sizes == "host":
+            te.te_fp8_kgrouped_wgrad(A, SA, E4, B, SB, E4, gk.tolist(), out, accum)
+        else:
+            te.te_fp8_kgrouped_wgrad_device_sizes(A, SA, E4, B, SB, E4, gkd, out, accum)
+        return [out]
+    wave, pers = both(monkeypatch, run)
+    same_bits(wave, pers, "kgrouped")
+    assert np.array_equal(wave[0][1].numpy().view(np.uint32), init[1].view(np.uint32)), "empty group touched"
+
+
+def _mgrouped_operands(seed, G, blocks, N, K, fx, std, pow2):
+    M = 256 * len(blocks)
+    X, SX = operand(seed, M, K, fx, std, pow2)
+    ws = [W.normal_bf16(np.random.SeedSequence(seed + 1 + e), (N, K), 0.02) for e in range(G)]
+    cw = [oracle.cast_per_token(w, oracle.E4M3, pow2) for w in ws]
+    Wq = dev(np.stack([c[0] for c in cw]))
+    Ws = torch.stack([sdev(c[1]) for c in cw]).contiguous()
+    return M, X, SX, Wq, Ws
+
+
+@pytest.mark.parametrize("accum,pow2", POL, ids=PID)
+def test_mgrouped_fwd_paths_agree(monkeypatch, accum, pow2):
+    """M-grouped forward with bias + GELU + pre-activation store; blocks on three experts, one
+    skipped (-1) and one out of range (5): its rows stay untouched on both kernels."""
+    blocks = np.array([2, 0, -1, 2, 1, 5], np.int32)
+    G, N, K = 3, 296, 384      # (a bias row per expert must stay 16-byte aligned: N a multiple of 8)
+    M, X, SX, Wq, Ws = _mgrouped_operands(81, G, blocks, N, K, oracle.E4M3, 1.0, pow2)
+    b = bf16_dev(W.normal_bf16(np.random.SeedSequence(89), (G, N), 0.1))
+    mb = torch.from_numpy(blocks).cuda()
+    epi = te.TE_EPI_BIAS | te.TE_EPI_GELU | te.TE_EPI_AUX_PREACT
+
+    def run():
+        y = padded(M, N, torch.bfloat16, 7.0)
+        z = padded(M, N, torch.bfloat16, 5.0)
+        te.te_fp8_mgrouped_gemm_fwd(X, SX, E4, Wq, Ws, E4, mb, bias=b, epilogue=epi, y=y, preact=z, accum=accum)
+        return [y, z]
+    wave, pers = both(monkeypatch, run)
+    same_bits(wave, pers, "mgrouped fwd")
+    dead = torch.from_numpy(np.repeat((blocks < 0) | (blocks >= G), 256))
+    assert torch.all(wave[0][dead] == 7.0) and torch.all(wave[1][dead] == 5.0), "a skipped block was written"
+
+
+@pytest.mark.parametrize("accum,pow2", POL, ids=PID)
+def test_mgrouped_dgrad_deterministic_paths_agree(monkeypatch, accum, pow2):
+    """M-grouped data gradient through GELU' with the deterministic per-expert bias gradients: dX
+    and every expert's bias gradient (expert 1 has no block: zeros) agree bit for bit."""
+    blocks = np.array([2, 0, -1, 2, 0], np.int32)
+    G, N, K = 3, 264, 256
+    M, D, SD, Wq, Ws = _mgrouped_operands(91, G, blocks, N, K, oracle.E5M2, 1e-3, pow2)
+    z = padded(M, N, torch.bfloat16)
+    z.copy_(bf16_dev(W.normal_bf16(np.random.SeedSequence(99), (M, N), 1.28)))
+    mb = torch.from_numpy(blocks).cuda()
+    epi = te.TE_EPI_DGELU | te.TE_EPI_BGRAD
+
+    def run():
+        bg = torch.full((G * N,), 3.0, dtype=torch.float32, device="cuda")
+        dx = padded(M, N, torch.float32, 9.0)
+        te.te_fp8_mgrouped_gemm_dgrad_deterministic(D, SD, E5, Wq, Ws, E4, mb, bg, epilogue=epi, preact=z, dx=dx,
+                                                    dx_dtype=te.TE_DTYPE_F32, accum=accum)
+        return [dx, bg]
+    wave, pers = both(monkeypatch, run)
+    same_bits(wave, pers, "mgrouped dgrad")
+    assert torch.all(wave[1].reshape(G, N)[1] == 0), "an expert without blocks must get a zero bias gradient"
