@@ -12,12 +12,16 @@
 // reads the scales of one 128-deep block as one contiguous vector.
 //
 // Memory-bound: 2 bytes read and 1 byte + 1/32 byte written per element.  One
-// group is handled by 8 consecutive lanes, 16 elements (32 bytes) each.  A
-// workgroup covers a tile of 32 rows x 4 groups (512 columns): each wave takes
-// 8 rows, each lane the same 16-element slice of its row in the 4 groups, so
-// a thread has its 8 16-byte loads in flight together, a row's 1 KiB of input
-// is read by 8 lanes as one run, and the 32 rows' scales of a group (adjacent
-// in the block-major layout) are one 128-byte line written by one workgroup.
+// group is handled by 8 consecutive lanes, 16 elements each: lane p of the
+// group takes elements 8p .. 8p + 7 and 64 + 8p .. 64 + 8p + 7, so each of its
+// two 16-byte loads is, across the 8 lanes, one whole 128-byte line of the
+// row (with 16 contiguous elements per lane instead, every load instruction
+// touched twice the lines, each half used: 6-9 % slower).  A workgroup covers
+// a tile of 32 rows x 2 groups (256 columns; 4 and 8 groups per tile were
+// slower, 1 no faster): each wave takes 8 rows, each lane the same slices of
+// its row in the 2 groups, so a thread has its 4 16-byte loads in flight
+// together, and the 32 rows' scales of a group (adjacent in the block-major
+// layout) are one 128-byte line written by one workgroup.
 // The group max is a 3-step DPP butterfly inside the 8 lanes.  The fp32 -> fp8
 // rounding is the hardware v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 on inputs
 // clamped to +-FP8_MAX (round to nearest even; the clamp gives saturation).
@@ -62,9 +66,9 @@ __device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
 constexpr int kTileRows = 32;   // 4 waves x 8 rows
-constexpr int kTileGroups = 4;  // 128-column groups per tile
+constexpr int kTileGroups = 2;  // 128-column groups per tile
 
-// One 32-row x 512-column tile of one operand.
+// One 32-row x 256-column tile of one operand.
 template <int kFmt, bool kPow2>
 __device__ __forceinline__ void cast_tile(const CastOperand& o, int64_t tile)
 {
@@ -85,9 +89,9 @@ __device__ __forceinline__ void cast_tile(const CastOperand& o, int64_t tile)
 #pragma unroll
     for (int t = 0; t < kTileGroups; ++t) {
         const int64_t gc = min(g0 + t, o.gpr - 1);
-        const u32x4* src = reinterpret_cast<const u32x4*>(o.x + row * o.ld_x + gc * 128 + part * 16);
-        u[t][0] = __builtin_nontemporal_load(src);
-        u[t][1] = __builtin_nontemporal_load(src + 1);
+        const uint16_t* src = o.x + row * o.ld_x + gc * 128 + part * 8;
+        u[t][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+        u[t][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 64));
     }
 #pragma unroll
     for (int t = 0; t < kTileGroups; ++t) {
@@ -118,7 +122,8 @@ __device__ __forceinline__ void cast_tile(const CastOperand& o, int64_t tile)
         const uint2 c1 = encode8<kFmt>(s1);
         const int64_t gc = g0 + t;
         if (row_ok && gc < o.gpr) {
-            *reinterpret_cast<uint4*>(o.q + row * o.ld_q + gc * 128 + part * 16) = make_uint4(c0.x, c0.y, c1.x, c1.y);
+            *reinterpret_cast<uint2*>(o.q + row * o.ld_q + gc * 128 + part * 8) = c0;
+            *reinterpret_cast<uint2*>(o.q + row * o.ld_q + gc * 128 + 64 + part * 8) = c1;
             if (part == 0) o.scales[gc * o.ld_s + row] = scale;  // block-major: [cols/128][ld_s]
         }
     }
