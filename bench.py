@@ -60,10 +60,16 @@ def parse():
 
 
 def kernel_hash():
+    """Hash of the kernel sources with comments and blank space removed, so that an edit of a
+    comment does not orphan counters taken on the same code."""
+    import re
     h = hashlib.sha256()
     for f in ("gemm.hip", "cast.hip"):
-        with open(os.path.join(ROOT, "fp8_linear_layer_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "fp8_linear_layer_amd", "csrc", f)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1792,7 +1792,7 @@ hipError_t launch_epi(const GemmArgs& a, dim3 grid, int64_t tiles, hipStream_t s
     return hipGetLastError();
 }
 
-// (dense products without the transposed store: launch_gemm's choice)
+// (every product but the transposed quantising store: launch_gemm's choice)
 template <int kFmtA, int kFmtB, bool kFast>
 hipError_t launch_wave_epi(const GemmArgs& a, dim3 grid, hipStream_t s)
 {
@@ -1903,16 +1903,17 @@ int device_cus()
     return cached[dev];
 }
 
-// Which kernel takes a dense product: the wave-tile one when the 256 x 256
-// tiles number at most a quarter of the compute units (its workgroups, one
-// per wave tile, then fill every CU at most twice over), the persistent one
-// otherwise.  Kernel trace, out += A B^T (FULL): 1 and 4 tiles, K = 512:
-// 14.0 vs 21.4-21.7 us; K = 2048: 21.7 vs 36.4-36.8 us; 32 tiles (1024 x
-// 2048), K = 4096: 37.3 vs 60.1 us; 64 tiles (2048 x 2048): 45.8 vs 61.9 us;
-// 128 tiles (2048 x 4096): 83.4 vs 64.5 us, where the persistent kernel's
-// eight waves per tile are ahead.  The environment variable TE_FP8_GEMM_PATH
-// ("wave" or "persistent") overrides the choice for the products the wave
-// kernel supports.
+// Which kernel takes a product: the wave-tile one when the 256 x 256 tiles
+// (of all groups together) number at most a quarter of the compute units (its
+// workgroups, one per wave tile, then fill every CU at most twice over), the
+// persistent one otherwise.  Kernel trace, out += A B^T (FULL), wave against
+// persistent: 1 and 4 tiles, K = 512: 8.7-8.8 vs 21.2-21.5 us; K = 2048:
+// 16.2 vs 36.6 us; 32 tiles (1024 x 2048), K = 4096: 29.8 vs 60.1 us; 64
+// tiles (2048 x 2048): 39.2 vs 61.9 us; 128 tiles (2048 x 4096): 33.3 vs 33.2
+// us at K = 1024 but 72.1 vs 64.5 us at K = 4096, where the persistent
+// kernel's eight waves per tile are ahead.  The environment variable
+// TE_FP8_GEMM_PATH ("wave" or "persistent") overrides the choice for the
+// products the wave kernel supports.
 bool use_wave_path(const GemmArgs& a, int64_t tiles, int cus)
 {
     const bool supported = !a.qt_out;
