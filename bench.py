@@ -559,7 +559,7 @@ def cpu_model():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only (the library has no multi-GPU path); --gpus must be 1"}))
         sys.exit(2)
     import torch
     import fp8_linear_layer_amd as te
