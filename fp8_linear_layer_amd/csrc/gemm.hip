@@ -573,9 +573,11 @@ __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&v)[8],
 // The saved pre-activation: its reader is the backward pass, long after this
 // kernel, so the full 16-byte runs are streamed (non-temporal stores: the
 // forward with the pre-activation measured 3-4 % faster, the MLP training
-// step 1 %); a run cut by the matrix edge goes out element by element.
+// step 1 %); a run cut by the matrix edge goes out element by element.  (The
+// two-layout store writes it in 8-byte runs, 32 contiguous bytes per row and
+// instruction; streamed, those partial lines made that kernel 5 % slower, so
+// it keeps ordinary stores.)
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void store_preact_bf16x8(uint16_t* dst, const float (&v)[8], bool full, int64_t left)
 {
     if (full) {
@@ -1175,9 +1177,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, v4f (&acc)[kTM][kJ],
                 uint16_t* o = p.aux + m * p.ld_aux + ng + q4 * 4;
 #pragma unroll
                 for (int j = 0; j < kTN; ++j)
-                    __builtin_nontemporal_store(u32x2_t{pack_bf16x2(acc[i][j][0], acc[i][j][1]),
-                                                        pack_bf16x2(acc[i][j][2], acc[i][j][3])},
-                                                reinterpret_cast<u32x2_t*>(o + j * 16));
+                    *reinterpret_cast<uint2*>(o + j * 16) = make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]),
+                                                                       pack_bf16x2(acc[i][j][2], acc[i][j][3]));
             }
         }
         if (has_gelu) {
