@@ -573,10 +573,10 @@ __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&v)[8],
 // The saved pre-activation: its reader is the backward pass, long after this
 // kernel, so the full 16-byte runs are streamed (non-temporal stores: the
 // forward with the pre-activation measured 3-4 % faster, the MLP training
-// step 1 %); a run cut by the matrix edge goes out element by element.  (The
-// two-layout store writes it in 8-byte runs, 32 contiguous bytes per row and
-// instruction; streamed, those partial lines made that kernel 5 % slower, so
-// it keeps ordinary stores.)
+// step 1 %); a run cut by the matrix edge goes out element by element.
+// (Streamed 8-byte runs, 32 contiguous bytes per row and instruction, made
+// the two-layout forward 3.5 % slower: every caller pairs column groups
+// first.)
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void store_preact_bf16x8(uint16_t* dst, const float (&v)[8], bool full, int64_t left)
 {
@@ -1170,15 +1170,25 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, v4f (&acc)[kTM][kJ],
             }
         }
         if (has_aux) {
+            // (paired column groups, as in the other forward epilogues: 16-byte runs, streamed)
 #pragma unroll
             for (int i = 0; i < kTM; ++i) {
                 const int64_t m = m0 + wm * kWM + i * 16 + r16;
-                if (!(group_in && (kFull || m < p.M))) continue;
-                uint16_t* o = p.aux + m * p.ld_aux + ng + q4 * 4;
+                const bool live = group_in && (kFull || m < p.M);
 #pragma unroll
-                for (int j = 0; j < kTN; ++j)
-                    *reinterpret_cast<uint2*>(o + j * 16) = make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]),
-                                                                       pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+                for (int jp = 0; jp < kTN / 2; ++jp) {
+                    float v[8];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const auto sw = __builtin_amdgcn_permlane16_swap(
+                            __float_as_uint(acc[i][2 * jp][c]), __float_as_uint(acc[i][2 * jp + 1][c]), false, false);
+                        v[c] = __uint_as_float(sw[0]);
+                        v[4 + c] = __uint_as_float(sw[1]);
+                    }
+                    if (live)
+                        store_preact_bf16x8(p.aux + m * p.ld_aux + ng + (2 * jp + (q4 & 1)) * 16 + (q4 >> 1) * 8, v,
+                                            true, 8);
+                }
             }
         }
         if (has_gelu) {
