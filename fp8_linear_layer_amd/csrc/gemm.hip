@@ -1767,13 +1767,27 @@ __global__ void zero_f32_kernel(float* p, int64_t n)
 
 // The second pass of the deterministic bias gradient: one thread per column
 // sums the workspace rows in order (coalesced across the threads of a row).
-__global__ void bgrad_reduce_kernel(const float* __restrict__ ws, int64_t rows, int64_t ld, int64_t N,
-                                    float* __restrict__ bias_grad)
+constexpr int kReduceThreads = 64;  // one column per thread; small workgroups spread the columns over the CUs
+constexpr int kReduceChunk = 32;    // rows whose loads are in flight together
+
+__global__ __launch_bounds__(kReduceThreads) void bgrad_reduce_kernel(const float* __restrict__ ws, int64_t rows,
+                                                                      int64_t ld, int64_t N,
+                                                                      float* __restrict__ bias_grad)
 {
     const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (n >= N) return;
+    // The rows are summed in order; their loads go out kReduceChunk at a time
+    // (one load after another cost a memory round trip per row: 44.6 us for
+    // the 128 rows x 14336 columns of an 8192 x 14336 bias gradient).
     float s = 0.0f;
-    for (int64_t r = 0; r < rows; ++r) s += ws[r * ld + n];
+    for (int64_t r0 = 0; r0 < rows; r0 += kReduceChunk) {
+        float v[kReduceChunk];
+#pragma unroll
+        for (int u = 0; u < kReduceChunk; ++u) v[u] = r0 + u < rows ? ws[(r0 + u) * ld + n] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < kReduceChunk; ++u)
+            if (r0 + u < rows) s += v[u];
+    }
     bias_grad[n] = s;
 }
 
@@ -2013,7 +2027,8 @@ hipError_t launch_bgrad_reduce(const float* ws, int64_t rows, int64_t ld, int64_
                                hipStream_t stream)
 {
     if (N <= 0) return hipSuccess;
-    bgrad_reduce_kernel<<<(unsigned)((N + 255) / 256), 256, 0, stream>>>(ws, rows, ld, N, bias_grad);
+    bgrad_reduce_kernel<<<(unsigned)((N + kReduceThreads - 1) / kReduceThreads), kReduceThreads, 0, stream>>>(
+        ws, rows, ld, N, bias_grad);
     return hipGetLastError();
 }
 
