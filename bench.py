@@ -176,6 +176,7 @@ def group_dense_wgrad(te, torch, g):
     pa, psa = te.te_cast_fp8_per_token(a, E4, te.TE_CAST_POW2_SCALE)
     pb, psb = te.te_cast_fp8_per_token(b, E4, te.TE_CAST_POW2_SCALE)
     o = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    bg = torch.empty((M,), dtype=torch.float32, device="cuda")
     dyt, xt = _randn(torch, g, (T, M), 1.0, 11), _randn(torch, g, (T, N), 1.0, 12)
     qa2 = torch.empty((M, T), dtype=torch.uint8, device="cuda")
     sa2 = torch.empty((T // 128, te.scale_ld(M)), dtype=torch.float32, device="cuda")
@@ -192,6 +193,9 @@ def group_dense_wgrad(te, torch, g):
     return {
         "wgrad_full_7168x2112x4096": Case(lambda: te.te_fp8_wgrad_accum(qa, sa, E4, qb, sb, E4, o,
                                                                         te.TE_ACCUM_FULL_FP32), f),
+        "wgrad_bgrad_full_7168x2112x4096": Case(
+            lambda: te.te_fp8_wgrad_accum_bgrad(qa, sa, E4, qb, sb, E4, o, bg, te.TE_ACCUM_FULL_FP32), f,
+            note="out += A B^T and the bias gradient as the row sums of A (dY^T) in the same call"),
         "wgrad_pow2_full_7168x2112x4096": Case(lambda: te.te_fp8_wgrad_accum(pa, psa, E4, pb, psb, E4, o,
                                                                              te.TE_ACCUM_FULL_FP32), f),
         "wgrad_pow2_fast_7168x2112x4096": Case(lambda: te.te_fp8_wgrad_accum(pa, psa, E4, pb, psb, E4, o,
@@ -200,7 +204,8 @@ def group_dense_wgrad(te, torch, g):
             lambda: te.te_cast_fp8_per_token_batch([a, b], E4, qs=[qa, qb], scales=[sa, sb]), nbytes=cast_bytes),
         "wgrad_from_token_major_7168x2112x4096": Case(
             token_major, f, note="cast-transpose dY and X (tokens x features, bf16) + out += A B^T"),
-    }, [("wgrad_pow2_full_7168x2112x4096", "wgrad_pow2_fast_7168x2112x4096")]
+    }, [("wgrad_pow2_full_7168x2112x4096", "wgrad_pow2_fast_7168x2112x4096"),
+        ("wgrad_full_7168x2112x4096", "wgrad_bgrad_full_7168x2112x4096")]
 
 
 def group_fprop(te, torch, g):
@@ -415,7 +420,8 @@ GROUPS = [group_tiny, group_dense_wgrad, group_fprop, group_dgrad, group_kgroupe
 # the cases of each group (so that --case sets up only its own group's inputs)
 GROUP_CASES = {
     group_tiny: ("tiny_fprop_bias_gelu_256x256x512", "tiny_wgrad_256x256x512"),
-    group_dense_wgrad: ("wgrad_full_7168x2112x4096", "wgrad_pow2_full_7168x2112x4096", "wgrad_pow2_fast_7168x2112x4096",
+    group_dense_wgrad: ("wgrad_full_7168x2112x4096", "wgrad_bgrad_full_7168x2112x4096", "wgrad_pow2_full_7168x2112x4096",
+                        "wgrad_pow2_fast_7168x2112x4096",
                         "cast_batch_e4m3_7168x4096_2112x4096", "wgrad_from_token_major_7168x2112x4096"),
     group_fprop: ("fprop_none_full", "fprop_bias_gelu_full", "fprop_none_fast", "fprop_none_fast_pow2",
                   "fprop_bias_gelu_fast_pow2", "fprop_bias_gelu_aux_fast_pow2", "fprop_bias_gelu_aux_full",
