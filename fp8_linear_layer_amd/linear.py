@@ -9,8 +9,10 @@ crafted epilogues" (dX = dY W, dW = dY^T X, db = column sums of dY; dGELU before
 gradient):
 
   forward   x -> (x_q, x^T_q)            one cast-transpose of x (e4m3)
-            y = x_q W_q^T + b            te_fp8_gemm_fwd, FAST accumulation (the fprop policy of
-                                         "FP8 GEMM for the fprop should use fast accumulation")
+            y = x_q W_q^T + b            te_fp8_gemm_fwd, FWD_ACCUM (fast accumulation, the fprop
+                                         policy of "FP8 GEMM for the fprop should use fast
+                                         accumulation", applies to power-of-two scales only; on
+                                         the IEEE scales of these casts it is FULL, see below)
   backward  dy -> (dy_q, dy^T_q)         one cast-transpose of dy (e5m2)
             dW += dy^T_q x^T_q^T, db     te_fp8_wgrad_accum_bgrad (fp32 accumulation into
                                          weight.main_grad, FULL policy), db from the fp8 dy^T
@@ -35,12 +37,17 @@ import math
 
 import torch
 
-from . import (TE_ACCUM_FAST, TE_ACCUM_FULL_FP32, TE_DTYPE_BF16, TE_DTYPE_E4M3, TE_DTYPE_E5M2, TE_EPI_AUX_PREACT,
+from . import (TE_ACCUM_FULL_FP32, TE_DTYPE_BF16, TE_DTYPE_E4M3, TE_DTYPE_E5M2, TE_EPI_AUX_PREACT,
                TE_EPI_BGRAD, TE_EPI_BIAS, TE_EPI_DGELU, TE_EPI_GELU, TE_EPI_NONE, te_cast_fp8_per_token_transpose,
                te_fp8_gemm_dgrad, te_fp8_gemm_fwd, te_fp8_wgrad_accum, te_fp8_wgrad_accum_bgrad)
 
 FWD_DTYPE = TE_DTYPE_E4M3    # activations and weights
 BWD_DTYPE = TE_DTYPE_E5M2    # gradients
+# Accumulation policy of the forward GEMMs.  Fast accumulation (the matrix core chaining the
+# blocks) applies only where a tile's scales are powers of two; the casts here use IEEE scales,
+# on which TE_ACCUM_FAST takes the FULL promotion in every tile after testing the tile's scales,
+# so FULL gives the same bits without the test (2-4 % of those GEMMs).
+FWD_ACCUM = TE_ACCUM_FULL_FP32
 
 
 def _check_dims(*dims):
@@ -90,7 +97,7 @@ class _Fp8LinearFn(torch.autograd.Function):
         qw, sw, _, _ = cache.get(weight)
         y = te_fp8_gemm_fwd(qx, sx, FWD_DTYPE, qw, sw, FWD_DTYPE, bias=bias,
                             epilogue=TE_EPI_BIAS if bias is not None else TE_EPI_NONE, y_dtype=TE_DTYPE_BF16,
-                            accum=TE_ACCUM_FAST)
+                            accum=FWD_ACCUM)
         ctx.save_for_backward(qxt, sxt, weight)
         ctx.cache, ctx.has_bias, ctx.keep = cache, bias is not None, keep
         if keep is not None:
@@ -130,11 +137,11 @@ class _Fp8MlpFn(torch.autograd.Function):
         z1 = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
         h = te_fp8_gemm_fwd(qx, sx, FWD_DTYPE, qw1, sw1, FWD_DTYPE, bias=b1,
                             epilogue=TE_EPI_BIAS | TE_EPI_GELU | TE_EPI_AUX_PREACT, preact=z1,
-                            y_dtype=TE_DTYPE_BF16, accum=TE_ACCUM_FAST)
+                            y_dtype=TE_DTYPE_BF16, accum=FWD_ACCUM)
         qh, sh, qht, sht = te_cast_fp8_per_token_transpose(h, FWD_DTYPE)
         qw2, sw2, _, _ = c2.get(w2)
         y = te_fp8_gemm_fwd(qh, sh, FWD_DTYPE, qw2, sw2, FWD_DTYPE, bias=b2, epilogue=TE_EPI_BIAS,
-                            y_dtype=TE_DTYPE_BF16, accum=TE_ACCUM_FAST)
+                            y_dtype=TE_DTYPE_BF16, accum=FWD_ACCUM)
         ctx.save_for_backward(qxt, sxt, z1, qht, sht, w1, w2)
         ctx.c1, ctx.c2, ctx.keep = c1, c2, keep
         if keep is not None:
