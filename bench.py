@@ -404,16 +404,22 @@ def group_modules(te, torch, g):
     T, D, H = 8192, 4096, 14336
     gen = torch.Generator(device="cuda").manual_seed(19)
     m = lin.Fp8Mlp(D, H, D, generator=gen)
+    mp = lin.Fp8Mlp(D, H, D, generator=torch.Generator(device="cuda").manual_seed(19), pow2_scales=True)
     x = _randn(torch, g, (T, D), 1.0, 20).requires_grad_(True)
     dy = _randn(torch, g, (T, D), 1e-3, 21)
 
-    def step():
-        m(x).backward(dy)
+    def step(mod):
+        mod(x).backward(dy)
         x.grad = None
-        m.b1.grad = None
-        m.b2.grad = None
-    return {"mlp_step_8192x4096x14336": Case(step, 6 * 2.0 * T * D * H,
-                                              note="forward (2 GEMMs) + backward (4 GEMMs) + casts")}, []
+        mod.b1.grad = None
+        mod.b2.grad = None
+    f = 6 * 2.0 * T * D * H
+    return {"mlp_step_8192x4096x14336": Case(lambda: step(m), f,
+                                              note="forward (2 GEMMs) + backward (4 GEMMs) + casts"),
+            "mlp_step_pow2_8192x4096x14336": Case(
+                lambda: step(mp), f, note="the same with pow2_scales: x, h and the weights cast with power-of-two "
+                                          "scales, both forward GEMMs on FAST (chained)")}, \
+        [("mlp_step_8192x4096x14336", "mlp_step_pow2_8192x4096x14336")]
 
 
 GROUPS = [group_tiny, group_dense_wgrad, group_fprop, group_dgrad, group_kgrouped, group_mgrouped, group_modules]
@@ -435,7 +441,7 @@ GROUP_CASES = {
     group_kgrouped: ("kgrouped_wgrad_full", "kgrouped_wgrad_device_sizes_full"),
     group_mgrouped: ("mgrouped_fwd_bias_gelu_full_8x1024x4096x7168", "mgrouped_dgrad_dgelu_bgrad_full_8x1024x7168x4096",
                      "mgrouped_dgrad_dgelu_bgrad_deterministic_full_8x1024x7168x4096"),
-    group_modules: ("mlp_step_8192x4096x14336",),
+    group_modules: ("mlp_step_8192x4096x14336", "mlp_step_pow2_8192x4096x14336"),
 }
 
 

@@ -37,9 +37,9 @@ def bf16_in(seed, shape, std):
     return torch.from_numpy(W.normal_bf16(np.random.SeedSequence(seed), shape, std)).view(torch.bfloat16).cuda()
 
 
-def check_cast_transpose(q, s, qt, st, x_bits, fmt, what):
+def check_cast_transpose(q, s, qt, st, x_bits, fmt, what, pow2=False):
     """The library's cast-transpose of x equals the oracle's cast of x and of x^T, bit for bit."""
-    oq, os_, oqt, ost = oracle.cast_per_token_transpose(x_bits, fmt)
+    oq, os_, oqt, ost = oracle.cast_per_token_transpose(x_bits, fmt, pow2)
     rows, cols = x_bits.shape
     assert np.array_equal(host(q).numpy(), oq), f"{what}: row-wise codes"
     assert np.array_equal(shost(s, rows).view(np.uint32), os_.view(np.uint32)), f"{what}: row-wise scales"
@@ -55,10 +55,12 @@ def op(q, s, rows):
 E4, E5 = oracle.E4M3, oracle.E5M2
 
 
-def test_fp8_linear_step_matches_oracle_per_call_and_caches_the_weight():
+@pytest.mark.parametrize("pow2", [False, True], ids=["ieee", "pow2"])
+def test_fp8_linear_step_matches_oracle_per_call_and_caches_the_weight(pow2):
+    """pow2: the forward operands with power-of-two scales and the forward GEMM on FAST (chained)."""
     M, K, N = 256, 384, 256
     g = torch.Generator(device="cuda").manual_seed(5)
-    m = lin.Fp8Linear(K, N, bias=True, generator=g)
+    m = lin.Fp8Linear(K, N, bias=True, generator=g, pow2_scales=pow2)
     with torch.no_grad():
         m.bias.copy_(bf16_in(1, (N,), 0.1))
     m.keep = {}
@@ -70,8 +72,8 @@ def test_fp8_linear_step_matches_oracle_per_call_and_caches_the_weight():
         y.backward(dy)
         torch.cuda.synchronize()
         k = m.keep
-        qx, sx, qxt, sxt = check_cast_transpose(k["qx"], k["sx"], k["qxt"], k["sxt"], bits(x), E4, "x")
-        qw, sw, qwt, swt = check_cast_transpose(*m.cache.get(m.weight), bits(m.weight), E4, "W")
+        qx, sx, qxt, sxt = check_cast_transpose(k["qx"], k["sx"], k["qxt"], k["sxt"], bits(x), E4, "x", pow2)
+        qw, sw, qwt, swt = check_cast_transpose(*m.cache.get(m.weight), bits(m.weight), E4, "W", pow2)
         o, d = oracle.gemm_nt(qx, sx, E4, qw, sw, E4)
         yo, _, zm = oracle.fwd_epilogue(o, d, bits(m.bias))
         check_bf16(bf16_host_f64(y), yo, zm, "linear y")
@@ -92,7 +94,7 @@ def test_fp8_linear_step_matches_oracle_per_call_and_caches_the_weight():
         m.weight.mul_(0.5)
     m(bf16_in(30, (M, K), 1.0))
     assert m.cache.casts == 2
-    check_cast_transpose(*m.cache.get(m.weight), bits(m.weight), E4, "W after update")
+    check_cast_transpose(*m.cache.get(m.weight), bits(m.weight), E4, "W after update", pow2)
 
 
 def test_fp8_linear_input_gradient():
@@ -114,10 +116,13 @@ def test_fp8_linear_input_gradient():
     check_f32(host(m.weight.main_grad).numpy(), want, mag, "linear dW", chain_gemm(M, 1))
 
 
-def test_fp8_mlp_step_matches_oracle_per_call():
+@pytest.mark.parametrize("pow2", [False, True], ids=["ieee", "pow2"])
+def test_fp8_mlp_step_matches_oracle_per_call(pow2):
+    """pow2: x, h, W1 and W2 cast with power-of-two scales, both forward GEMMs on FAST (chained);
+    the gradients keep IEEE scales."""
     M, K, H, N = 256, 256, 512, 384
     g = torch.Generator(device="cuda").manual_seed(9)
-    m = lin.Fp8Mlp(K, H, N, generator=g)
+    m = lin.Fp8Mlp(K, H, N, generator=g, pow2_scales=pow2)
     with torch.no_grad():
         m.b1.copy_(bf16_in(2, (H,), 0.1))
         m.b2.copy_(bf16_in(3, (N,), 0.1))
@@ -128,16 +133,16 @@ def test_fp8_mlp_step_matches_oracle_per_call():
     y.backward(dy)
     torch.cuda.synchronize()
     k = m.keep
-    qx, sx, qxt, sxt = check_cast_transpose(k["qx"], k["sx"], k["qxt"], k["sxt"], bits(x), E4, "x")
-    qw1, sw1, qw1t, sw1t = check_cast_transpose(*m.c1.get(m.w1), bits(m.w1), E4, "W1")
-    qw2, sw2, qw2t, sw2t = check_cast_transpose(*m.c2.get(m.w2), bits(m.w2), E4, "W2")
+    qx, sx, qxt, sxt = check_cast_transpose(k["qx"], k["sx"], k["qxt"], k["sxt"], bits(x), E4, "x", pow2)
+    qw1, sw1, qw1t, sw1t = check_cast_transpose(*m.c1.get(m.w1), bits(m.w1), E4, "W1", pow2)
+    qw2, sw2, qw2t, sw2t = check_cast_transpose(*m.c2.get(m.w2), bits(m.w2), E4, "W2", pow2)
     # fc1 forward: h = GELU(z), z saved
     o, d = oracle.gemm_nt(qx, sx, E4, qw1, sw1, E4)
     h, z, zm = oracle.fwd_epilogue(o, d, bits(m.b1), True)
     check_bf16(bf16_host_f64(k["h"]), h, zm * GELU_LIP, "mlp h")
     check_bf16(bf16_host_f64(k["z1"]), z, zm, "mlp z1")
     # fc2 forward on the GPU's own h
-    qh, sh, qht, sht = check_cast_transpose(k["qh"], k["sh"], k["qht"], k["sht"], bits(k["h"]), E4, "h")
+    qh, sh, qht, sht = check_cast_transpose(k["qh"], k["sh"], k["qht"], k["sht"], bits(k["h"]), E4, "h", pow2)
     o, d = oracle.gemm_nt(qh, sh, E4, qw2, sw2, E4)
     yo, _, ym = oracle.fwd_epilogue(o, d, bits(m.b2))
     check_bf16(bf16_host_f64(y), yo, ym, "mlp y")
