@@ -645,6 +645,52 @@ def test_fast_on_ieee_scales_is_full_bit_for_bit(M, N, K, gemm_path):
         assert torch.equal(f.view(torch.int32), g.view(torch.int32)), f"{what}: FAST on IEEE scales differs from FULL"
 
 
+def spread_operand(seed, rows, K, dt, pow2):
+    """An operand whose rows span 2^-12 .. 2^12 in magnitude, so its per-row scales (and their
+    E8M0 exponents, where they are powers of two) differ widely."""
+    rng = np.random.default_rng(seed)
+    mag = np.exp2(rng.integers(-12, 13, (rows, 1))).astype(np.float32)
+    bits = W.f32_to_bf16_bits(rng.standard_normal((rows, K), dtype=np.float32) * mag)
+    return oracle.cast_per_token(bits, OF[dt], pow2)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 264, 384), (512, 768, 1024)])
+def test_fast_on_one_pow2_operand_is_full_bit_for_bit(M, N, K, gemm_path):
+    """Power-of-two scales on one operand only (B: the backward products of a pow2_scales module,
+    IEEE-scaled gradients times power-of-two-scaled forward operands; or A): the matrix core may
+    chain only where both operands' scales are powers of two, so every tile takes the FULL
+    promotion and each entry point's FAST result is its FULL result bit for bit.  The operands'
+    rows span 2^-12 .. 2^12, so a scale wrongly taken as an E8M0 exponent would show."""
+    qa, sa = spread_operand(161, M, K, E5, False)
+    qb, sb = spread_operand(162, N, K, E4, True)
+    qp, sp = spread_operand(163, M, K, E5, True)
+    qi, si = spread_operand(164, N, K, E4, False)
+    b = bf16_dev(W.normal_bf16(np.random.SeedSequence(165), (N,), 0.1))
+    Z = bf16_dev(W.normal_bf16(np.random.SeedSequence(166), (M, N), 1.28))
+    out0 = dev(W.normal_f32(np.random.SeedSequence(167), (M, N)))
+    for what, (A, SA, B, SB) in (("pow2 B", (dev(qa), sdev(sa), dev(qb), sdev(sb))),
+                                 ("pow2 A", (dev(qp), sdev(sp), dev(qi), sdev(si)))):
+        res = {}
+        for accum in (FULL, FAST):
+            y = te.te_fp8_gemm_fwd(A, SA, E5, B, SB, E4, bias=b, epilogue=te.TE_EPI_BIAS | te.TE_EPI_GELU,
+                                   y_dtype=te.TE_DTYPE_F32, accum=accum)
+            bg = torch.empty((N,), dtype=torch.float32, device="cuda")
+            dz = te.te_fp8_gemm_dgrad_deterministic(A, SA, E5, B, SB, E4, bg,
+                                                    epilogue=te.TE_EPI_DGELU | te.TE_EPI_BGRAD, preact=Z,
+                                                    dx_dtype=te.TE_DTYPE_F32, accum=accum)
+            out = out0.clone()
+            te.te_fp8_wgrad_accum(A, SA, E5, B, SB, E4, out, accum)
+            res[accum] = [host(t) for t in (y, dz, bg, out)]
+        for op, f, g in zip(("fwd", "dgrad", "bias grad", "wgrad"), res[FULL], res[FAST]):
+            assert torch.equal(f.view(torch.int32), g.view(torch.int32)), f"{what}, {op}: FAST differs from FULL"
+    # and the FAST result against the oracle
+    o, d = oracle.gemm_nt(qa, sa, OF[E5], qb, sb, OF[E4])
+    want, mag = oracle.wgrad(o, d, host(out0).numpy())
+    out = out0.clone()
+    te.te_fp8_wgrad_accum(dev(qa), sdev(sa), E5, dev(qb), sdev(sb), E4, out, FAST)
+    check_f32(host(out).numpy(), want, mag, "wgrad, pow2 B only, on FAST", chain_gemm(K, 1))
+
+
 # ------------------------------------------------------------------ M-grouped
 def mgrouped_case(seed, G, blocks, N, K, pow2=False, fx=E4, wstd=0.05):
     sum_m = 256 * len(blocks)
